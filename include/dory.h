@@ -1,0 +1,207 @@
+/*
+ * dory.h -- C ABI of the MI355X (gfx950) forward pass of the looped
+ * normalized-GPT described in "Dory1.0-4B: A Looped Normalized-GPT"
+ * (paper body page).
+ *
+ * The model (sections Architecture and Training with Loops): an input block,
+ * a recurrent block applied k times with every parameter shared across the k
+ * invocations, and an output block. Each block is a sequence of sublayers,
+ * attention-only or MLP-only. Every sublayer ends in the normalized
+ * Transformer's residual update h <- N(h + alpha * (N(y) - h)), N being
+ * per-token L2 normalization. Before each recurrent invocation the input
+ * block's output x is added to the state and the sum normalized; the state
+ * is replaced by the block's output and normalized again; the final state
+ * feeds the output block and the LM head. Attention is grouped-query with an
+ * input-dependent sigmoid gate on the head outputs; layers are
+ * sliding-window or full attention in a 3:1 pattern, with RoPE bases and
+ * window from section Long-Context Extension. Keys and values are cached per
+ * loop or, with last-loop caching (section Last-Loop KV Caching), from the
+ * final loop only so that the cache size does not depend on k.
+ *
+ * Conventions for every call below:
+ *   - Device memory (weights, KV buffer, workspace, token ids, logits,
+ *     hidden states) is allocated and owned by the caller. The library keeps
+ *     only the pointers it is given and small host-side handles; it never
+ *     allocates or frees device memory.
+ *   - Matrices are row-major. "bf16" buffers hold bfloat16 bit patterns,
+ *     weight matrices use the [out_features, in_features] layout.
+ *   - All argument checks run on the host before anything is enqueued: on a
+ *     non-OK status nothing was enqueued and the cache is unchanged.
+ *   - Compute calls are asynchronous on the given HIP stream (a hipStream_t
+ *     passed as void*; NULL = default stream); outputs are valid once that
+ *     stream has been synchronized. A failed kernel launch returns
+ *     DORY_ERR_HIP and marks the KV handle invalid until dory_kv_reset().
+ *   - dory_last_error() returns a thread-local description of the last
+ *     non-OK status returned on the calling thread.
+ */
+#ifndef DORY_H_
+#define DORY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dory_status {
+  DORY_OK = 0,
+  DORY_ERR_ARG = 1,          /* null pointer, k < 1, B or T <= 0, bad shape */
+  DORY_ERR_MODE = 2,         /* cache-mode mismatch, or per-loop k rule */
+  DORY_ERR_CAPACITY = 3,     /* cache length + T > max_seq, or B > bound batch */
+  DORY_ERR_WORKSPACE = 4,    /* workspace too small */
+  DORY_ERR_UNSUPPORTED = 5,  /* shape without a kernel (head_dim, widths) */
+  DORY_ERR_HIP = 6,          /* a HIP launch failed */
+  DORY_ERR_STATE = 7         /* KV handle invalid after a HIP failure */
+} dory_status;
+
+/* Cache policies of section Last-Loop KV Caching. */
+typedef enum dory_cache_mode {
+  DORY_CACHE_LAST_LOOP = 0, /* one cache per recurrent attention sublayer, holding the final loop's K/V */
+  DORY_CACHE_PER_LOOP = 1   /* one cache per recurrent attention sublayer and loop */
+} dory_cache_mode;
+
+/* Sublayer kinds. Section Architecture: attention-only and MLP-only layers,
+ * attention either sliding-window or full. */
+typedef enum dory_layer_kind {
+  DORY_LAYER_ATTN_SWA = 0,
+  DORY_LAYER_ATTN_FULL = 1,
+  DORY_LAYER_MLP = 2
+} dory_layer_kind;
+
+typedef struct dory_config {
+  int32_t d_model;      /* d */
+  int32_t n_q_heads;    /* query heads (16 in section Architecture) */
+  int32_t n_kv_heads;   /* KV groups (4); n_q_heads % n_kv_heads == 0 */
+  int32_t head_dim;     /* 32, 64 or 128 */
+  int32_t d_ff;         /* SwiGLU width F */
+  int32_t vocab;        /* V */
+  int32_t n_input;      /* sublayers in the input block (16) */
+  int32_t n_recurrent;  /* sublayers in the shared recurrent block (40) */
+  int32_t n_output;     /* sublayers in the output block (16) */
+  int32_t window;       /* sliding window W (1024): query p sees keys u with p - u < W */
+  int32_t full_every;   /* default schedule: attention sublayer j is full iff j % full_every == full_every - 1 */
+  int32_t has_lm_head;  /* 0: no LM head (logits unavailable) */
+  double rope_base_swa;  /* 1e4 */
+  double rope_base_full; /* 1e7 */
+  double softmax_scale;  /* logit scale on q_hat.k_hat; <= 0 selects sqrt(head_dim) */
+  /* Optional explicit schedule: n_input + n_recurrent + n_output entries of
+   * dory_layer_kind. NULL: sublayers alternate attention and MLP starting
+   * with attention, attention kinds by full_every. Copied at model creation. */
+  const int32_t* layer_kinds;
+} dory_config;
+
+/* Device pointers of one sublayer. Attention sublayers use the first group,
+ * MLP sublayers the second; alpha is used by both. */
+typedef struct dory_sublayer_weights {
+  const void* w_qkvg;   /* bf16 [2*d_q + 2*d_kv, d]: rows q (d_q = n_q*head_dim), k (d_kv), v (d_kv), gate (d_q) */
+  const void* w_o;      /* bf16 [d, d_q] */
+  const float* s_qk;    /* fp32 [head_dim]: scale applied to the normalized q and k heads */
+  const void* w_upgate; /* bf16 [2*F, d]: rows up (F), then gate (F) */
+  const void* w_down;   /* bf16 [d, F] */
+  const float* s_u;     /* fp32 [F] */
+  const float* s_v;     /* fp32 [F] */
+  const float* alpha;   /* fp32 [d]: effective residual rate */
+} dory_sublayer_weights;
+
+typedef struct dory_weights {
+  const void* embed;    /* bf16 [V, d] */
+  const void* lm_head;  /* bf16 [V, d] (ignored without an LM head) */
+  const float* s_z;     /* fp32 [V]: logit scale */
+  const dory_sublayer_weights* sublayers; /* host array of n_input + n_recurrent + n_output; copied */
+} dory_weights;
+
+typedef struct dory_model dory_model;
+typedef struct dory_kv dory_kv;
+
+/* Location of one cache slot, for tests and tools. Keys of (b, g, position
+ * u) live at k + ((b * n_kv + g) * rows + r(u)) * head_dim, values
+ * transposed at v + ((b * n_kv + g) * head_dim + dim) * rows + r(u), with
+ * r(u) = u mod ring when ring > 0 (sliding-window slots) and r(u) = u
+ * otherwise. */
+typedef struct dory_kv_slot_info {
+  void* k;
+  void* v;
+  int64_t rows;
+  int64_t ring;
+} dory_kv_slot_info;
+
+/* Validates the configuration and weight table and builds the host-side
+ * schedule. Pointers are stored, not copied or dereferenced. */
+dory_status dory_model_create(const dory_config* cfg, const dory_weights* w, dory_model** out);
+void dory_model_destroy(dory_model* m);
+
+/* Writes the kind of each sublayer (dory_layer_kind) into kinds_out, which
+ * holds `capacity` entries. Schedule of section Architecture (27
+ * sliding-window + 9 full + 36 MLP at the paper's 72 sublayers). */
+dory_status dory_schedule(const dory_config* cfg, int32_t* kinds_out, int32_t capacity);
+
+/* Bytes of KV storage for a cache bound with these parameters (closed form:
+ * per attention sublayer, slots x batch x 2 x n_kv x head_dim x 2 bytes x
+ * rows; recurrent sublayers hold k_max slots under per-loop caching and one
+ * otherwise; sliding-window slots hold min(max_seq, window) rows, rounded up
+ * to a multiple of 8, as a ring; full-attention slots hold max_seq rows
+ * rounded up to a multiple of 8). Returns 0 on invalid arguments. */
+size_t dory_kv_bytes(const dory_config* cfg, dory_cache_mode mode, int32_t k_max,
+                     int32_t batch, int64_t max_seq);
+
+/* Bytes of workspace needed by a call with B sequences of T tokens each
+ * (decode: T = 1). Returns 0 on invalid arguments. */
+size_t dory_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t tokens);
+
+/* Binds a caller-owned device buffer of at least dory_kv_bytes() bytes as
+ * the KV cache of `batch` sequences of at most max_seq tokens, in `mode`;
+ * lengths start at 0. */
+dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dory_cache_mode mode,
+                         int32_t k_max, int32_t batch, int64_t max_seq, dory_kv** out);
+void dory_kv_destroy(dory_kv* kv);
+/* Forgets all cached tokens (length 0) and clears the invalid flag and the
+ * loop count recorded for per-loop caching. Device memory is not touched. */
+dory_status dory_kv_reset(dory_kv* kv);
+/* Tokens cached per sequence, or -1 for a NULL handle. */
+int64_t dory_kv_length(const dory_kv* kv);
+/* Slot of a sublayer: loop is 0-based and only meaningful for recurrent
+ * sublayers under per-loop caching. */
+dory_status dory_kv_slot(const dory_kv* kv, int32_t sublayer, int32_t loop, dory_kv_slot_info* out);
+
+/* One forward step over T new tokens per sequence at positions
+ * L .. L + T - 1, where L = dory_kv_length(kv) (the same for all B rows).
+ * Chunked prefill is a sequence of such calls.
+ *   tokens: device int32 [B, T]; ids outside [0, V) produce NaN outputs.
+ *   k >= 1: loop count (section Training with Loops). Under per-loop
+ *     caching k <= k_max and every step on one cache uses the same k.
+ *   mode: must equal the mode the cache was bound with.
+ *   ws / ws_bytes: device workspace of at least dory_workspace_bytes(cfg, B, T).
+ *   logits: device fp32 [B, V], logits of the last position, or NULL.
+ *   next: device int32 [B], greedy token of the last position (argmax, lowest
+ *     index on ties), or NULL. Needs an LM head.
+ *   hidden: device fp32 [B, T, d], output of the last sublayer, or NULL.
+ *   states: device fp32 [k, B, T, d], recurrent state after each loop
+ *     (s_1 .. s_k), or NULL.
+ * On success the cache length grows by T. */
+dory_status dory_prefill(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                         int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
+                         float* logits, int32_t* next, float* hidden, float* states,
+                         void* stream);
+
+/* One decode step: one new token per sequence (tokens: device int32 [B]) at
+ * position dory_kv_length(kv). Arguments as for dory_prefill with T = 1;
+ * hidden is [B, d] and states [k, B, d]. */
+dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                             int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
+                             float* logits, int32_t* next, float* hidden, float* states,
+                             void* stream);
+
+/* Mask dump for bit-exact tests: out (device uint8 [T, L + T]) receives 1
+ * where the attention kernels treat key position u as visible to the query
+ * at position L + t (u <= L + t, and L + t - u < window unless window is 0). */
+dory_status dory_debug_mask(int32_t window, int64_t L, int32_t T, uint8_t* out, void* stream);
+
+const char* dory_status_string(dory_status s);
+const char* dory_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DORY_H_ */

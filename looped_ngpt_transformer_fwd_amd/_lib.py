@@ -1,0 +1,183 @@
+"""ctypes view of include/dory.h: the same names, argument marshalling only.
+
+Loading fails loudly when libdory.so has not been built; there is no other
+implementation to fall back to.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdory.so")
+
+DORY_OK = 0
+DORY_ERR_ARG = 1
+DORY_ERR_MODE = 2
+DORY_ERR_CAPACITY = 3
+DORY_ERR_WORKSPACE = 4
+DORY_ERR_UNSUPPORTED = 5
+DORY_ERR_HIP = 6
+DORY_ERR_STATE = 7
+
+DORY_CACHE_LAST_LOOP = 0
+DORY_CACHE_PER_LOOP = 1
+
+DORY_LAYER_ATTN_SWA = 0
+DORY_LAYER_ATTN_FULL = 1
+DORY_LAYER_MLP = 2
+
+
+class dory_config(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32),
+        ("n_input", ctypes.c_int32), ("n_recurrent", ctypes.c_int32),
+        ("n_output", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("full_every", ctypes.c_int32), ("has_lm_head", ctypes.c_int32),
+        ("rope_base_swa", ctypes.c_double), ("rope_base_full", ctypes.c_double),
+        ("softmax_scale", ctypes.c_double),
+        ("layer_kinds", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class dory_sublayer_weights(ctypes.Structure):
+    _fields_ = [
+        ("w_qkvg", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("s_qk", ctypes.c_void_p),
+        ("w_upgate", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("s_u", ctypes.c_void_p), ("s_v", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
+    ]
+
+
+class dory_weights(ctypes.Structure):
+    _fields_ = [
+        ("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("s_z", ctypes.c_void_p),
+        ("sublayers", ctypes.POINTER(dory_sublayer_weights)),
+    ]
+
+
+class dory_kv_slot_info(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("ring", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "dory_model_create": (_I32, [ctypes.POINTER(dory_config), ctypes.POINTER(dory_weights),
+                                 ctypes.POINTER(_P)]),
+    "dory_model_destroy": (None, [_P]),
+    "dory_schedule": (_I32, [ctypes.POINTER(dory_config), ctypes.POINTER(_I32), _I32]),
+    "dory_kv_bytes": (_SZ, [ctypes.POINTER(dory_config), _I32, _I32, _I32, _I64]),
+    "dory_workspace_bytes": (_SZ, [ctypes.POINTER(dory_config), _I32, _I32]),
+    "dory_kv_bind": (_I32, [_P, _P, _SZ, _I32, _I32, _I32, _I64, ctypes.POINTER(_P)]),
+    "dory_kv_destroy": (None, [_P]),
+    "dory_kv_reset": (_I32, [_P]),
+    "dory_kv_length": (_I64, [_P]),
+    "dory_kv_slot": (_I32, [_P, _I32, _I32, ctypes.POINTER(dory_kv_slot_info)]),
+    "dory_prefill": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
+    "dory_decode_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
+    "dory_debug_mask": (_I32, [_I32, _I64, _I32, _P, _P]),
+    "dory_status_string": (ctypes.c_char_p, [_I32]),
+    "dory_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libdory.so not found at %s: build it with "
+                "`python -m looped_ngpt_transformer_fwd_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class DoryError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        L = lib()
+        msg = "%s: %s (%s)" % (where, L.dory_status_string(status).decode(),
+                               L.dory_last_error().decode())
+        super().__init__(msg)
+
+
+def check(status, where):
+    if status != DORY_OK:
+        raise DoryError(status, where)
+    return status
+
+
+# Thin wrappers with the C names (status returned, not raised).
+def dory_model_create(cfg, w, out):
+    return lib().dory_model_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(out))
+
+
+def dory_model_destroy(m):
+    lib().dory_model_destroy(m)
+
+
+def dory_schedule(cfg, kinds_out, capacity):
+    return lib().dory_schedule(ctypes.byref(cfg), kinds_out, capacity)
+
+
+def dory_kv_bytes(cfg, mode, k_max, batch, max_seq):
+    return lib().dory_kv_bytes(ctypes.byref(cfg), mode, k_max, batch, max_seq)
+
+
+def dory_workspace_bytes(cfg, batch, tokens):
+    return lib().dory_workspace_bytes(ctypes.byref(cfg), batch, tokens)
+
+
+def dory_kv_bind(m, buf, nbytes, mode, k_max, batch, max_seq, out):
+    return lib().dory_kv_bind(m, buf, nbytes, mode, k_max, batch, max_seq, ctypes.byref(out))
+
+
+def dory_kv_destroy(kv):
+    lib().dory_kv_destroy(kv)
+
+
+def dory_kv_reset(kv):
+    return lib().dory_kv_reset(kv)
+
+
+def dory_kv_length(kv):
+    return lib().dory_kv_length(kv)
+
+
+def dory_kv_slot(kv, sublayer, loop, out):
+    return lib().dory_kv_slot(kv, sublayer, loop, ctypes.byref(out))
+
+
+def dory_prefill(m, kv, tokens, B, T, k, mode, ws, ws_bytes, logits, nxt, hidden, states, stream):
+    return lib().dory_prefill(m, kv, tokens, B, T, k, mode, ws, ws_bytes, logits, nxt, hidden,
+                              states, stream)
+
+
+def dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidden, states, stream):
+    return lib().dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidden,
+                                  states, stream)
+
+
+def dory_debug_mask(window, L, T, out, stream):
+    return lib().dory_debug_mask(window, L, T, out, stream)
+
+
+def dory_status_string(s):
+    return lib().dory_status_string(s).decode()
+
+
+def dory_last_error():
+    return lib().dory_last_error().decode()

@@ -1,0 +1,134 @@
+// Host-side launchers of the gfx950 kernels. Each returns the HIP error of
+// its launch. All pointers are device pointers; bf16 values are passed as
+// their 16-bit patterns.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dory {
+
+// ---------------------------------------------------------------- GEMM
+// C[m, n] = sum_k A[m, k] * B[n, k]  (both operands K-contiguous, bf16;
+// accumulation in fp32 on MFMA). K must be a multiple of 64.
+enum GemmEpi {
+  EPI_F32 = 0,     // C (+ split * split_stride) = partial sum of split z
+  EPI_SWIGLU = 1,  // B = [W_up; W_gate] (2F rows); C16[m, f] =
+                   //   bf16(SiLU(s2[f] * gate) * s1[f] * up); N = 2F; no split
+  EPI_LOGITS = 2,  // C[m, n] = s1[n] * acc; no split
+};
+
+struct GemmArgs {
+  const uint16_t* A = nullptr;
+  int64_t lda = 0;
+  const uint16_t* B = nullptr;
+  int64_t ldb = 0;
+  int M = 0, N = 0, K = 0;
+  int nsplit = 1;
+  float* C = nullptr;
+  int64_t ldc = 0;
+  int64_t split_stride = 0;
+  uint16_t* C16 = nullptr;
+  int64_t ldc16 = 0;
+  const float* s1 = nullptr;
+  const float* s2 = nullptr;
+  int F = 0;
+};
+
+// Picks a tile configuration and split factor; `max_split` bounds the split
+// (the workspace holds that many partial outputs).
+int gemm_pick_split(int M, int N, int K, int max_split);
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+
+// ---------------------------------------------------------------- row ops
+// h32/h16[m, :] = E[tok[m], :]; out-of-range ids give NaN rows.
+hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M, int d,
+                        float* h32, uint16_t* h16, float* x32, hipStream_t st);
+
+// nGPT update h <- N(h + alpha (N(y) - h)), y = sum of nsplit partials.
+// If x != null, additionally applies the loop boundary to the result:
+//   state_out (optional) = result; h <- N(result + x).
+hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
+                         int64_t split_stride, int64_t ldy, const float* alpha, int M, int d,
+                         const float* x, float* state_out, float* copy_out, hipStream_t st);
+
+// Loop boundary h <- N(h + x) (also writes the bf16 shadow).
+hipError_t launch_boundary(float* h32, uint16_t* h16, const float* x, int M, int d,
+                           hipStream_t st);
+
+// Copy fp32 rows (row stride `ld_src`) into `dst` [rows, d].
+hipError_t launch_copy_rows(const float* src, int64_t ld_src, float* dst, int rows, int d,
+                            hipStream_t st);
+
+// Split-sum of [nsplit][M][2F] partials and SwiGLU -> a [M, F] bf16.
+hipError_t launch_swiglu_partials(const float* p, int nsplit, int64_t split_stride, int M, int F,
+                                  const float* s_u, const float* s_v, uint16_t* a, hipStream_t st);
+
+// Query/key transform. P = [nsplit][M][d_q + 2 d_kv + d_q] projections
+// (rows m = b * C + t, position p0 + t). Writes
+//   q_hat [B][n_q][C][dh] bf16 = s_qk * N(RoPE(q))
+//   k_hat to kdst, v to vdst (see QkDest), sigma(g) [M][d_q] bf16.
+struct QkDest {
+  // Key rows: kbase + ((b * n_kv + g) * k_rows + row(t)) * dh
+  // V^T:      vbase + ((b * n_kv + g) * dh + d) * v_cols + row(t)
+  // row(t) = (p0 + t - pos_origin) mod ring  (ring = 0: no modulo)
+  uint16_t* kbase;
+  uint16_t* vbase;
+  int64_t k_rows;
+  int64_t v_cols;
+  int64_t pos_origin;
+  int64_t ring;
+};
+hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
+                          int64_t p0, int n_q, int n_kv, int dh, double rope_base,
+                          const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
+                          hipStream_t st);
+
+// Copy cached K / V^T entries of positions [pos_a, pos_b) into the fresh
+// buffers (layout as QkDest with pos_origin = pos_a, no ring).
+hipError_t launch_prefix_copy(const uint16_t* kc, const uint16_t* vc, int64_t c_rows,
+                              int64_t ring, int B, int n_kv, int dh, int64_t pos_a,
+                              int64_t pos_b, uint16_t* kf, uint16_t* vf, int64_t f_rows,
+                              hipStream_t st);
+
+// Persistent-cache store of positions [pos_a, pos_b) from fresh buffers
+// (origin f_origin) into the cache (ring slots if ring > 0).
+hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
+                           int64_t f_origin, int B, int n_kv, int dh, int64_t pos_a,
+                           int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
+                           int64_t ring, hipStream_t st);
+
+// Greedy argmax over rows of [rows, n] fp32, lowest index on ties.
+hipError_t launch_argmax(const float* x, int rows, int n, int32_t* out, hipStream_t st);
+
+// Visibility predicate dump: out[t * L + u] = 1 iff key u is visible to the
+// query at position p0 + t (u < p0 + C), for window (0 = full attention).
+hipError_t launch_debug_mask(int window, int64_t p0, int C, uint8_t* out, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint16_t* q;     // [B][n_q][C][dh]
+  const uint16_t* kc;    // cache K [B][n_kv][c_rows][dh] (nullptr if no prefix)
+  const uint16_t* vc;    // cache V^T [B][n_kv][dh][c_rows]
+  int64_t c_rows;        // rows per (b, g) in the cache
+  int64_t ring;          // 0: linear (row = pos), else row = pos mod ring
+  const uint16_t* kf;    // fresh K [B][n_kv][f_rows][dh]; row = pos - f_origin
+  const uint16_t* vf;    // fresh V^T [B][n_kv][dh][f_rows]
+  int64_t f_rows;
+  int64_t f_origin;      // position of fresh row 0 (multiple of 8, <= p0)
+  const uint16_t* gate;  // sigma(g) [B*C][n_q*dh] bf16
+  uint16_t* z;           // out [B*C][n_q*dh] bf16 (gated, un-normalized)
+  int B, C, n_q, n_kv, dh;
+  int64_t p0;            // position of query row 0
+  int window;            // 0 = full (causal) else sliding window
+  float scale;           // logit scale (sqrt(dh))
+};
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
+
+// Decode attention over cache rows only (current token already stored);
+// split over keys with `part` scratch of decode_attn_part_floats() floats.
+int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit);
+int decode_attn_pick_split(int B, int n_kv, int64_t keys);
+hipError_t launch_attn_decode(const AttnArgs& a, int nsplit, float* part, hipStream_t st);
+
+}  // namespace dory

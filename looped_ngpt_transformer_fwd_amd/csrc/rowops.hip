@@ -1,0 +1,364 @@
+// Bandwidth-bound row kernels of the forward pass: embedding gather, the
+// fused nGPT normalize-and-update (optionally with the loop-boundary
+// re-injection fused in), the query/key transform (RoPE, per-head L2 norm,
+// s_qk) with the K/V placement, KV-cache copies, SwiGLU over split partials,
+// greedy argmax and the mask dump used by the bit-exact tests.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+namespace {
+
+constexpr int NT_ROW = 256;
+constexpr int MAXV = 4;  // float4 per thread: d <= 4 * 4 * 256 = 4096
+
+__global__ void __launch_bounds__(NT_ROW)
+embed_kernel(const int32_t* tok, const uint16_t* E, int vocab, int d, float* h32,
+             uint16_t* h16, float* x32) {
+  const int m = blockIdx.x;
+  const int id = tok[m];
+  const bool ok = id >= 0 && id < vocab;
+  const uint16_t* src = E + (int64_t)(ok ? id : 0) * d;
+  const float nanv = __uint_as_float(0x7fc00000u);
+  for (int i = threadIdx.x; i < d; i += NT_ROW) {
+    const uint16_t v = src[i];
+    const float f = ok ? bf2f(v) : nanv;
+    h32[(int64_t)m * d + i] = f;
+    h16[(int64_t)m * d + i] = ok ? v : (uint16_t)0x7fc0;
+    if (x32) x32[(int64_t)m * d + i] = f;
+  }
+}
+
+// h <- N(h + alpha (N(y) - h)); optional aux copy of the result, optional
+// boundary h <- N(result + x).
+__global__ void __launch_bounds__(NT_ROW)
+update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss, int64_t ldy,
+              const float* alpha, int d, const float* x, float* aux) {
+  __shared__ float red[NT_ROW / 64];
+  const int m = blockIdx.x;
+  const int nv = d >> 2;
+  float4 hv[MAXV], yv[MAXV];
+  float syy = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + i * NT_ROW;
+    if (c < nv) {
+      hv[i] = reinterpret_cast<const float4*>(h32 + (int64_t)m * d)[c];
+      float4 acc = reinterpret_cast<const float4*>(y + (int64_t)m * ldy)[c];
+      for (int s = 1; s < nsplit; ++s) {
+        const float4 t = reinterpret_cast<const float4*>(y + s * ss + (int64_t)m * ldy)[c];
+        acc.x += t.x; acc.y += t.y; acc.z += t.z; acc.w += t.w;
+      }
+      yv[i] = acc;
+      syy += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+    }
+  }
+  const float iy = 1.0f / sqrtf(block_sum<NT_ROW>(syy, red));
+  float stt = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + i * NT_ROW;
+    if (c < nv) {
+      const float4 a = reinterpret_cast<const float4*>(alpha)[c];
+      float4 t;
+      t.x = hv[i].x + a.x * (yv[i].x * iy - hv[i].x);
+      t.y = hv[i].y + a.y * (yv[i].y * iy - hv[i].y);
+      t.z = hv[i].z + a.z * (yv[i].z * iy - hv[i].z);
+      t.w = hv[i].w + a.w * (yv[i].w * iy - hv[i].w);
+      hv[i] = t;
+      stt += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+    }
+  }
+  float it = 1.0f / sqrtf(block_sum<NT_ROW>(stt, red));
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + i * NT_ROW;
+    if (c < nv) {
+      hv[i].x *= it; hv[i].y *= it; hv[i].z *= it; hv[i].w *= it;
+      if (aux) reinterpret_cast<float4*>(aux + (int64_t)m * d)[c] = hv[i];
+    }
+  }
+  if (x) {
+    float suu = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int c = threadIdx.x + i * NT_ROW;
+      if (c < nv) {
+        const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)m * d)[c];
+        hv[i].x += xv.x; hv[i].y += xv.y; hv[i].z += xv.z; hv[i].w += xv.w;
+        suu += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
+      }
+    }
+    it = 1.0f / sqrtf(block_sum<NT_ROW>(suu, red));
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      hv[i].x *= it; hv[i].y *= it; hv[i].z *= it; hv[i].w *= it;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + i * NT_ROW;
+    if (c < nv) {
+      reinterpret_cast<float4*>(h32 + (int64_t)m * d)[c] = hv[i];
+      ushort4 o;
+      o.x = f2bf(hv[i].x); o.y = f2bf(hv[i].y); o.z = f2bf(hv[i].z); o.w = f2bf(hv[i].w);
+      reinterpret_cast<ushort4*>(h16 + (int64_t)m * d)[c] = o;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(NT_ROW)
+boundary_kernel(float* h32, uint16_t* h16, const float* x, int d) {
+  __shared__ float red[NT_ROW / 64];
+  const int m = blockIdx.x;
+  const int nv = d >> 2;
+  float4 v[MAXV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + i * NT_ROW;
+    if (c < nv) {
+      const float4 a = reinterpret_cast<const float4*>(h32 + (int64_t)m * d)[c];
+      const float4 b = reinterpret_cast<const float4*>(x + (int64_t)m * d)[c];
+      v[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+      s += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    }
+  }
+  const float it = 1.0f / sqrtf(block_sum<NT_ROW>(s, red));
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + i * NT_ROW;
+    if (c < nv) {
+      float4 r = make_float4(v[i].x * it, v[i].y * it, v[i].z * it, v[i].w * it);
+      reinterpret_cast<float4*>(h32 + (int64_t)m * d)[c] = r;
+      ushort4 o;
+      o.x = f2bf(r.x); o.y = f2bf(r.y); o.z = f2bf(r.z); o.w = f2bf(r.w);
+      reinterpret_cast<ushort4*>(h16 + (int64_t)m * d)[c] = o;
+    }
+  }
+}
+
+__global__ void copy_rows_kernel(const float* src, int64_t lds, float* dst, int d) {
+  const int m = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[(int64_t)m * d + i] = src[(int64_t)m * lds + i];
+}
+
+__global__ void swiglu_partials_kernel(const float* p, int nsplit, int64_t ss, int M, int F,
+                                       const float* s_u, const float* s_v, uint16_t* a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * F) return;
+  const int64_t m = idx / F;
+  const int f = (int)(idx - m * F);
+  float up = 0.f, gt = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    up += p[s * ss + m * 2 * F + f];
+    gt += p[s * ss + m * 2 * F + F + f];
+  }
+  up *= s_u[f];
+  gt *= s_v[f];
+  a[idx] = f2bf(gt / (1.f + __expf(-gt)) * up);
+}
+
+// One block per token row. dh/2 threads per head (dh in {32, 64, 128}).
+__global__ void __launch_bounds__(NT_ROW)
+qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq, int nkv,
+               int dh, double base, const float* s_qk, uint16_t* qh, QkDest kv,
+               uint16_t* gate) {
+  __shared__ float cs[128], sn[128];
+  const int m = blockIdx.x;
+  const int b = m / C, t = m - b * C;
+  const int64_t pos = p0 + t;
+  const int half = dh >> 1;
+  const int dq = nq * dh, dkv = nkv * dh;
+  const int N = 2 * dq + 2 * dkv;
+  const float* row = P + (int64_t)m * N;
+  for (int i = threadIdx.x; i < half; i += NT_ROW) {
+    const double invf = pow(base, -2.0 * (double)i / (double)dh);
+    double s, c;
+    sincos((double)pos * invf, &s, &c);
+    cs[i] = (float)c;
+    sn[i] = (float)s;
+  }
+  __syncthreads();
+  int64_t krow = pos - kv.pos_origin;
+  if (kv.ring > 0) krow %= kv.ring;
+  const int per_pass = NT_ROW / half;
+  const int i = threadIdx.x % half;
+  for (int hh = threadIdx.x / half; hh < nq + nkv; hh += per_pass) {
+    const int col = hh < nq ? hh * dh : dq + (hh - nq) * dh;
+    float x1 = 0.f, x2 = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      x1 += row[s * ss + col + i];
+      x2 += row[s * ss + col + i + half];
+    }
+    const float r1 = x1 * cs[i] - x2 * sn[i];
+    const float r2 = x2 * cs[i] + x1 * sn[i];
+    float sq = r1 * r1 + r2 * r2;
+    for (int o = half >> 1; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+    const float inv = 1.0f / sqrtf(sq);
+    const uint16_t o1 = f2bf(s_qk[i] * r1 * inv);
+    const uint16_t o2 = f2bf(s_qk[i + half] * r2 * inv);
+    uint16_t* dst;
+    if (hh < nq) {
+      dst = qh + (((int64_t)b * nq + hh) * C + t) * dh;
+    } else {
+      dst = kv.kbase + (((int64_t)b * nkv + (hh - nq)) * kv.k_rows + krow) * dh;
+    }
+    dst[i] = o1;
+    dst[i + half] = o2;
+  }
+  for (int idx = threadIdx.x; idx < dkv; idx += NT_ROW) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += row[s * ss + dq + dkv + idx];
+    const int g = idx / dh, d = idx - g * dh;
+    kv.vbase[(((int64_t)b * nkv + g) * dh + d) * kv.v_cols + krow] = f2bf(v);
+  }
+  for (int idx = threadIdx.x; idx < dq; idx += NT_ROW) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += row[s * ss + dq + 2 * dkv + idx];
+    gate[(int64_t)m * dq + idx] = f2bf(1.0f / (1.0f + __expf(-v)));
+  }
+}
+
+// grid (npos, n_kv, B), block dh
+__global__ void prefix_copy_kernel(const uint16_t* kc, const uint16_t* vc, int64_t c_rows,
+                                   int64_t ring, int nkv, int dh, int64_t pos_a, uint16_t* kf,
+                                   uint16_t* vf, int64_t f_rows) {
+  const int64_t pos = pos_a + blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int64_t bg = (int64_t)b * nkv + g;
+  const int64_t crow = ring > 0 ? pos % ring : pos;
+  const int64_t frow = blockIdx.x;
+  kf[(bg * f_rows + frow) * dh + d] = kc[(bg * c_rows + crow) * dh + d];
+  vf[(bg * dh + d) * f_rows + frow] = vc[(bg * dh + d) * c_rows + crow];
+}
+
+__global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
+                                int64_t f_origin, int nkv, int dh, int64_t pos_a, uint16_t* kc,
+                                uint16_t* vc, int64_t c_rows, int64_t ring) {
+  const int64_t pos = pos_a + blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int64_t bg = (int64_t)b * nkv + g;
+  const int64_t crow = ring > 0 ? pos % ring : pos;
+  const int64_t frow = pos - f_origin;
+  kc[(bg * c_rows + crow) * dh + d] = kf[(bg * f_rows + frow) * dh + d];
+  vc[(bg * dh + d) * c_rows + crow] = vf[(bg * dh + d) * f_rows + frow];
+}
+
+constexpr int NT_ARG = 1024;
+
+__global__ void __launch_bounds__(NT_ARG) argmax_kernel(const float* x, int n, int32_t* out) {
+  __shared__ float bv[NT_ARG / 64];
+  __shared__ int bi[NT_ARG / 64];
+  const float* row = x + (int64_t)blockIdx.x * n;
+  float best = -INFINITY;
+  int idx = n;  // sentinel above every index
+  for (int i = threadIdx.x; i < n; i += NT_ARG) {
+    const float v = row[i];
+    if (v > best) { best = v; idx = i; }  // strided scan: first hit is the lowest index
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (ov > best || (ov == best && oi < idx)) { best = ov; idx = oi; }
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { bv[w] = best; bi[w] = idx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int j = 1; j < NT_ARG / 64; ++j)
+      if (bv[j] > best || (bv[j] == best && bi[j] < idx)) { best = bv[j]; idx = bi[j]; }
+    out[blockIdx.x] = idx < n ? idx : 0;
+  }
+}
+
+__global__ void debug_mask_kernel(int window, int64_t p0, int C, uint8_t* out) {
+  const int64_t L = p0 + C;
+  const int t = blockIdx.x;
+  for (int64_t u = threadIdx.x; u < L; u += blockDim.x)
+    out[(int64_t)t * L + u] = key_visible(p0 + t, u, window) ? 1 : 0;
+}
+
+}  // namespace
+
+hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M, int d,
+                        float* h32, uint16_t* h16, float* x32, hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(NT_ROW), 0, st, tok, E, vocab, d, h32, h16, x32);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
+                         int64_t split_stride, int64_t ldy, const float* alpha, int M, int d,
+                         const float* x, float* state_out, float* copy_out, hipStream_t st) {
+  if (d % 4 != 0 || d > 4 * MAXV * NT_ROW) return hipErrorInvalidValue;
+  float* aux = state_out ? state_out : copy_out;
+  if (state_out && copy_out) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(update_kernel, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
+                     split_stride, ldy, alpha, d, x, aux);
+  return hipGetLastError();
+}
+
+hipError_t launch_boundary(float* h32, uint16_t* h16, const float* x, int M, int d,
+                           hipStream_t st) {
+  if (d % 4 != 0 || d > 4 * MAXV * NT_ROW) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(boundary_kernel, dim3(M), dim3(NT_ROW), 0, st, h32, h16, x, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const float* src, int64_t ld_src, float* dst, int rows, int d,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(rows), dim3(256), 0, st, src, ld_src, dst, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_partials(const float* p, int nsplit, int64_t split_stride, int M, int F,
+                                  const float* s_u, const float* s_v, uint16_t* a, hipStream_t st) {
+  const int64_t n = (int64_t)M * F;
+  hipLaunchKernelGGL(swiglu_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     p, nsplit, split_stride, M, F, s_u, s_v, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
+                          int64_t p0, int n_q, int n_kv, int dh, double rope_base,
+                          const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
+                          hipStream_t st) {
+  if (dh != 32 && dh != 64 && dh != 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qk_prep_kernel, dim3(B * C), dim3(NT_ROW), 0, st, P, nsplit, split_stride, C,
+                     p0, n_q, n_kv, dh, rope_base, s_qk, q_hat, kv, gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_copy(const uint16_t* kc, const uint16_t* vc, int64_t c_rows,
+                              int64_t ring, int B, int n_kv, int dh, int64_t pos_a,
+                              int64_t pos_b, uint16_t* kf, uint16_t* vf, int64_t f_rows,
+                              hipStream_t st) {
+  if (pos_b <= pos_a) return hipSuccess;
+  hipLaunchKernelGGL(prefix_copy_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
+                     kc, vc, c_rows, ring, n_kv, dh, pos_a, kf, vf, f_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
+                           int64_t f_origin, int B, int n_kv, int dh, int64_t pos_a,
+                           int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
+                           int64_t ring, hipStream_t st) {
+  if (pos_b <= pos_a) return hipSuccess;
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
+                     kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* x, int rows, int n, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(NT_ARG), 0, st, x, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_mask(int window, int64_t p0, int C, uint8_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(debug_mask_kernel, dim3(C), dim3(256), 0, st, window, p0, C, out);
+  return hipGetLastError();
+}
+
+}  // namespace dory

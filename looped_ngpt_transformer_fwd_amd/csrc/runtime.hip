@@ -1,0 +1,589 @@
+// Host runtime behind include/dory.h: argument validation, the sublayer
+// schedule, KV-cache layout, workspace planning and the forward executor
+// that enqueues the kernels of one prefill or decode step on a stream.
+//
+// Model structure followed here ("Dory1.0-4B: A Looped Normalized-GPT"):
+// section Training with Loops (input block once, shared recurrent block k
+// times with the input-block output re-injected and the state normalized at
+// both loop boundaries, output block once) and section Last-Loop KV Caching
+// (per-loop versus last-loop cache slots).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dory.h"
+#include "kernels.h"
+
+using namespace dory;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dory_status fail(dory_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+constexpr int kMaxDecodeSplits = 1024;
+constexpr int kMaxGemmSplit = 8;
+constexpr int64_t kLargeM = 1024;  // GEMMs at or above this many rows run unsplit
+
+struct Shape {
+  int d, nq, nkv, dh, F, V, nin, nrec, nout, W, full_every, lm;
+  double base_swa, base_full, scale;
+  int dq() const { return nq * dh; }
+  int dkv() const { return nkv * dh; }
+  int nsub() const { return nin + nrec + nout; }
+  int nqkvg() const { return 2 * dq() + 2 * dkv(); }
+};
+
+dory_status read_shape(const dory_config* c, Shape* s) {
+  if (!c) return fail(DORY_ERR_ARG, "config is NULL");
+  s->d = c->d_model; s->nq = c->n_q_heads; s->nkv = c->n_kv_heads; s->dh = c->head_dim;
+  s->F = c->d_ff; s->V = c->vocab; s->nin = c->n_input; s->nrec = c->n_recurrent;
+  s->nout = c->n_output; s->W = c->window; s->full_every = c->full_every;
+  s->lm = c->has_lm_head ? 1 : 0;
+  s->base_swa = c->rope_base_swa; s->base_full = c->rope_base_full;
+  s->scale = c->softmax_scale > 0 ? c->softmax_scale : std::sqrt((double)c->head_dim);
+  if (s->d <= 0 || s->nq <= 0 || s->nkv <= 0 || s->dh <= 0 || s->F <= 0 || s->V <= 0 ||
+      s->nin < 0 || s->nrec < 0 || s->nout < 0 || s->nsub() <= 0 || s->W <= 0)
+    return fail(DORY_ERR_ARG, "non-positive dimension in config");
+  if (s->nq % s->nkv != 0) return fail(DORY_ERR_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (!c->layer_kinds && s->full_every <= 0) return fail(DORY_ERR_ARG, "full_every must be >= 1");
+  if (!(s->base_swa > 0) || !(s->base_full > 0)) return fail(DORY_ERR_ARG, "RoPE bases must be > 0");
+  const int grp = s->nq / s->nkv;
+  if (s->dh != 32 && s->dh != 64 && s->dh != 128)
+    return fail(DORY_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+    return fail(DORY_ERR_UNSUPPORTED, "n_q/n_kv must be 1, 2, 4 or 8");
+  if (s->d % 64 || s->dq() % 64 || s->F % 64)
+    return fail(DORY_ERR_UNSUPPORTED, "d_model, n_q*head_dim and d_ff must be multiples of 64");
+  if (s->d > 4096) return fail(DORY_ERR_UNSUPPORTED, "d_model above 4096");
+  return DORY_OK;
+}
+
+dory_status build_schedule(const dory_config* c, const Shape& s, std::vector<int>* kinds) {
+  kinds->assign(s.nsub(), DORY_LAYER_MLP);
+  if (c->layer_kinds) {
+    for (int i = 0; i < s.nsub(); ++i) {
+      const int k = c->layer_kinds[i];
+      if (k != DORY_LAYER_ATTN_SWA && k != DORY_LAYER_ATTN_FULL && k != DORY_LAYER_MLP)
+        return fail(DORY_ERR_ARG, "invalid layer kind");
+      (*kinds)[i] = k;
+    }
+    return DORY_OK;
+  }
+  // alternate attention / MLP starting with attention; every full_every-th
+  // attention sublayer (1-based) is full attention
+  int j = 0;
+  for (int i = 0; i < s.nsub(); ++i) {
+    if (i % 2 == 0) {
+      (*kinds)[i] = (j % s.full_every == s.full_every - 1) ? DORY_LAYER_ATTN_FULL : DORY_LAYER_ATTN_SWA;
+      ++j;
+    }
+  }
+  return DORY_OK;
+}
+
+bool is_recurrent(const Shape& s, int i) { return i >= s.nin && i < s.nin + s.nrec; }
+
+int64_t slot_rows(const Shape& s, int kind, int64_t max_seq) {
+  if (kind == DORY_LAYER_ATTN_SWA) return round8(std::min<int64_t>(max_seq, s.W));
+  return round8(max_seq);
+}
+
+size_t slot_bytes(const Shape& s, int kind, int batch, int64_t max_seq) {
+  return (size_t)2 * batch * s.nkv * slot_rows(s, kind, max_seq) * s.dh * 2;
+}
+
+// Workspace layout for B sequences of T tokens.
+struct WsLayout {
+  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, total;
+  int64_t f_rows;
+};
+
+WsLayout plan_ws(const Shape& s, int B, int T) {
+  WsLayout L{};
+  const int64_t M = (int64_t)B * T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.f_rows = round8(T + 7);
+  L.h32 = take(M * s.d * 4);
+  L.h16 = take(M * s.d * 2);
+  L.x32 = take(M * s.d * 4);
+  L.qh = take(M * s.dq() * 2);
+  L.kf = take((size_t)B * s.nkv * L.f_rows * s.dh * 2);
+  L.vf = take((size_t)B * s.nkv * L.f_rows * s.dh * 2);
+  L.gate = take(M * s.dq() * 2);
+  L.z = take(M * s.dq() * 2);
+  L.a = take(M * s.F * 2);
+  int64_t ncols = std::max<int64_t>(s.nqkvg(), s.d);
+  int64_t nsplit = 1;
+  if (M < kLargeM) {
+    ncols = std::max<int64_t>(ncols, 2 * (int64_t)s.F);
+    nsplit = kMaxGemmSplit;
+  }
+  L.P = take((size_t)nsplit * M * ncols * 4);
+  L.part = take((size_t)decode_attn_part_floats(B, s.nq, s.dh, kMaxDecodeSplits) * 4);
+  L.logits = s.lm ? take((size_t)B * s.V * 4) : 0;
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct dory_model {
+  Shape s;
+  std::vector<int> kinds;
+  std::vector<dory_sublayer_weights> sub;
+  const uint16_t* embed;
+  const uint16_t* lm_head;
+  const float* s_z;
+};
+
+struct dory_kv {
+  const dory_model* m;
+  uint8_t* base;
+  size_t bytes;
+  dory_cache_mode mode;
+  int k_max, batch;
+  int64_t max_seq;
+  int64_t len;
+  int k_used;
+  bool invalid;
+  // per sublayer: offset of slot 0 (or SIZE_MAX for MLP), rows and ring
+  std::vector<size_t> off;
+  std::vector<int> nslots;
+  std::vector<int64_t> rows, ring;
+};
+
+namespace {
+
+struct SlotPtr {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t rows, ring;
+};
+
+SlotPtr slot_ptr(const dory_kv* kv, int sub, int slot) {
+  const Shape& s = kv->m->s;
+  const size_t half = (size_t)kv->batch * s.nkv * kv->rows[sub] * s.dh * 2;
+  uint8_t* p = kv->base + kv->off[sub] + (size_t)slot * 2 * half;
+  return SlotPtr{reinterpret_cast<uint16_t*>(p), reinterpret_cast<uint16_t*>(p + half),
+                 kv->rows[sub], kv->ring[sub]};
+}
+
+struct Ctx {
+  dory_model* m;
+  dory_kv* kv;
+  const Shape& s;
+  int B, T;
+  int64_t M, p0;
+  uint8_t* ws;
+  WsLayout L;
+  hipStream_t st;
+  float* h32() const { return reinterpret_cast<float*>(ws + L.h32); }
+  uint16_t* h16() const { return reinterpret_cast<uint16_t*>(ws + L.h16); }
+  float* x32() const { return reinterpret_cast<float*>(ws + L.x32); }
+  uint16_t* qh() const { return reinterpret_cast<uint16_t*>(ws + L.qh); }
+  uint16_t* kf() const { return reinterpret_cast<uint16_t*>(ws + L.kf); }
+  uint16_t* vf() const { return reinterpret_cast<uint16_t*>(ws + L.vf); }
+  uint16_t* gate() const { return reinterpret_cast<uint16_t*>(ws + L.gate); }
+  uint16_t* z() const { return reinterpret_cast<uint16_t*>(ws + L.z); }
+  uint16_t* a() const { return reinterpret_cast<uint16_t*>(ws + L.a); }
+  float* P() const { return reinterpret_cast<float*>(ws + L.P); }
+  float* part() const { return reinterpret_cast<float*>(ws + L.part); }
+  float* logits_scratch() const { return reinterpret_cast<float*>(ws + L.logits); }
+};
+
+#define HIPCHK(expr)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      g_last_error = std::string(#expr) + ": " + hipGetErrorString(e_);           \
+      return DORY_ERR_HIP;                                                        \
+    }                                                                             \
+  } while (0)
+
+// y = A W^T into P (split partials), returns the split used.
+dory_status gemm_f32(Ctx& c, const uint16_t* A, int64_t lda, const void* W, int N, int K,
+                     int64_t M, int* nsplit_out) {
+  GemmArgs g;
+  g.A = A; g.lda = lda;
+  g.B = reinterpret_cast<const uint16_t*>(W); g.ldb = K;
+  g.M = (int)M; g.N = N; g.K = K;
+  g.nsplit = gemm_pick_split((int)M, N, K, M < kLargeM ? kMaxGemmSplit : 1);
+  g.C = c.P(); g.ldc = N; g.split_stride = M * N;
+  HIPCHK(launch_gemm(g, EPI_F32, c.st));
+  *nsplit_out = g.nsplit;
+  return DORY_OK;
+}
+
+// The update after a sublayer, with the loop-boundary fusion options.
+struct UpdateOpts {
+  const float* x = nullptr;  // apply boundary N(r + x) after the update
+  float* aux = nullptr;      // copy of the post-update value
+};
+
+dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const UpdateOpts& uo) {
+  const Shape& s = c.s;
+  const dory_sublayer_weights& w = c.m->sub[i];
+  const int kind = c.m->kinds[i];
+  const bool full = kind == DORY_LAYER_ATTN_FULL;
+  const double base = full ? s.base_full : s.base_swa;
+  const SlotPtr sp = slot_ptr(c.kv, i, slot);
+  int ns = 1;
+  dory_status st = gemm_f32(c, c.h16(), s.d, w.w_qkvg, s.nqkvg(), s.d, c.M, &ns);
+  if (st != DORY_OK) return st;
+  const int64_t split_stride = c.M * s.nqkvg();
+
+  AttnArgs aa{};
+  aa.q = c.qh();
+  aa.kc = sp.k; aa.vc = sp.v; aa.c_rows = sp.rows; aa.ring = sp.ring;
+  aa.gate = c.gate(); aa.z = c.z();
+  aa.B = c.B; aa.C = c.T; aa.n_q = s.nq; aa.n_kv = s.nkv; aa.dh = s.dh;
+  aa.p0 = c.p0; aa.window = full ? 0 : s.W; aa.scale = (float)s.scale;
+
+  if (c.T == 1) {
+    // decode: the current token's K/V go straight into the cache slot (the
+    // last-loop rule read literally: overwrite at every loop), then the
+    // attention reads the cache only
+    QkDest kd{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring};
+    HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh, base,
+                          w.s_qk, c.qh(), kd, c.gate(), c.st));
+    const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
+    int nsd = decode_attn_pick_split(c.B, s.nkv, c.p0 - lo + 1);
+    if (nsd > kMaxDecodeSplits) return fail(DORY_ERR_UNSUPPORTED, "context too long for decode splits");
+    HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
+  } else {
+    // prefill: fresh K/V of the step live in the workspace, rows counted from
+    // f_origin (the step's first position rounded down to a multiple of 8);
+    // cached positions [f_origin, p0) are copied in front of them
+    const int64_t f_origin = c.p0 / 8 * 8;
+    QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
+    HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh, base,
+                          w.s_qk, c.qh(), kd, c.gate(), c.st));
+    HIPCHK(launch_prefix_copy(sp.k, sp.v, sp.rows, sp.ring, c.B, s.nkv, s.dh, f_origin, c.p0,
+                              c.kf(), c.vf(), c.L.f_rows, c.st));
+    aa.kf = c.kf(); aa.vf = c.vf(); aa.f_rows = c.L.f_rows; aa.f_origin = f_origin;
+    HIPCHK(launch_attn_prefill(aa, c.st));
+    if (write) {
+      // persistent store after the step's attention; a ring keeps only the
+      // newest `ring` positions
+      int64_t pa = c.p0;
+      if (sp.ring > 0) pa = std::max<int64_t>(pa, c.p0 + c.T - sp.ring);
+      HIPCHK(launch_kv_write(c.kf(), c.vf(), c.L.f_rows, f_origin, c.B, s.nkv, s.dh, pa,
+                             c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st));
+    }
+  }
+  st = gemm_f32(c, c.z(), s.dq(), w.w_o, s.d, s.dq(), c.M, &ns);
+  if (st != DORY_OK) return st;
+  HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
+                       uo.aux, nullptr, c.st));
+  return DORY_OK;
+}
+
+dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
+  const Shape& s = c.s;
+  const dory_sublayer_weights& w = c.m->sub[i];
+  const int ns_up = gemm_pick_split((int)c.M, 2 * s.F, s.d, c.M < kLargeM ? kMaxGemmSplit : 1);
+  if (ns_up == 1) {
+    GemmArgs g;
+    g.A = c.h16(); g.lda = s.d;
+    g.B = reinterpret_cast<const uint16_t*>(w.w_upgate); g.ldb = s.d;
+    g.M = (int)c.M; g.N = 2 * s.F; g.K = s.d; g.nsplit = 1;
+    g.C16 = c.a(); g.ldc16 = s.F; g.s1 = w.s_u; g.s2 = w.s_v; g.F = s.F;
+    HIPCHK(launch_gemm(g, EPI_SWIGLU, c.st));
+  } else {
+    int ns = 1;
+    dory_status st = gemm_f32(c, c.h16(), s.d, w.w_upgate, 2 * s.F, s.d, c.M, &ns);
+    if (st != DORY_OK) return st;
+    HIPCHK(launch_swiglu_partials(c.P(), ns, c.M * 2 * s.F, (int)c.M, s.F, w.s_u, w.s_v, c.a(),
+                                  c.st));
+  }
+  int ns = 1;
+  dory_status st = gemm_f32(c, c.a(), s.F, w.w_down, s.d, s.F, c.M, &ns);
+  if (st != DORY_OK) return st;
+  HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
+                       uo.aux, nullptr, c.st));
+  return DORY_OK;
+}
+
+dory_status run_sublayer(Ctx& c, int i, int slot, bool write, const UpdateOpts& uo) {
+  if (c.m->kinds[i] == DORY_LAYER_MLP) return mlp_sublayer(c, i, uo);
+  return attention_sublayer(c, i, slot, write, uo);
+}
+
+dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_t* next,
+                     float* hidden, float* states) {
+  const Shape& s = c.s;
+  const int64_t Md = c.M * s.d;
+  const bool per_loop = c.kv->mode == DORY_CACHE_PER_LOOP;
+  HIPCHK(launch_embed(tokens, c.m->embed, s.V, (int)c.M, s.d, c.h32(), c.h16(),
+                      s.nin == 0 ? c.x32() : nullptr, c.st));
+  for (int i = 0; i < s.nin; ++i) {
+    UpdateOpts uo;
+    if (i == s.nin - 1) uo.aux = c.x32();  // x: output of the input block
+    dory_status st = run_sublayer(c, i, 0, true, uo);
+    if (st != DORY_OK) return st;
+  }
+  // loop 1 starts from N(x + x) = N(x): x is already unit-norm when it comes
+  // out of an update; a bare embedding is normalized here
+  if (s.nin == 0) HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
+  for (int it = 0; it < k; ++it) {
+    const int slot = per_loop ? it : 0;
+    const bool write = per_loop || it == k - 1;
+    float* st_out = states ? states + (int64_t)it * Md : nullptr;
+    if (s.nrec == 0) {
+      if (it > 0) HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
+      if (st_out) HIPCHK(hipMemcpyAsync(st_out, c.h32(), Md * 4, hipMemcpyDeviceToDevice, c.st));
+      continue;
+    }
+    for (int i = s.nin; i < s.nin + s.nrec; ++i) {
+      UpdateOpts uo;
+      if (i == s.nin + s.nrec - 1) {
+        uo.aux = st_out;                        // s_{it+1}
+        if (it < k - 1) uo.x = c.x32();         // boundary into the next loop
+      }
+      dory_status st = run_sublayer(c, i, slot, write, uo);
+      if (st != DORY_OK) return st;
+    }
+  }
+  for (int i = s.nin + s.nrec; i < s.nsub(); ++i) {
+    dory_status st = run_sublayer(c, i, 0, true, UpdateOpts());
+    if (st != DORY_OK) return st;
+  }
+  if (hidden) HIPCHK(hipMemcpyAsync(hidden, c.h32(), Md * 4, hipMemcpyDeviceToDevice, c.st));
+  if (logits || next) {
+    float* out = logits ? logits : c.logits_scratch();
+    GemmArgs g;
+    g.A = c.h16() + (int64_t)(c.T - 1) * s.d; g.lda = (int64_t)c.T * s.d;
+    g.B = c.m->lm_head; g.ldb = s.d;
+    g.M = c.B; g.N = s.V; g.K = s.d; g.nsplit = 1;
+    g.C = out; g.ldc = s.V; g.s1 = c.m->s_z;
+    HIPCHK(launch_gemm(g, EPI_LOGITS, c.st));
+    if (next) HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
+  }
+  return DORY_OK;
+}
+
+dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                        int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes, float* logits,
+                        int32_t* next, float* hidden, float* states, void* stream) {
+  if (!m || !kv || !tokens) return fail(DORY_ERR_ARG, "model, cache and tokens must be non-NULL");
+  if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
+  if (B <= 0 || T <= 0) return fail(DORY_ERR_ARG, "B and T must be >= 1");
+  if (k < 1) return fail(DORY_ERR_ARG, "loop count k must be >= 1");
+  if (kv->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure; call dory_kv_reset");
+  if (mode != kv->mode) return fail(DORY_ERR_MODE, "cache mode differs from the bound mode");
+  if (mode == DORY_CACHE_PER_LOOP) {
+    if (k > kv->k_max) return fail(DORY_ERR_MODE, "per-loop cache: k exceeds k_max");
+    if (kv->k_used != 0 && kv->k_used != k)
+      return fail(DORY_ERR_MODE, "per-loop cache: k differs from earlier steps");
+  }
+  if (B > kv->batch) return fail(DORY_ERR_CAPACITY, "B exceeds the bound batch");
+  if (B < kv->batch) return fail(DORY_ERR_ARG, "B must equal the bound batch");
+  if (kv->len + T > kv->max_seq) return fail(DORY_ERR_CAPACITY, "cache capacity exceeded");
+  if (!ws) return fail(DORY_ERR_ARG, "workspace is NULL");
+  const Shape& s = m->s;
+  WsLayout L = plan_ws(s, B, T);
+  if (ws_bytes < L.total) return fail(DORY_ERR_WORKSPACE, "workspace smaller than dory_workspace_bytes()");
+  if ((logits || next) && !s.lm) return fail(DORY_ERR_ARG, "model has no LM head");
+  Ctx c{m, kv, s, B, T, (int64_t)B * T, kv->len, reinterpret_cast<uint8_t*>(ws), L,
+        reinterpret_cast<hipStream_t>(stream)};
+  dory_status st = run_step(c, tokens, k, logits, next, hidden, states);
+  if (st != DORY_OK) {
+    if (st == DORY_ERR_HIP) kv->invalid = true;
+    return st;
+  }
+  kv->len += T;
+  if (mode == DORY_CACHE_PER_LOOP) kv->k_used = k;
+  return DORY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dory_status dory_schedule(const dory_config* cfg, int32_t* kinds_out, int32_t capacity) {
+  Shape s;
+  dory_status st = read_shape(cfg, &s);
+  if (st != DORY_OK) return st;
+  if (!kinds_out || capacity < s.nsub()) return fail(DORY_ERR_ARG, "kinds_out too small");
+  std::vector<int> kinds;
+  st = build_schedule(cfg, s, &kinds);
+  if (st != DORY_OK) return st;
+  for (int i = 0; i < s.nsub(); ++i) kinds_out[i] = kinds[i];
+  return DORY_OK;
+}
+
+dory_status dory_model_create(const dory_config* cfg, const dory_weights* w, dory_model** out) {
+  if (!out) return fail(DORY_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  Shape s;
+  dory_status st = read_shape(cfg, &s);
+  if (st != DORY_OK) return st;
+  if (!w || !w->embed || !w->sublayers) return fail(DORY_ERR_ARG, "weights incomplete");
+  if (s.lm && (!w->lm_head || !w->s_z)) return fail(DORY_ERR_ARG, "LM head weights missing");
+  std::vector<int> kinds;
+  st = build_schedule(cfg, s, &kinds);
+  if (st != DORY_OK) return st;
+  for (int i = 0; i < s.nsub(); ++i) {
+    const dory_sublayer_weights& sw = w->sublayers[i];
+    if (!sw.alpha) return fail(DORY_ERR_ARG, "sublayer " + std::to_string(i) + ": alpha missing");
+    if (kinds[i] == DORY_LAYER_MLP) {
+      if (!sw.w_upgate || !sw.w_down || !sw.s_u || !sw.s_v)
+        return fail(DORY_ERR_ARG, "sublayer " + std::to_string(i) + ": MLP weights missing");
+    } else if (!sw.w_qkvg || !sw.w_o || !sw.s_qk) {
+      return fail(DORY_ERR_ARG, "sublayer " + std::to_string(i) + ": attention weights missing");
+    }
+  }
+  dory_model* m = new dory_model();
+  m->s = s;
+  m->kinds = kinds;
+  m->sub.assign(w->sublayers, w->sublayers + s.nsub());
+  m->embed = reinterpret_cast<const uint16_t*>(w->embed);
+  m->lm_head = reinterpret_cast<const uint16_t*>(w->lm_head);
+  m->s_z = w->s_z;
+  *out = m;
+  return DORY_OK;
+}
+
+void dory_model_destroy(dory_model* m) { delete m; }
+
+size_t dory_kv_bytes(const dory_config* cfg, dory_cache_mode mode, int32_t k_max, int32_t batch,
+                     int64_t max_seq) {
+  Shape s;
+  if (read_shape(cfg, &s) != DORY_OK) return 0;
+  if (k_max < 1 || batch < 1 || max_seq < 1) return 0;
+  if (mode != DORY_CACHE_LAST_LOOP && mode != DORY_CACHE_PER_LOOP) return 0;
+  std::vector<int> kinds;
+  if (build_schedule(cfg, s, &kinds) != DORY_OK) return 0;
+  size_t total = 0;
+  for (int i = 0; i < s.nsub(); ++i) {
+    if (kinds[i] == DORY_LAYER_MLP) continue;
+    const int slots = (mode == DORY_CACHE_PER_LOOP && is_recurrent(s, i)) ? k_max : 1;
+    total += slots * slot_bytes(s, kinds[i], batch, max_seq);
+  }
+  return total;
+}
+
+size_t dory_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t tokens) {
+  Shape s;
+  if (read_shape(cfg, &s) != DORY_OK) return 0;
+  if (batch < 1 || tokens < 1) return 0;
+  return plan_ws(s, batch, tokens).total;
+}
+
+dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dory_cache_mode mode,
+                         int32_t k_max, int32_t batch, int64_t max_seq, dory_kv** out) {
+  if (!out) return fail(DORY_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!m || !kv_dev) return fail(DORY_ERR_ARG, "model and buffer must be non-NULL");
+  if (mode != DORY_CACHE_LAST_LOOP && mode != DORY_CACHE_PER_LOOP)
+    return fail(DORY_ERR_MODE, "unknown cache mode");
+  if (k_max < 1 || batch < 1 || max_seq < 1) return fail(DORY_ERR_ARG, "k_max, batch, max_seq must be >= 1");
+  const Shape& s = m->s;
+  dory_kv* kv = new dory_kv();
+  kv->m = m; kv->base = reinterpret_cast<uint8_t*>(kv_dev); kv->bytes = kv_bytes;
+  kv->mode = mode; kv->k_max = k_max; kv->batch = batch; kv->max_seq = max_seq;
+  kv->len = 0; kv->k_used = 0; kv->invalid = false;
+  kv->off.assign(s.nsub(), (size_t)-1);
+  kv->nslots.assign(s.nsub(), 0);
+  kv->rows.assign(s.nsub(), 0);
+  kv->ring.assign(s.nsub(), 0);
+  size_t off = 0;
+  for (int i = 0; i < s.nsub(); ++i) {
+    const int kind = m->kinds[i];
+    if (kind == DORY_LAYER_MLP) continue;
+    const int slots = (mode == DORY_CACHE_PER_LOOP && is_recurrent(s, i)) ? k_max : 1;
+    kv->off[i] = off;
+    kv->nslots[i] = slots;
+    kv->rows[i] = slot_rows(s, kind, max_seq);
+    kv->ring[i] = kind == DORY_LAYER_ATTN_SWA ? kv->rows[i] : 0;
+    off += slots * slot_bytes(s, kind, batch, max_seq);
+  }
+  if (kv_bytes < off) {
+    delete kv;
+    return fail(DORY_ERR_CAPACITY, "KV buffer smaller than dory_kv_bytes()");
+  }
+  *out = kv;
+  return DORY_OK;
+}
+
+void dory_kv_destroy(dory_kv* kv) { delete kv; }
+
+dory_status dory_kv_reset(dory_kv* kv) {
+  if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");
+  kv->len = 0;
+  kv->k_used = 0;
+  kv->invalid = false;
+  return DORY_OK;
+}
+
+int64_t dory_kv_length(const dory_kv* kv) { return kv ? kv->len : -1; }
+
+dory_status dory_kv_slot(const dory_kv* kv, int32_t sublayer, int32_t loop, dory_kv_slot_info* out) {
+  if (!kv || !out) return fail(DORY_ERR_ARG, "NULL argument");
+  const Shape& s = kv->m->s;
+  if (sublayer < 0 || sublayer >= s.nsub() || kv->m->kinds[sublayer] == DORY_LAYER_MLP)
+    return fail(DORY_ERR_ARG, "not an attention sublayer");
+  int slot = 0;
+  if (kv->nslots[sublayer] > 1) {
+    if (loop < 0 || loop >= kv->nslots[sublayer]) return fail(DORY_ERR_ARG, "loop out of range");
+    slot = loop;
+  }
+  SlotPtr p = slot_ptr(kv, sublayer, slot);
+  out->k = p.k; out->v = p.v; out->rows = p.rows; out->ring = p.ring;
+  return DORY_OK;
+}
+
+dory_status dory_prefill(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                         int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
+                         float* logits, int32_t* next, float* hidden, float* states,
+                         void* stream) {
+  return step_common(m, kv, tokens, B, T, k, mode, ws, ws_bytes, logits, next, hidden, states,
+                     stream);
+}
+
+dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                             int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
+                             float* logits, int32_t* next, float* hidden, float* states,
+                             void* stream) {
+  return step_common(m, kv, tokens, B, 1, k, mode, ws, ws_bytes, logits, next, hidden, states,
+                     stream);
+}
+
+dory_status dory_debug_mask(int32_t window, int64_t L, int32_t T, uint8_t* out, void* stream) {
+  if (!out || T < 1 || L < 0 || window < 0) return fail(DORY_ERR_ARG, "bad mask arguments");
+  hipError_t e = launch_debug_mask(window, L, T, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DORY_ERR_HIP, hipGetErrorString(e));
+  return DORY_OK;
+}
+
+const char* dory_status_string(dory_status s) {
+  switch (s) {
+    case DORY_OK: return "ok";
+    case DORY_ERR_ARG: return "invalid argument";
+    case DORY_ERR_MODE: return "cache mode / loop count mismatch";
+    case DORY_ERR_CAPACITY: return "cache capacity exceeded";
+    case DORY_ERR_WORKSPACE: return "workspace too small";
+    case DORY_ERR_UNSUPPORTED: return "unsupported shape";
+    case DORY_ERR_HIP: return "HIP launch failure";
+    case DORY_ERR_STATE: return "cache invalid";
+  }
+  return "unknown status";
+}
+
+const char* dory_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

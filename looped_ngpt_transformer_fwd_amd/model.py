@@ -1,0 +1,199 @@
+"""Python handles over the C ABI. PyTorch supplies device memory and the
+stream; every step of the forward pass runs in libdory.so."""
+import ctypes
+
+import torch
+
+from . import _lib as C
+
+KIND_CODE = {"swa": C.DORY_LAYER_ATTN_SWA, "full": C.DORY_LAYER_ATTN_FULL, "mlp": C.DORY_LAYER_MLP}
+MODE_CODE = {"last_loop": C.DORY_CACHE_LAST_LOOP, "per_loop": C.DORY_CACHE_PER_LOOP}
+
+
+def make_config(shape):
+    """dory_config from any object with the Shape attributes (d_model,
+    n_q_heads, ..., layer_kinds as a tuple of 'swa'/'full'/'mlp' or None)."""
+    cfg = C.dory_config()
+    cfg.d_model = shape.d_model
+    cfg.n_q_heads = shape.n_q_heads
+    cfg.n_kv_heads = shape.n_kv_heads
+    cfg.head_dim = shape.head_dim
+    cfg.d_ff = shape.d_ff
+    cfg.vocab = shape.vocab
+    cfg.n_input = shape.n_input
+    cfg.n_recurrent = shape.n_recurrent
+    cfg.n_output = shape.n_output
+    cfg.window = shape.window
+    cfg.full_every = getattr(shape, "full_every", 4)
+    cfg.has_lm_head = 1 if getattr(shape, "has_lm_head", True) else 0
+    cfg.rope_base_swa = shape.rope_base_swa
+    cfg.rope_base_full = shape.rope_base_full
+    cfg.softmax_scale = 0.0
+    kinds = getattr(shape, "layer_kinds", None)
+    cfg._kinds_keepalive = None
+    if kinds is not None:
+        arr = (ctypes.c_int32 * len(kinds))(*[KIND_CODE[k] for k in kinds])
+        cfg._kinds_keepalive = arr
+        cfg.layer_kinds = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return cfg
+
+
+def schedule(shape):
+    cfg = make_config(shape)
+    n = shape.n_input + shape.n_recurrent + shape.n_output
+    out = (ctypes.c_int32 * n)()
+    C.check(C.dory_schedule(cfg, out, n), "dory_schedule")
+    inv = {v: k for k, v in KIND_CODE.items()}
+    return [inv[x] for x in out]
+
+
+def kv_bytes(shape, mode, k_max, batch, max_seq):
+    return C.dory_kv_bytes(make_config(shape), MODE_CODE[mode], k_max, batch, max_seq)
+
+
+def workspace_bytes(shape, batch, tokens):
+    return C.dory_workspace_bytes(make_config(shape), batch, tokens)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Model:
+    """Wraps dory_model. `tensors` maps weight names to device tensors:
+    embed, lm_head, s_z, sub{i}.w_qkvg, sub{i}.w_o, sub{i}.s_qk,
+    sub{i}.w_upgate, sub{i}.w_down, sub{i}.s_u, sub{i}.s_v, sub{i}.alpha
+    (bf16 matrices in [out, in] layout, fp32 vectors)."""
+
+    def __init__(self, shape, tensors):
+        self.shape = shape
+        self.cfg = make_config(shape)
+        self.tensors = tensors
+        self.kinds = schedule(shape)
+        n = len(self.kinds)
+        subs = (C.dory_sublayer_weights * n)()
+        for i, kind in enumerate(self.kinds):
+            s = subs[i]
+            s.alpha = _ptr(tensors[f"sub{i}.alpha"])
+            if kind == "mlp":
+                s.w_upgate = _ptr(tensors[f"sub{i}.w_upgate"])
+                s.w_down = _ptr(tensors[f"sub{i}.w_down"])
+                s.s_u = _ptr(tensors[f"sub{i}.s_u"])
+                s.s_v = _ptr(tensors[f"sub{i}.s_v"])
+            else:
+                s.w_qkvg = _ptr(tensors[f"sub{i}.w_qkvg"])
+                s.w_o = _ptr(tensors[f"sub{i}.w_o"])
+                s.s_qk = _ptr(tensors[f"sub{i}.s_qk"])
+        w = C.dory_weights()
+        w.embed = _ptr(tensors["embed"])
+        if getattr(shape, "has_lm_head", True):
+            w.lm_head = _ptr(tensors["lm_head"])
+            w.s_z = _ptr(tensors["s_z"])
+        w.sublayers = subs
+        self._subs = subs
+        self.handle = ctypes.c_void_p()
+        C.check(C.dory_model_create(self.cfg, w, self.handle), "dory_model_create")
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        try:
+            if h is not None and h.value:
+                C.dory_model_destroy(h)
+        except Exception:  # interpreter shutdown
+            pass
+        self.handle = None
+
+    def workspace(self, batch, tokens, device="cuda"):
+        n = workspace_bytes(self.shape, batch, tokens)
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+    def kv_cache(self, mode, k_max, batch, max_seq, device="cuda"):
+        return KVCache(self, mode, k_max, batch, max_seq, device)
+
+    def prefill(self, kv, tokens, k, ws=None, logits=True, next_token=False, hidden=False,
+                states=False):
+        """tokens: int32 device tensor [B, T]. Returns a dict of the requested
+        outputs (logits [B, V], next [B], hidden [B, T, d], states [k, B, T, d])."""
+        B, T = tokens.shape
+        return self._step(kv, tokens, B, T, k, ws, logits, next_token, hidden, states, decode=False)
+
+    def decode_step(self, kv, tokens, k, ws=None, logits=True, next_token=True, hidden=False,
+                    states=False):
+        """tokens: int32 device tensor [B]."""
+        B = tokens.shape[0]
+        return self._step(kv, tokens, B, 1, k, ws, logits, next_token, hidden, states, decode=True)
+
+    def _step(self, kv, tokens, B, T, k, ws, logits, next_token, hidden, states, decode):
+        dev = tokens.device
+        sh = self.shape
+        if ws is None:
+            ws = self.workspace(B, T, dev)
+        out = {}
+        lg = torch.empty(B, sh.vocab, dtype=torch.float32, device=dev) if logits else None
+        nx = torch.empty(B, dtype=torch.int32, device=dev) if next_token else None
+        hd = torch.empty(B, T, sh.d_model, dtype=torch.float32, device=dev) if hidden else None
+        stt = torch.empty(k, B, T, sh.d_model, dtype=torch.float32, device=dev) if states else None
+        mode = kv.mode_code
+        if decode:
+            st = C.dory_decode_step(self.handle, kv.handle, _ptr(tokens), B, k, mode, _ptr(ws),
+                                    ws.numel(), _ptr(lg), _ptr(nx), _ptr(hd), _ptr(stt), _stream())
+            where = "dory_decode_step"
+        else:
+            st = C.dory_prefill(self.handle, kv.handle, _ptr(tokens), B, T, k, mode, _ptr(ws),
+                                ws.numel(), _ptr(lg), _ptr(nx), _ptr(hd), _ptr(stt), _stream())
+            where = "dory_prefill"
+        C.check(st, where)
+        if lg is not None:
+            out["logits"] = lg
+        if nx is not None:
+            out["next"] = nx
+        if hd is not None:
+            out["hidden"] = hd
+        if stt is not None:
+            out["states"] = stt
+        return out
+
+
+class KVCache:
+    def __init__(self, model, mode, k_max, batch, max_seq, device="cuda"):
+        self.model = model
+        self.mode = mode
+        self.mode_code = MODE_CODE[mode]
+        n = kv_bytes(model.shape, mode, k_max, batch, max_seq)
+        if n == 0:
+            raise ValueError("invalid cache parameters")
+        self.buffer = torch.empty(n, dtype=torch.uint8, device=device)
+        self.handle = ctypes.c_void_p()
+        C.check(C.dory_kv_bind(model.handle, _ptr(self.buffer), n, self.mode_code, k_max, batch,
+                               max_seq, self.handle), "dory_kv_bind")
+
+    @property
+    def length(self):
+        return C.dory_kv_length(self.handle)
+
+    def reset(self):
+        C.check(C.dory_kv_reset(self.handle), "dory_kv_reset")
+
+    def slot(self, sublayer, loop=0):
+        info = C.dory_kv_slot_info()
+        C.check(C.dory_kv_slot(self.handle, sublayer, loop, info), "dory_kv_slot")
+        return info
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        try:
+            if h is not None and h.value:
+                C.dory_kv_destroy(h)
+        except Exception:  # interpreter shutdown
+            pass
+        self.handle = None
+
+
+def debug_mask(window, L, T, device="cuda"):
+    out = torch.empty(T, L + T, dtype=torch.uint8, device=device)
+    C.check(C.dory_debug_mask(window, L, T, _ptr(out), _stream()), "dory_debug_mask")
+    return out

@@ -12,5 +12,5 @@ module docstring.
 from .ref import (  # noqa: F401
     Cache, OracleModel, attention_core, kv_bytes,
     layer_kinds, l2_normalize, ngpt_update, rope, rope_inv_freq, silu,
-    swiglu, greedy, sigmoid, softmax_rows, block_of,
+    swiglu, greedy, sigmoid, softmax_rows, block_of, visible,
 )

@@ -142,6 +142,17 @@ def greedy(logits: np.ndarray) -> np.ndarray:
     return np.argmax(logits, axis=-1).astype(np.int32)
 
 
+def visible(qpos: np.ndarray, kpos: np.ndarray, window: Optional[int]) -> np.ndarray:
+    """[T, L] boolean: key position u is visible to the query at position p iff
+    u <= p and, for a sliding-window layer, p - u < window (reading R3)."""
+    qpos = np.asarray(qpos)[:, None]
+    kpos = np.asarray(kpos)[None, :]
+    ok = kpos <= qpos
+    if window is not None:
+        ok &= (qpos - kpos) < window
+    return ok
+
+
 def attention_core(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                    qpos: np.ndarray, kpos: np.ndarray,
                    window: Optional[int], tau: float,
@@ -169,10 +180,7 @@ def attention_core(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         if sel.size == 0:
             raise ValueError("query without keys")
         ks, ke = sel[0], sel[-1] + 1
-        kp = kpos[ks:ke]
-        allowed = kp[None, :] <= qp[:, None]
-        if window is not None:
-            allowed &= (qp[:, None] - kp[None, :]) < window
+        allowed = visible(qp, kpos[ks:ke], window)
         for g in range(nkv):
             qq = q[:, g * grp:(g + 1) * grp, t0:t1, :]            # [B, grp, Tc, dh]
             kk = k[:, g, ks:ke, :]                                  # [B, Lc, dh]

@@ -96,7 +96,8 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
 
 
 def f64_from_bf16_bits(b: np.ndarray) -> np.ndarray:
-    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def unit_rows(seed: int, name: str, rows: int, cols: int) -> np.ndarray:

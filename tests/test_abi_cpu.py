@@ -1,0 +1,179 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports every declared symbol, the schedule and byte formulas agree with the
+oracle, and every validation path returns its status without touching the
+device (fake device pointers are never dereferenced on the host)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from looped_ngpt_transformer_fwd_amd import _lib as C
+from looped_ngpt_transformer_fwd_amd import model as M
+from oracle import ref
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dory.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dory_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in C.SIGNATURES, n
+
+
+@pytest.mark.parametrize("shape", [synth.FULL, synth.TINY, synth.TINY_REC_FULL, synth.PAIR])
+def test_schedule_matches_oracle(shape):
+    assert M.schedule(shape) == ref.layer_kinds(shape)
+
+
+def test_kv_bytes_matches_oracle_closed_form():
+    for sh in (synth.TINY, synth.TINY_REC_FULL):
+        for mode in ("last_loop", "per_loop"):
+            for k in (1, 2, 4):
+                # lengths that are multiples of 8 and windows below them: rows = formula rows
+                assert M.kv_bytes(sh, mode, k, 2, 64) == ref.kv_bytes(sh, mode, k, 2, 64)
+    for mode in ("last_loop", "per_loop"):
+        for k in (1, 2, 4):
+            assert M.kv_bytes(synth.FULL, mode, k, 64, 33024) == \
+                ref.kv_bytes(synth.FULL, mode, k, 64, 33024)
+
+
+def test_kv_bytes_constant_in_k_for_last_loop():
+    v = [M.kv_bytes(synth.FULL, "last_loop", k, 4, 8192) for k in (1, 2, 3, 4, 8)]
+    assert len(set(v)) == 1
+    p = [M.kv_bytes(synth.FULL, "per_loop", k, 4, 8192) for k in (1, 2, 3, 4)]
+    assert np.all(np.diff(p) == p[1] - p[0]) and p[1] > p[0]
+
+
+def test_workspace_bytes_monotone():
+    a = M.workspace_bytes(synth.TINY, 2, 16)
+    b = M.workspace_bytes(synth.TINY, 2, 64)
+    assert 0 < a < b
+
+
+def _fake_tensor_map(shape):
+    """Fake device addresses: the validation paths never dereference them."""
+    kinds = ref.layer_kinds(shape)
+    names = synth.Weights(shape, kinds).names()
+
+    class Fake:
+        def __init__(self, addr):
+            self.addr = addr
+
+        def data_ptr(self):
+            return self.addr
+    return {n: Fake(0x10000 + 0x1000 * i) for i, n in enumerate(names)}
+
+
+class _FakeT:
+    def __init__(self, addr, n=0):
+        self.addr, self.n = addr, n
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+
+def _model_and_kv(shape=synth.TINY, mode="last_loop", k_max=4, batch=2, max_seq=64):
+    m = M.Model(shape, _fake_tensor_map(shape))
+    kvb = M.kv_bytes(shape, mode, k_max, batch, max_seq)
+    h = ctypes.c_void_p()
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, M.MODE_CODE[mode], k_max,
+                           batch, max_seq, h), "bind")
+    return m, h
+
+
+def _prefill(m, kv, B=2, T=8, k=1, mode=C.DORY_CACHE_LAST_LOOP, ws_bytes=None, tokens=0x500000,
+             ws=0x700000, logits=None):
+    if ws_bytes is None:
+        ws_bytes = M.workspace_bytes(m.shape, B, T)
+    return C.dory_prefill(m.handle, kv, ctypes.c_void_p(tokens) if tokens else None, B, T, k, mode,
+                          ctypes.c_void_p(ws) if ws else None, ws_bytes, logits, None, None, None,
+                          None)
+
+
+def test_validation_errors_enqueue_nothing():
+    m, kv = _model_and_kv()
+    assert _prefill(m, kv, k=0) == C.DORY_ERR_ARG
+    assert _prefill(m, kv, T=0) == C.DORY_ERR_ARG
+    assert _prefill(m, kv, B=0) == C.DORY_ERR_ARG
+    assert _prefill(m, kv, tokens=0) == C.DORY_ERR_ARG
+    assert _prefill(m, kv, ws=0) == C.DORY_ERR_ARG
+    assert _prefill(m, kv, mode=C.DORY_CACHE_PER_LOOP) == C.DORY_ERR_MODE
+    assert _prefill(m, kv, B=3) == C.DORY_ERR_CAPACITY
+    assert _prefill(m, kv, T=65) == C.DORY_ERR_CAPACITY
+    assert _prefill(m, kv, ws_bytes=16) == C.DORY_ERR_WORKSPACE
+    assert "workspace" in C.dory_last_error()
+    assert C.dory_kv_length(kv) == 0
+    C.dory_kv_destroy(kv)
+
+
+def test_per_loop_k_above_k_max_rejected():
+    m, kv = _model_and_kv(mode="per_loop", k_max=2)
+    assert _prefill(m, kv, k=3, mode=C.DORY_CACHE_PER_LOOP) == C.DORY_ERR_MODE
+    assert C.dory_kv_length(kv) == 0
+    C.dory_kv_destroy(kv)
+
+
+def test_bind_rejects_small_buffer_and_bad_mode():
+    m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
+    h = ctypes.c_void_p()
+    n = M.kv_bytes(synth.TINY, "last_loop", 1, 2, 64)
+    assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n - 1, 0, 1, 2, 64, h) == \
+        C.DORY_ERR_CAPACITY
+    assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n, 7, 1, 2, 64, h) == C.DORY_ERR_MODE
+
+
+def test_model_create_rejects_bad_configs():
+    bad = [
+        dict(n_q_heads=3),           # not a multiple of n_kv
+        dict(head_dim=48),           # no kernel
+        dict(d_model=100),           # not a multiple of 64
+        dict(window=0),
+    ]
+    for kw in bad:
+        import dataclasses
+        sh = dataclasses.replace(synth.TINY, **kw)
+        with pytest.raises(C.DoryError):
+            M.Model(sh, _fake_tensor_map(synth.TINY))
+
+
+def test_model_create_rejects_missing_weights():
+    t = _fake_tensor_map(synth.TINY)
+
+    class Null:
+        def data_ptr(self):
+            return 0
+    t["sub1.w_down"] = Null()
+    with pytest.raises(C.DoryError) as e:
+        M.Model(synth.TINY, t)
+    assert e.value.status == C.DORY_ERR_ARG
+
+
+def test_no_lm_head_rejects_logits_request():
+    m = M.Model(synth.PAIR, _fake_tensor_map(synth.PAIR))
+    kvb = M.kv_bytes(synth.PAIR, "last_loop", 1, 1, 64)
+    h = ctypes.c_void_p()
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, 0, 1, 1, 64, h), "bind")
+    st = C.dory_prefill(m.handle, h, ctypes.c_void_p(0x500000), 1, 8, 1, 0, ctypes.c_void_p(0x700000),
+                        M.workspace_bytes(synth.PAIR, 1, 8), ctypes.c_void_p(0x800000), None, None,
+                        None, None)
+    assert st == C.DORY_ERR_ARG
+
+
+def test_status_strings():
+    for s in range(8):
+        assert C.dory_status_string(s)
