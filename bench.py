@@ -1,0 +1,293 @@
+"""Benchmark of the looped normalized-GPT forward pass on one MI355X.
+
+Step = one prefill of the full 72-sublayer model (16 input + 40 recurrent x k
++ 16 output sublayers, d=2304, 16/4 heads of 128, SwiGLU 6144, window 1024,
+vocab 131072) over B=4 sequences of 8192 synthetic tokens with last-loop KV
+caching: embedding, every sublayer, the last-loop KV writes, the LM head for
+the last position and greedy selection. Weights are random row-normalized
+bf16 matrices drawn on the GPU from a seeded generator; inputs are resident
+in HBM before timing starts.
+
+Prints one JSON line: `value` is prefill tokens/s at the chosen k (default
+4); extra fields give prefill tokens/s at k = 1, 2, 4, decode tokens/s at
+B=64 with 32768 tokens of synthesized cached context for k = 1, 2, 4 under
+both cache policies, per-kernel-class timings measured with HIP events on the
+call's stream over the timed region, the roofline entry of the dominant
+kernel and the CPU oracle baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def gpu_weights(shape, kinds, seed=0, device="cuda"):
+    """Random N(0,1) rows scaled to unit length, rounded to bf16 on the GPU;
+    per-channel vectors as in the parity tests (alpha 0.05 U(.5,1.5), s_qk
+    U(.5,1.5), s_u U(.5,1.5), s_v and s_z sqrt(d) U(.5,1.5))."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def mat(r, c):
+        out = torch.empty(r, c, dtype=torch.bfloat16, device=device)
+        step = max(1, (1 << 26) // c)
+        for r0 in range(0, r, step):
+            w = torch.randn(min(step, r - r0), c, device=device, generator=g)
+            w /= w.norm(dim=1, keepdim=True)
+            out[r0:r0 + w.shape[0]] = w.to(torch.bfloat16)
+        return out.view(torch.int16)
+
+    def vec(n, mult=1.0):
+        return (mult * (0.5 + torch.rand(n, device=device, generator=g))).float()
+
+    s = shape
+    sd = s.d_model ** 0.5
+    t = {"embed": mat(s.vocab, s.d_model), "lm_head": mat(s.vocab, s.d_model), "s_z": vec(s.vocab, sd)}
+    for i, k in enumerate(kinds):
+        t[f"sub{i}.alpha"] = vec(s.d_model, 0.05)
+        if k == "mlp":
+            t[f"sub{i}.w_upgate"] = mat(2 * s.d_ff, s.d_model)
+            t[f"sub{i}.w_down"] = mat(s.d_model, s.d_ff)
+            t[f"sub{i}.s_u"] = vec(s.d_ff)
+            t[f"sub{i}.s_v"] = vec(s.d_ff, sd)
+        else:
+            t[f"sub{i}.w_qkvg"] = mat(2 * s.d_q + 2 * s.d_kv, s.d_model)
+            t[f"sub{i}.w_o"] = mat(s.d_model, s.d_q)
+            t[f"sub{i}.s_qk"] = vec(s.head_dim)
+    return t
+
+
+def attention_flops(shape, kinds, B, T, k):
+    """Algorithmic attention FLOPs of one prefill from position 0: per query
+    4 * n_q * head_dim per visible key (QK^T and PV)."""
+    p = np.arange(T, dtype=np.float64)
+    full = np.sum(p + 1)
+    swa = np.sum(np.minimum(p + 1, shape.window))
+    per = 4.0 * shape.n_q_heads * shape.head_dim * B
+    tot = 0.0
+    for i, kind in enumerate(kinds):
+        if kind == "mlp":
+            continue
+        rep = k if shape.n_input <= i < shape.n_input + shape.n_recurrent else 1
+        tot += rep * per * (full if kind == "full" else swa)
+    return tot
+
+
+def class_work(shape, M):
+    """Algorithmic work per launch of each kernel class at M token rows:
+    (amount, unit, bound)."""
+    s = shape
+    d, F, dq, dkv = s.d_model, s.d_ff, s.d_q, s.d_kv
+    return {
+        "gemm_qkvg": (2.0 * M * (2 * dq + 2 * dkv) * d, "flop", "mfma"),
+        "gemm_o": (2.0 * M * d * dq, "flop", "mfma"),
+        "gemm_upgate": (2.0 * M * 2 * F * d, "flop", "mfma"),
+        "gemm_down": (2.0 * M * d * F, "flop", "mfma"),
+        # read h (fp32) and y (fp32), write h (fp32) and its bf16 copy
+        "update": (float(M) * d * (4 + 4 + 4 + 2), "byte", "hbm"),
+    }
+
+
+def run_prefill(gm, kv, toks, k, ws):
+    kv.reset()
+    return gm.prefill(kv, toks, k, ws=ws, logits=True, next_token=True)
+
+
+def time_steps(fn, steps):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4):
+    """Decode tokens/s at a fixed position with `ctx` cached tokens whose K/V
+    are synthesized at random (the cost of a step depends on the context
+    length, not on the cached values)."""
+    out = {}
+    ws = gm.workspace(B, 1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    toks = torch.randint(0, shape.vocab, (B,), dtype=torch.int32, device="cuda", generator=g)
+    for mode in modes:
+        for k in ks:
+            kv = gm.kv_cache(mode, k, B, ctx + 1)
+            buf = kv.buffer.view(torch.bfloat16)
+            chunk = 1 << 28
+            for o in range(0, buf.numel(), chunk):
+                n = min(chunk, buf.numel() - o)
+                buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
+
+            def one():
+                kv.set_length(ctx)
+                gm.decode_step(kv, toks, k, ws=ws, logits=True, next_token=True)
+            one()
+            dt = time_steps(one, steps)
+            out[f"{mode}_k{k}"] = round(B * steps / dt, 1)
+            out[f"{mode}_k{k}_kv_gb"] = round(kv.buffer.numel() / 1e9, 2)
+            del kv, buf
+            torch.cuda.empty_cache()
+    return out
+
+
+class _RowGather:
+    """Embedding rows widened to float64 on demand."""
+
+    def __init__(self, bits):
+        self.bits = bits
+
+    def __getitem__(self, idx):
+        return synth.f64_from_bf16_bits(self.bits[idx])
+
+
+def cpu_baseline(k, n_tokens=512):
+    """The float64 oracle, unchanged, timed on this host's cores over a bounded
+    sample of the same workload: the first n_tokens tokens of sequence 0 at
+    loop count k, full model shape. Every attention sublayer is given one
+    drawn weight set and every MLP sublayer another (identical shapes and
+    arithmetic, a fraction of the host memory)."""
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sh = synth.FULL
+    kinds = ref.layer_kinds(sh)
+    W = synth.Weights(sh, kinds, 0)
+    cache = {"embed": _RowGather(W.raw("embed"))}
+
+    def weight(name):
+        if name.startswith("sub"):
+            i, rest = name[3:].split(".", 1)
+            name = ("sub1." if kinds[int(i)] == "mlp" else "sub0.") + rest
+        if name not in cache:
+            cache[name] = W.f64(name)
+        return cache[name]
+    for n in ("lm_head", "s_z", "sub0.w_qkvg", "sub0.w_o", "sub0.s_qk", "sub0.alpha",
+              "sub1.w_upgate", "sub1.w_down", "sub1.s_u", "sub1.s_v", "sub1.alpha"):
+        weight(n)
+    om = ref.OracleModel(sh, weight)
+    toks = synth.tokens(0, 1, n_tokens, sh.vocab)
+    t0 = time.perf_counter()
+    om.step(ref.Cache(sh, ref.MODE_LAST, 1), toks, k)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle, full 72-sublayer shape, k={k}, sequence 0 tokens "
+                      f"0..{n_tokens - 1} (of 4 x 8192), one prefill step, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--no-extra", action="store_true", help="skip k-sweep and decode table")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences are independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    from looped_ngpt_transformer_fwd_amd import model as M
+
+    shape = synth.FULL
+    B, T, k = 4, 8192, args.k
+    kinds = M.schedule(shape)
+    weights = gpu_weights(shape, kinds)
+    gm = M.Model(shape, weights)
+    ws = gm.workspace(B, T)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    toks = torch.randint(0, shape.vocab, (B, T), dtype=torch.int32, device="cuda", generator=g)
+    kv = gm.kv_cache("last_loop", k, B, T)
+
+    for _ in range(args.warmup):
+        run_prefill(gm, kv, toks, k, ws)
+    torch.cuda.synchronize()
+    gm.profile_begin(max_launches=2000 * max(1, args.steps))
+    dt = time_steps(lambda: run_prefill(gm, kv, toks, k, ws), args.steps)
+    prof = gm.profile_end()
+    value = B * T * args.steps / dt
+    ms_per_step = dt / args.steps * 1e3
+
+    M_rows = B * T
+    work = class_work(shape, M_rows)
+    attn_flop = attention_flops(shape, kinds, B, T, k)
+    kernels = {}
+    for cls, (n, ms) in prof.items():
+        if n == 0:
+            continue
+        e = {"launches": n, "ms_total": round(ms, 3), "ms_avg": round(ms / n, 4),
+             "share": round(ms / max(1e-9, sum(v[1] for v in prof.values())), 4)}
+        if cls in work:
+            amt, unit, bound = work[cls]
+            rate = amt / (ms / n * 1e-3)
+            e["rate"] = round(rate / (1e12 if unit == "flop" else 1e9), 2)
+            e["rate_unit"] = "TFLOP/s" if unit == "flop" else "GB/s"
+        if cls == "attn":
+            e["rate"] = round(attn_flop * args.steps / (ms * 1e-3) / 1e12, 2)
+            e["rate_unit"] = "TFLOP/s"
+        kernels[cls] = e
+    dom = max((c for c in kernels if c in work), key=lambda c: kernels[c]["ms_total"])
+    amt, unit, bound = work[dom]
+    achieved = kernels[dom]["rate"]
+    peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS
+    roofline = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "work_per_launch": amt, "work_unit": unit}
+
+    result = {
+        "metric": "prefill & decode tokens/sec at k=1/2/4 on 1 GPU; % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefill, full 72-sublayer looped nGPT (16+40k+16), k={k}, "
+                               f"last_loop KV, B={B} x T={T}",
+                   "global_batch": B, "seq_len": T, "loops": k, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_extra:
+        pre = {f"k{k}": round(value, 1)}
+        for kk in (1, 2, 4):
+            if kk == k:
+                continue
+            kv2 = gm.kv_cache("last_loop", kk, B, T)
+            run_prefill(gm, kv2, toks, kk, ws)
+            d2 = time_steps(lambda: run_prefill(gm, kv2, toks, kk, ws), 2)
+            pre[f"k{kk}"] = round(B * T * 2 / d2, 1)
+            del kv2
+        result["prefill_tok_s"] = dict(sorted(pre.items()))
+        del kv, ws
+        torch.cuda.empty_cache()
+        result["decode_tok_s"] = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
+        result["decode_config"] = "B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each"
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(k)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

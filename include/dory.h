@@ -192,6 +192,39 @@ dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, 
                              float* logits, int32_t* next, float* hidden, float* states,
                              void* stream);
 
+/* Declares that the first `length` positions of every sequence in the bound
+ * buffer already hold valid K/V (for example a cache restored by the caller),
+ * so that the next step starts at that position. 0 <= length <= max_seq;
+ * under per-loop caching the loop count of later steps is not constrained
+ * by earlier ones after this call. */
+dory_status dory_kv_set_length(dory_kv* kv, int64_t length);
+
+/* Kernel classes timed by the measurement hooks below. */
+typedef enum dory_kernel_class {
+  DORY_K_GEMM_QKVG = 0,   /* q/k/v/gate projection */
+  DORY_K_GEMM_O = 1,      /* attention output projection */
+  DORY_K_GEMM_UPGATE = 2, /* SwiGLU up/gate projection (with the activation) */
+  DORY_K_GEMM_DOWN = 3,   /* MLP down projection */
+  DORY_K_GEMM_LM = 4,     /* LM head */
+  DORY_K_ATTN = 5,        /* attention (prefill or decode, incl. split combine) */
+  DORY_K_QK = 6,          /* RoPE / q-k norm / K-V placement */
+  DORY_K_UPDATE = 7,      /* nGPT normalize-and-update (and loop boundary) */
+  DORY_K_KV_WRITE = 8,    /* persistent cache store */
+  DORY_K_OTHER = 9,       /* embedding, SwiGLU over partials, argmax, copies */
+  DORY_K_NUM_CLASSES = 10
+} dory_kernel_class;
+
+/* Measurement hooks. Between dory_profile_begin and dory_profile_end, each
+ * kernel launch of the model is bracketed by a pair of HIP events recorded
+ * on the call's stream (at most max_launches launches are recorded; later
+ * ones are not timed). dory_profile_end synchronizes those events and writes,
+ * per dory_kernel_class, the number of timed launches and their summed
+ * duration in milliseconds into counts[DORY_K_NUM_CLASSES] and
+ * ms[DORY_K_NUM_CLASSES]. The events are host-side HIP objects; no device
+ * memory is allocated. */
+dory_status dory_profile_begin(dory_model* m, int32_t max_launches);
+dory_status dory_profile_end(dory_model* m, int64_t* counts, double* ms);
+
 /* Mask dump for bit-exact tests: out (device uint8 [T, L + T]) receives 1
  * where the attention kernels treat key position u as visible to the query
  * at position L + t (u <= L + t, and L + t - u < window unless window is 0). */

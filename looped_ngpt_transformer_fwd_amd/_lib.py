@@ -81,6 +81,9 @@ SIGNATURES = {
     "dory_prefill": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_decode_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_debug_mask": (_I32, [_I32, _I64, _I32, _P, _P]),
+    "dory_kv_set_length": (_I32, [_P, _I64]),
+    "dory_profile_begin": (_I32, [_P, _I32]),
+    "dory_profile_end": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "dory_status_string": (ctypes.c_char_p, [_I32]),
     "dory_last_error": (ctypes.c_char_p, []),
 }
@@ -173,6 +176,23 @@ def dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidde
 
 def dory_debug_mask(window, L, T, out, stream):
     return lib().dory_debug_mask(window, L, T, out, stream)
+
+
+def dory_kv_set_length(kv, length):
+    return lib().dory_kv_set_length(kv, length)
+
+
+DORY_K_NUM_CLASSES = 10
+KERNEL_CLASSES = ["gemm_qkvg", "gemm_o", "gemm_upgate", "gemm_down", "gemm_lm", "attn", "qk",
+                  "update", "kv_write", "other"]
+
+
+def dory_profile_begin(m, max_launches):
+    return lib().dory_profile_begin(m, max_launches)
+
+
+def dory_profile_end(m, counts, ms):
+    return lib().dory_profile_end(m, counts, ms)
 
 
 def dory_status_string(s):

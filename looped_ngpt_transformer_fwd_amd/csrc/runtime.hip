@@ -139,15 +139,48 @@ WsLayout plan_ws(const Shape& s, int B, int T) {
   return L;
 }
 
+// Event pairs around kernel launches, for the measurement hooks.
+struct Profiler {
+  bool on = false;
+  int max = 0;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  std::vector<int> cls;        // class of each recorded launch
+  void clear() {
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+    ev.clear();
+    cls.clear();
+    on = false;
+    max = 0;
+  }
+};
+
+struct ProfScope {
+  Profiler* p;
+  hipStream_t st;
+  int idx = -1;
+  ProfScope(Profiler* p_, hipStream_t st_, int c) : p(p_), st(st_) {
+    if (p->on && (int)p->cls.size() < p->max) {
+      idx = (int)p->cls.size();
+      p->cls.push_back(c);
+      hipEventRecord(p->ev[2 * idx], st);
+    }
+  }
+  ~ProfScope() {
+    if (idx >= 0) hipEventRecord(p->ev[2 * idx + 1], st);
+  }
+};
+
 }  // namespace
 
 struct dory_model {
   Shape s;
+  Profiler prof;
   std::vector<int> kinds;
   std::vector<dory_sublayer_weights> sub;
   const uint16_t* embed;
   const uint16_t* lm_head;
   const float* s_z;
+  ~dory_model() { prof.clear(); }
 };
 
 struct dory_kv {
@@ -203,7 +236,10 @@ struct Ctx {
   float* P() const { return reinterpret_cast<float*>(ws + L.P); }
   float* part() const { return reinterpret_cast<float*>(ws + L.part); }
   float* logits_scratch() const { return reinterpret_cast<float*>(ws + L.logits); }
+  Profiler* prof() const { return &m->prof; }
 };
+
+#define PROF(c, cls) ProfScope prof_scope_##__LINE__((c).prof(), (c).st, (cls))
 
 #define HIPCHK(expr)                                                              \
   do {                                                                            \
@@ -216,7 +252,8 @@ struct Ctx {
 
 // y = A W^T into P (split partials), returns the split used.
 dory_status gemm_f32(Ctx& c, const uint16_t* A, int64_t lda, const void* W, int N, int K,
-                     int64_t M, int* nsplit_out) {
+                     int64_t M, int* nsplit_out, int cls) {
+  PROF(c, cls);
   GemmArgs g;
   g.A = A; g.lda = lda;
   g.B = reinterpret_cast<const uint16_t*>(W); g.ldb = K;
@@ -242,7 +279,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
   const double base = full ? s.base_full : s.base_swa;
   const SlotPtr sp = slot_ptr(c.kv, i, slot);
   int ns = 1;
-  dory_status st = gemm_f32(c, c.h16(), s.d, w.w_qkvg, s.nqkvg(), s.d, c.M, &ns);
+  dory_status st = gemm_f32(c, c.h16(), s.d, w.w_qkvg, s.nqkvg(), s.d, c.M, &ns, DORY_K_GEMM_QKVG);
   if (st != DORY_OK) return st;
   const int64_t split_stride = c.M * s.nqkvg();
 
@@ -258,11 +295,15 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     // last-loop rule read literally: overwrite at every loop), then the
     // attention reads the cache only
     QkDest kd{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring};
-    HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh, base,
+    {
+      PROF(c, DORY_K_QK);
+      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh, base,
                           w.s_qk, c.qh(), kd, c.gate(), c.st));
+    }
     const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
     int nsd = decode_attn_pick_split(c.B, s.nkv, c.p0 - lo + 1);
     if (nsd > kMaxDecodeSplits) return fail(DORY_ERR_UNSUPPORTED, "context too long for decode splits");
+    PROF(c, DORY_K_ATTN);
     HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
   } else {
     // prefill: fresh K/V of the step live in the workspace, rows counted from
@@ -270,13 +311,23 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     // cached positions [f_origin, p0) are copied in front of them
     const int64_t f_origin = c.p0 / 8 * 8;
     QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
-    HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh, base,
-                          w.s_qk, c.qh(), kd, c.gate(), c.st));
-    HIPCHK(launch_prefix_copy(sp.k, sp.v, sp.rows, sp.ring, c.B, s.nkv, s.dh, f_origin, c.p0,
-                              c.kf(), c.vf(), c.L.f_rows, c.st));
+    {
+      PROF(c, DORY_K_QK);
+      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh, base,
+                            w.s_qk, c.qh(), kd, c.gate(), c.st));
+    }
+    if (c.p0 > f_origin) {
+      PROF(c, DORY_K_KV_WRITE);
+      HIPCHK(launch_prefix_copy(sp.k, sp.v, sp.rows, sp.ring, c.B, s.nkv, s.dh, f_origin, c.p0,
+                                c.kf(), c.vf(), c.L.f_rows, c.st));
+    }
     aa.kf = c.kf(); aa.vf = c.vf(); aa.f_rows = c.L.f_rows; aa.f_origin = f_origin;
-    HIPCHK(launch_attn_prefill(aa, c.st));
+    {
+      PROF(c, DORY_K_ATTN);
+      HIPCHK(launch_attn_prefill(aa, c.st));
+    }
     if (write) {
+      PROF(c, DORY_K_KV_WRITE);
       // persistent store after the step's attention; a ring keeps only the
       // newest `ring` positions
       int64_t pa = c.p0;
@@ -285,8 +336,9 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                              c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st));
     }
   }
-  st = gemm_f32(c, c.z(), s.dq(), w.w_o, s.d, s.dq(), c.M, &ns);
+  st = gemm_f32(c, c.z(), s.dq(), w.w_o, s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O);
   if (st != DORY_OK) return st;
+  PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
                        uo.aux, nullptr, c.st));
   return DORY_OK;
@@ -297,6 +349,7 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
   const dory_sublayer_weights& w = c.m->sub[i];
   const int ns_up = gemm_pick_split((int)c.M, 2 * s.F, s.d, c.M < kLargeM ? kMaxGemmSplit : 1);
   if (ns_up == 1) {
+    PROF(c, DORY_K_GEMM_UPGATE);
     GemmArgs g;
     g.A = c.h16(); g.lda = s.d;
     g.B = reinterpret_cast<const uint16_t*>(w.w_upgate); g.ldb = s.d;
@@ -305,14 +358,16 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
     HIPCHK(launch_gemm(g, EPI_SWIGLU, c.st));
   } else {
     int ns = 1;
-    dory_status st = gemm_f32(c, c.h16(), s.d, w.w_upgate, 2 * s.F, s.d, c.M, &ns);
+    dory_status st = gemm_f32(c, c.h16(), s.d, w.w_upgate, 2 * s.F, s.d, c.M, &ns, DORY_K_GEMM_UPGATE);
     if (st != DORY_OK) return st;
+    PROF(c, DORY_K_OTHER);
     HIPCHK(launch_swiglu_partials(c.P(), ns, c.M * 2 * s.F, (int)c.M, s.F, w.s_u, w.s_v, c.a(),
                                   c.st));
   }
   int ns = 1;
-  dory_status st = gemm_f32(c, c.a(), s.F, w.w_down, s.d, s.F, c.M, &ns);
+  dory_status st = gemm_f32(c, c.a(), s.F, w.w_down, s.d, s.F, c.M, &ns, DORY_K_GEMM_DOWN);
   if (st != DORY_OK) return st;
+  PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
                        uo.aux, nullptr, c.st));
   return DORY_OK;
@@ -328,8 +383,11 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   const Shape& s = c.s;
   const int64_t Md = c.M * s.d;
   const bool per_loop = c.kv->mode == DORY_CACHE_PER_LOOP;
-  HIPCHK(launch_embed(tokens, c.m->embed, s.V, (int)c.M, s.d, c.h32(), c.h16(),
-                      s.nin == 0 ? c.x32() : nullptr, c.st));
+  {
+    PROF(c, DORY_K_OTHER);
+    HIPCHK(launch_embed(tokens, c.m->embed, s.V, (int)c.M, s.d, c.h32(), c.h16(),
+                        s.nin == 0 ? c.x32() : nullptr, c.st));
+  }
   for (int i = 0; i < s.nin; ++i) {
     UpdateOpts uo;
     if (i == s.nin - 1) uo.aux = c.x32();  // x: output of the input block
@@ -338,7 +396,10 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   }
   // loop 1 starts from N(x + x) = N(x): x is already unit-norm when it comes
   // out of an update; a bare embedding is normalized here
-  if (s.nin == 0) HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
+  if (s.nin == 0) {
+    PROF(c, DORY_K_UPDATE);
+    HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
+  }
   for (int it = 0; it < k; ++it) {
     const int slot = per_loop ? it : 0;
     const bool write = per_loop || it == k - 1;
@@ -370,8 +431,14 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
     g.B = c.m->lm_head; g.ldb = s.d;
     g.M = c.B; g.N = s.V; g.K = s.d; g.nsplit = 1;
     g.C = out; g.ldc = s.V; g.s1 = c.m->s_z;
-    HIPCHK(launch_gemm(g, EPI_LOGITS, c.st));
-    if (next) HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
+    {
+      PROF(c, DORY_K_GEMM_LM);
+      HIPCHK(launch_gemm(g, EPI_LOGITS, c.st));
+    }
+    if (next) {
+      PROF(c, DORY_K_OTHER);
+      HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
+    }
   }
   return DORY_OK;
 }
@@ -561,6 +628,47 @@ dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, 
                              void* stream) {
   return step_common(m, kv, tokens, B, 1, k, mode, ws, ws_bytes, logits, next, hidden, states,
                      stream);
+}
+
+dory_status dory_kv_set_length(dory_kv* kv, int64_t length) {
+  if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");
+  if (length < 0 || length > kv->max_seq) return fail(DORY_ERR_CAPACITY, "length outside [0, max_seq]");
+  kv->len = length;
+  kv->k_used = 0;
+  return DORY_OK;
+}
+
+dory_status dory_profile_begin(dory_model* m, int32_t max_launches) {
+  if (!m || max_launches < 1) return fail(DORY_ERR_ARG, "bad profile arguments");
+  m->prof.clear();
+  m->prof.ev.resize(2 * (size_t)max_launches);
+  for (auto& e : m->prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      m->prof.ev.resize(&e - m->prof.ev.data());
+      m->prof.clear();
+      return fail(DORY_ERR_HIP, hipGetErrorString(r));
+    }
+  }
+  m->prof.max = max_launches;
+  m->prof.on = true;
+  return DORY_OK;
+}
+
+dory_status dory_profile_end(dory_model* m, int64_t* counts, double* ms) {
+  if (!m || !counts || !ms) return fail(DORY_ERR_ARG, "bad profile arguments");
+  for (int i = 0; i < DORY_K_NUM_CLASSES; ++i) { counts[i] = 0; ms[i] = 0.0; }
+  Profiler& p = m->prof;
+  dory_status st = DORY_OK;
+  for (size_t i = 0; i < p.cls.size(); ++i) {
+    if (hipEventSynchronize(p.ev[2 * i + 1]) != hipSuccess) { st = fail(DORY_ERR_HIP, "event sync"); break; }
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) { st = fail(DORY_ERR_HIP, "event time"); break; }
+    counts[p.cls[i]] += 1;
+    ms[p.cls[i]] += t;
+  }
+  p.clear();
+  return st;
 }
 
 dory_status dory_debug_mask(int32_t window, int64_t L, int32_t T, uint8_t* out, void* stream) {

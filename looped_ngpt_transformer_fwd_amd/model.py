@@ -107,6 +107,17 @@ class Model:
             pass
         self.handle = None
 
+    def profile_begin(self, max_launches=100000):
+        C.check(C.dory_profile_begin(self.handle, max_launches), "dory_profile_begin")
+
+    def profile_end(self):
+        """{class: (launches, total ms)} of the launches timed since profile_begin."""
+        counts = (ctypes.c_int64 * C.DORY_K_NUM_CLASSES)()
+        ms = (ctypes.c_double * C.DORY_K_NUM_CLASSES)()
+        C.check(C.dory_profile_end(self.handle, counts, ms), "dory_profile_end")
+        return {C.KERNEL_CLASSES[i]: (int(counts[i]), float(ms[i]))
+                for i in range(C.DORY_K_NUM_CLASSES)}
+
     def workspace(self, batch, tokens, device="cuda"):
         n = workspace_bytes(self.shape, batch, tokens)
         return torch.empty(n, dtype=torch.uint8, device=device)
@@ -177,6 +188,9 @@ class KVCache:
 
     def reset(self):
         C.check(C.dory_kv_reset(self.handle), "dory_kv_reset")
+
+    def set_length(self, length):
+        C.check(C.dory_kv_set_length(self.handle, length), "dory_kv_set_length")
 
     def slot(self, sublayer, loop=0):
         info = C.dory_kv_slot_info()

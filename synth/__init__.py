@@ -89,9 +89,13 @@ def _rng(seed: int, name: str) -> np.random.Generator:
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even);
-    returns the 16-bit patterns. Inputs must be finite."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    returns the 16-bit patterns. Inputs must be finite (no overflow of the
+    32-bit sum is then possible)."""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = (u >> 16) & 1
+    u += 0x7FFF
+    u += lsb
+    u >>= 16
     return u.astype(np.uint16)
 
 
@@ -104,11 +108,11 @@ def unit_rows(seed: int, name: str, rows: int, cols: int) -> np.ndarray:
     """bf16 bit patterns of an N(0,1) [rows, cols] matrix with unit-L2 rows."""
     g = _rng(seed, name)
     out = np.empty((rows, cols), dtype=np.uint16)
-    step = max(1, (1 << 24) // max(cols, 1))
+    step = max(1, (1 << 22) // max(cols, 1))
     for r0 in range(0, rows, step):
         r1 = min(rows, r0 + step)
         w = g.standard_normal((r1 - r0, cols), dtype=np.float32)
-        w /= np.sqrt(np.sum(w.astype(np.float64) ** 2, axis=1, keepdims=True)).astype(np.float32)
+        w /= np.sqrt(np.einsum("ij,ij->i", w, w, dtype=np.float64)).astype(np.float32)[:, None]
         out[r0:r1] = bf16_bits_from_f32(w)
     return out
 
