@@ -183,6 +183,200 @@ gemm_nt_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M kernel: 256 x 256 x 64 tiles, 8 waves (4 x 2, each 64 x 128), two
+// LDS stages filled by direct global->LDS DMA (global_load_lds_dwordx4), so
+// no VGPRs stage the operands. Each 1 KiB DMA block holds 8 rows x 128 B;
+// lane l of a block writes LDS bytes [16 l, 16 l + 16) and fetches logical
+// 16-byte chunk (l % 8) ^ (row % 8) of its row, i.e. the tile is stored
+// XOR-swizzled and fragment reads of 8 consecutive rows hit 8 distinct bank
+// groups. One barrier per K step: after it, the loads of step k+1 are issued
+// into the other stage and stay in flight during the MFMAs of step k. The
+// loop has a single body (stage chosen at run time): a body unrolled per
+// stage with an exit between the copies doubles the live accumulators.
+// Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives
+// each XCD a contiguous range of tiles, traversed in groups of 8 row panels,
+// so concurrently running tiles of one XCD share A and B panels in its L2.
+constexpr int BIG_BM = 256, BIG_BN = 256, BIG_WM = 64, BIG_WN = 128;
+constexpr int BIG_NT = 512;
+constexpr int BIG_TILE_BYTES = 256 * 128;  // one operand tile of one stage
+
+__device__ __forceinline__ void big_tile_coords(int bid, int ntm, int ntn, int* tm, int* tn) {
+  const int ntiles = ntm * ntn;
+  int t = bid;
+  if ((ntiles & 7) == 0) t = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+  constexpr int G = 8;
+  const int per_group = G * ntn;
+  const int grp = t / per_group;
+  const int first = grp * G;
+  const int gsz = min(ntm - first, G);
+  const int r = t - grp * per_group;
+  *tm = first + r % gsz;
+  *tn = r / gsz;
+}
+
+// Buffer resource over [base, base + bytes): raw (stride 0) buffer loads
+// with 32-bit per-lane byte offsets; bytes past the end read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voff + soff into LDS at lds_block + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      uint8_t* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16,
+                                           voff, soff, 0, 0);
+}
+
+// vmcnt(0), expcnt/lgkmcnt untouched
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void big_compute(const uint8_t* sa, const uint8_t* sb,
+                                            const int (&loff)[4], floatx16 (&acc)[2][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 af[2], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(sa + i * 32 * 128 + loff[kk]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(sb + j * 32 * 128 + loff[kk]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(BIG_NT, 1)
+gemm_big_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BIG_TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BIG_TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BIG_TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BIG_TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntm = (g.M + BIG_BM - 1) / BIG_BM, ntn = (g.N + BIG_BN - 1) / BIG_BN;
+  int tm, tn;
+  big_tile_coords(blockIdx.x, ntm, ntn, &tm, &tn);
+  const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
+  const int ksteps = g.K / BK;
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
+  const int brows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)(brows - 1) * g.ldb * 2 + g.K * 2));
+
+  // DMA sources: wave w fills blocks w, w+8, w+16, w+24 of each operand tile
+  const int lr = lane >> 3;                 // row within the block
+  const int lc = (lane & 7) ^ lr;           // logical chunk fetched by this lane
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave + 8 * i) * 8 + lr;
+    aoff[i] = (uint32_t)((int64_t)min(m0 + r, g.M - 1) * g.lda * 2 + lc * 16);
+    int v = min(n0 + r, g.N - 1);
+    int row = v;
+    if (EPI == EPI_SWIGLU) {
+      const int f = ((v >> 6) << 5) | (v & 31);
+      row = (v & 32) ? g.F + f : f;
+    }
+    boff[i] = (uint32_t)((int64_t)row * g.ldb * 2 + lc * 16);
+  }
+  // LDS lane offsets of the fragment reads for the 4 k-steps of 16; rows of
+  // every fragment are multiples of 32 apart, so row & 7 = lane & 7
+  const int fr = lane & 31, fh = lane >> 5;
+  int loff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ (fr & 7)) << 4);
+  const int a_wave = wm * BIG_WM * 128, b_wave = wn * BIG_WN * 128;
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+#define DORY_ISSUE(KS, SA, SB)                                              \
+  do {                                                                      \
+    const uint32_t ko_ = (uint32_t)(KS) * (BK * 2);                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                      \
+      dma16(ra, aoff[i_], ko_, (SA) + (wave + 8 * i_) * 1024);              \
+      dma16(rb, boff[i_], ko_, (SB) + (wave + 8 * i_) * 1024);              \
+    }                                                                       \
+  } while (0)
+
+  DORY_ISSUE(0, sA0, sB0);
+  for (int ks = 0; ks < ksteps; ++ks) {
+    wait_vm0();
+    __syncthreads();
+    const bool odd = ks & 1;
+    if (ks + 1 < ksteps) {
+      if (odd) DORY_ISSUE(ks + 1, sA0, sB0);
+      else DORY_ISSUE(ks + 1, sA1, sB1);
+    }
+    big_compute((odd ? sA1 : sA0) + a_wave, (odd ? sB1 : sB0) + b_wave, loff, acc);
+  }
+#undef DORY_ISSUE
+
+  const int rbase = m0 + wm * BIG_WM + (lane >> 5) * 4;
+  const int cbase = n0 + wn * BIG_WN + (lane & 31);
+  if (EPI == EPI_F32 || EPI == EPI_LOGITS) {
+    float* C = g.C;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = cbase + j * 32;
+      if (col >= g.N) continue;
+      const float sc = (EPI == EPI_LOGITS) ? g.s1[col] : 1.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
+          if (row < g.M) C[(int64_t)row * g.ldc + col] = acc[i][j][e] * sc;
+        }
+    }
+  } else {
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int v = cbase + jp * 64;
+      if (v >= g.N) continue;
+      const int f = ((v >> 6) << 5) | (v & 31);
+      const float su = g.s1[f], sv = g.s2[f];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
+          if (row < g.M) {
+            const float up = acc[i][2 * jp][e] * su;
+            const float gt = acc[i][2 * jp + 1][e] * sv;
+            const float act = gt / (1.f + __expf(-gt));
+            g.C16[(int64_t)row * g.ldc16 + f] = f2bf(act * up);
+          }
+        }
+    }
+  }
+}
+
+hipError_t launch_big(const GemmArgs& a, int epi, hipStream_t st) {
+  const int tiles = ((a.M + BIG_BM - 1) / BIG_BM) * ((a.N + BIG_BN - 1) / BIG_BN);
+  dim3 grid(tiles), block(BIG_NT);
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL((gemm_big_kernel<EPI_F32>), grid, block, 0, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big_kernel<EPI_SWIGLU>), grid, block, 0, st, a); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_big_kernel<EPI_LOGITS>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmArgs& a, int epi, hipStream_t st) {
   constexpr int NT = 64 * (BM / WM) * (BN / WN);
@@ -213,7 +407,7 @@ int gemm_pick_split(int M, int N, int K, int max_split) {
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.K % BK != 0 || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi != EPI_F32 && a.nsplit != 1) return hipErrorInvalidValue;
-  if (a.M >= kLargeM) return launch_cfg<256, 256, 64, 128>(a, epi, st);
+  if (a.M >= kLargeM) return launch_big(a, epi, st);
   return launch_cfg<64, 128, 32, 64>(a, epi, st);
 }
 

@@ -72,6 +72,12 @@ TINY_REC_FULL = dataclasses.replace(
     TINY, layer_kinds=(KIND_SWA, KIND_MLP,
                        KIND_SWA, KIND_MLP, KIND_FULL, KIND_MLP,
                        KIND_FULL, KIND_MLP))
+# Mid-size model whose projections take the large-M GEMM path with ragged
+# tiles: d=192 (3 K steps of 64), q/k/v/gate width 384, SwiGLU 320.
+MID = Shape(d_model=192, n_q_heads=4, n_kv_heads=2, head_dim=32, d_ff=320,
+            vocab=300, n_input=2, n_recurrent=4, n_output=2, window=64,
+            layer_kinds=(KIND_SWA, KIND_MLP, KIND_SWA, KIND_MLP, KIND_FULL, KIND_MLP,
+                         KIND_FULL, KIND_MLP))
 # Full-size shape: d=2304, 16 query / 4 KV heads of 128, SwiGLU 6144,
 # vocab 131072, 16 input + 40 recurrent + 16 output sublayers, window 1024.
 FULL = Shape(d_model=2304, n_q_heads=16, n_kv_heads=4, head_dim=128, d_ff=6144,

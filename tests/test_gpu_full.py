@@ -1,0 +1,74 @@
+"""GPU parity where the projections run the large-M GEMM path.
+
+* mid-size model, 1100 tokens: ragged M and N tiles, an odd number of K
+  steps, two chunks (the second with a cached prefix) under both policies;
+* the full-width recurrent pair [SWA, MLP, full, MLP] at d=2304, 16/4 heads
+  of 128, SwiGLU 6144, window 1024, B=1 x T=4096, k = 1..4, compared with the
+  float64 oracle on every loop state and the final hidden states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref
+from tests.gpu_util import log, oracle_model, per_token_check, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    from looped_ngpt_transformer_fwd_amd import model
+    return model
+
+
+@pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
+def test_mid_model_large_gemm_path(M, mode):
+    shape = synth.MID
+    k = 2
+    log(f"mid {mode}")
+    W = synth.Weights(shape, ref.layer_kinds(shape), 3)
+    gm = M.Model(shape, upload(W))
+    om = oracle_model(shape, W)
+    B = 1
+    toks = synth.tokens(9, B, 1300, shape.vocab)
+    kv = gm.kv_cache(mode, k, B, 1400)
+    oc = ref.Cache(shape, mode, B)
+    for a, b in [(0, 1100), (1100, 1300)]:
+        out = gm.prefill(kv, torch.from_numpy(toks[:, a:b].copy()).cuda(), k, hidden=True,
+                         states=True)
+        torch.cuda.synchronize()
+        o = om.step(oc, toks[:, a:b], k)
+        per_token_check(out["hidden"].cpu().numpy(), o["hidden"], f"hidden[{a}:{b}]")
+        st = out["states"].cpu().numpy()
+        for i in range(k):
+            per_token_check(st[i], o["states"][i], f"s_{i + 1}[{a}:{b}]")
+        per_token_check(out["logits"].cpu().numpy(), o["logits"], f"logits[{a}:{b}]")
+
+
+@pytest.fixture(scope="module")
+def pair(M):
+    shape = synth.PAIR
+    W = synth.Weights(shape, ref.layer_kinds(shape), 0)
+    log("pair: drawing weights")
+    gm = M.Model(shape, upload(W))
+    om = oracle_model(shape, W)
+    return shape, W, gm, om
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_recurrent_pair_full_width(pair, k):
+    shape, W, gm, om = pair
+    log(f"pair k={k}")
+    B, T = 1, 4096
+    toks = synth.tokens(2, B, T, shape.vocab)
+    kv = gm.kv_cache("last_loop", k, B, T)
+    out = gm.prefill(kv, torch.from_numpy(toks).cuda(), k, logits=False, hidden=True, states=True)
+    torch.cuda.synchronize()
+    o = om.step(ref.Cache(shape, "last_loop", B), toks, k, logits=None)
+    st = out["states"].cpu().numpy()
+    for i in range(k):
+        c, m = per_token_check(st[i], o["states"][i], f"s_{i + 1}")
+        log(f"  s_{i + 1}: min cos {c:.6f} max abs {m:.2e}")
+    per_token_check(out["hidden"].cpu().numpy(), o["hidden"], "hidden")
