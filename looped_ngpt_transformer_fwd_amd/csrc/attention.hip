@@ -29,33 +29,64 @@ namespace {
 constexpr int PF_WAVES = 8;
 constexpr int PF_BN = 64;
 
+__device__ __forceinline__ void dma16_flat(const void* src, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm0_attn() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// K/V tiles are staged by direct global->LDS DMA into two stages (the next
+// tile's loads are in flight during the current tile's MFMAs). Both tiles are
+// stored XOR-swizzled by row so that the MFMA fragment reads of consecutive
+// rows hit distinct bank groups:
+//   K tile   [BN keys][DH]   row = DH*2 bytes, chunk c of row r stored at c ^ key(r)
+//   V^T tile [DH][BN keys]   row = BN*2 = 128 bytes, chunk c of row d at c ^ (d & 7)
+template <int DH>
+__device__ __forceinline__ int kswz(int r) {
+  constexpr int KCH = DH / 8;
+  return r & ((KCH < 8 ? KCH : 8) - 1);
+}
+
 template <int DH, int GRP>
 __global__ void __launch_bounds__(PF_WAVES * 64)
 attn_prefill_kernel(AttnArgs a) {
   constexpr int QB = PF_WAVES / GRP;   // 32-query blocks per workgroup
   constexpr int BQ = QB * 32;          // queries per workgroup
   constexpr int BN = PF_BN;
-  constexpr int KROW = DH * 2 + 16;    // padded LDS bytes per key row
-  constexpr int VROW = BN * 2 + 8;     // padded LDS bytes per V^T row
+  constexpr int KT_BYTES = BN * DH * 2;
+  constexpr int VT_BYTES = DH * BN * 2;
+  constexpr int KCH = DH / 8;
+  constexpr int K_BLOCKS = KT_BYTES / 1024, V_BLOCKS = VT_BYTES / 1024;
+  constexpr int KRPB = 1024 / (DH * 2);  // key rows per DMA block
   constexpr int NT = PF_WAVES * 64;
-  constexpr int K_CHUNKS = BN * DH / 8;
-  constexpr int V_CHUNKS = DH * BN / 8;
-  static_assert(K_CHUNKS % NT == 0 || K_CHUNKS < NT, "");
 
-  __shared__ __attribute__((aligned(16))) uint8_t ks[BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[DH * VROW];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[VT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[VT_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // heaviest query tiles (most keys under the causal mask) start first
+  const int qt = gridDim.x - 1 - blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
   const int qb = wave / GRP, head = g * GRP + (wave % GRP);
   const int C = a.C;
   const int t0 = qt * BQ + qb * 32;
-  const int tq = t0 + (lane & 31);           // this lane's query row
-  const int64_t pq = a.p0 + tq;              // its position
-  const int hl = lane >> 5;                  // lane half
+  const int tq = t0 + (lane & 31);
+  const int hl = lane >> 5;
   const int64_t bg = (int64_t)b * a.n_kv + g;
+  const int64_t pq = a.p0 + tq;
 
-  // query fragments (B operand of S^T): column = query, k = head dims
+  // V^T stages start zeroed: lanes whose keys lie past the last key skip
+  // their DMA, and the probabilities (exactly 0) of those keys must meet
+  // finite values
+  for (int i = tid; i < VT_BYTES / 16; i += NT) {
+    reinterpret_cast<uint4*>(vs0)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(vs1)[i] = make_uint4(0, 0, 0, 0);
+  }
+
   bf16x8 qf[DH / 16];
   {
     const int tc = min(tq, C - 1);
@@ -73,19 +104,42 @@ attn_prefill_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
 
-  // key range of the workgroup
   const int tw0 = qt * BQ;
   const int tw1 = min(C, tw0 + BQ) - 1;
   const int64_t p_lo = a.p0 + tw0, p_hi = a.p0 + tw1;
-  const int64_t k_end = a.p0 + C;            // keys [0, k_end) exist
+  const int64_t k_end = a.p0 + C;
   int64_t k_lo = 0;
   if (a.window > 0) k_lo = max((int64_t)0, p_lo - a.window + 1);
   const int64_t kt_first = (k_lo / BN) * BN;
+  const int ntiles = (int)((p_hi - kt_first) / BN) + 1;
 
-  for (int64_t kt = kt_first; kt <= p_hi; kt += BN) {
-    // ---- stage K tile [BN][DH]
-    for (int c = tid; c < K_CHUNKS; c += NT) {
-      const int r = c / (DH / 8), cc = c % (DH / 8);
+  // per-wave query extent
+  const bool wave_live = t0 < C;
+  const int64_t wq_lo = a.p0 + t0, wq_hi = a.p0 + min(t0 + 31, C - 1);
+
+  // fragment read offsets (lane parts)
+  int koff[DH / 16];
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) {
+    const int r = lane & 31;
+    koff[s] = r * DH * 2 + (((2 * s + hl) ^ kswz<DH>(r)) << 4);
+  }
+  int voff[BN / 32][2][2];
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int d = lane & 31;
+        const int c = kb * 4 + kc * 2 + h;
+        voff[kb][kc][h] = d * (BN * 2) + ((c ^ (d & 7)) << 4) + hl * 8;
+      }
+
+  auto issue = [&](int64_t kt, uint8_t* kst, uint8_t* vst) {
+    for (int blk = wave; blk < K_BLOCKS; blk += PF_WAVES) {
+      const int r = blk * KRPB + lane / KCH;
+      const int c = (lane % KCH) ^ kswz<DH>(r);
       const int64_t u = kt + r;
       const uint16_t* src;
       if (u < a.f_origin) {
@@ -95,14 +149,12 @@ attn_prefill_kernel(AttnArgs a) {
         const int64_t row = min(u - a.f_origin, a.f_rows - 1);
         src = a.kf + (bg * a.f_rows + row) * DH;
       }
-      *reinterpret_cast<uint4*>(ks + r * KROW + cc * 16) =
-          *reinterpret_cast<const uint4*>(src + cc * 8);
+      dma16_flat(src + c * 8, kst + blk * 1024);
     }
-    // ---- stage V^T tile [DH][BN]; keys at or beyond k_end read as zero
-    for (int c = tid; c < V_CHUNKS; c += NT) {
-      const int d = c / (BN / 8), cc = c % (BN / 8);
-      const int64_t u = kt + cc * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
+    for (int blk = wave; blk < V_BLOCKS; blk += PF_WAVES) {
+      const int d = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (d & 7);
+      const int64_t u = kt + c * 8;
       if (u < k_end) {
         const uint16_t* src;
         if (u < a.f_origin) {
@@ -111,22 +163,31 @@ attn_prefill_kernel(AttnArgs a) {
         } else {
           src = a.vf + (bg * DH + d) * a.f_rows + (u - a.f_origin);
         }
-        v = *reinterpret_cast<const uint4*>(src);
-        if (u + 8 > k_end) {
-          const int keep = (int)(k_end - u);
-          uint16_t* e = reinterpret_cast<uint16_t*>(&v);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j >= keep) e[j] = 0;
-        }
+        dma16_flat(src, vst + blk * 1024);
       }
-      uint2* dst = reinterpret_cast<uint2*>(vs + d * VROW + cc * 16);
-      dst[0] = make_uint2(v.x, v.y);
-      dst[1] = make_uint2(v.z, v.w);
     }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T for BN/32 key blocks
+  __syncthreads();  // zeroed V^T stages visible before any DMA lands
+  issue(kt_first, ks0, vs0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int64_t kt = kt_first + (int64_t)it * BN;
+    wait_vm0_attn();
+    __syncthreads();
+    const bool odd = it & 1;
+    if (it + 1 < ntiles) {
+      if (odd) issue(kt + BN, ks0, vs0);
+      else issue(kt + BN, ks1, vs1);
+    }
+    const uint8_t* kst = odd ? ks1 : ks0;
+    const uint8_t* vst = odd ? vs1 : vs0;
+
+    // tile class for this wave
+    const bool dead = !wave_live || kt > wq_hi ||
+                      (a.window > 0 && wq_lo - (kt + BN - 1) >= a.window);
+    if (dead) continue;
+    const bool interior = kt + BN - 1 <= wq_lo && (a.window == 0 || wq_hi - kt < a.window);
+
     floatx16 sacc[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -134,60 +195,65 @@ attn_prefill_kernel(AttnArgs a) {
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
       for (int s = 0; s < DH / 16; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            ks + (kb * 32 + (lane & 31)) * KROW + (s * 2 + hl) * 16);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+        const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * DH * 2 + koff[s]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[s], sacc[kb], 0, 0, 0);
       }
     }
-    // ---- mask, scale (log2 domain), online softmax
+    if (!interior) {
+      // relative positions fit 32 bits: |pq - u| < C + 64
+      const int rel0 = (int)(pq - kt) - hl * 4;  // pq - (key index within tile)
+      const bool qok = tq < C;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int dist = rel0 - (kb * 32 + (e >> 2) * 8 + (e & 3));  // pq - u
+          const bool vis = qok && dist >= 0 && (a.window == 0 || dist < a.window);
+          if (!vis) sacc[kb][e] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t u = kt + kb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-        const bool vis = tq < C && key_visible(pq, u, a.window);
-        const float sv = vis ? sacc[kb][e] * sl2 : -INFINITY;
-        sacc[kb][e] = sv;
-        mx = fmaxf(mx, sv);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = exp2f(m_run - m_use);
+    const float corr = exp2f((m_run - m_use) * sl2);
     m_run = m_new;
-    l_run *= corr;
+    if (__ballot(corr != 1.f)) {
+      l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < DH / 32; ++i)
+      for (int i = 0; i < DH / 32; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] *= corr;
+        for (int e = 0; e < 16; ++e) o[i][e] *= corr;
+    }
+    const float nm = -m_use * sl2;
     bf16x8 pf[BN / 32][2];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(sacc[kb][e] - m_use);
+        const float p = exp2f(fmaf(sacc[kb][e], sl2, nm));
         l_run += p;
         pf[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
       }
-    // ---- O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) {
-      const uint8_t* vrow = vs + (db * 32 + (lane & 31)) * VROW;
+      const uint8_t* vrow = vst + db * 32 * (BN * 2);
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const int k0 = kb * 32 + kc * 16 + hl * 4;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + k0 * 2);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + (k0 + 8) * 2);
-          bf16x8 vf;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + voff[kb][kc][0]);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + voff[kb][kc][1]);
+          bf16x8 vfr;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { vf[j] = lo[j]; vf[j + 4] = hi[j]; }
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][kc], o[db], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) { vfr[j] = lo[j]; vfr[j + 4] = hi[j]; }
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, pf[kb][kc], o[db], 0, 0, 0);
         }
     }
-    __syncthreads();
   }
 
   // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]

@@ -98,6 +98,11 @@ hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_row
                            int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
                            int64_t ring, hipStream_t st);
 
+// Zero columns [c0, c1) of every row of a fresh V^T buffer
+// ([B][n_kv][dh][f_rows]); the prefill attention reads whole 8-key chunks.
+hipError_t launch_vt_zero_cols(uint16_t* vf, int64_t f_rows, int B, int n_kv, int dh, int64_t c0,
+                               int64_t c1, hipStream_t st);
+
 // Greedy argmax over rows of [rows, n] fp32, lowest index on ties.
 hipError_t launch_argmax(const float* x, int rows, int n, int32_t* out, hipStream_t st);
 

@@ -246,6 +246,15 @@ __global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t 
   vc[(bg * dh + d) * c_rows + crow] = vf[(bg * dh + d) * f_rows + frow];
 }
 
+// Zero V^T columns [c0, c1) of every (b, g, d) row of the fresh buffer.
+__global__ void vt_zero_cols_kernel(uint16_t* vf, int64_t f_rows, int nkv, int dh, int64_t c0,
+                                    int64_t c1) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int64_t bg = (int64_t)b * nkv + g;
+  for (int d = threadIdx.x; d < dh; d += blockDim.x)
+    for (int64_t c = c0; c < c1; ++c) vf[(bg * dh + d) * f_rows + c] = 0;
+}
+
 constexpr int NT_ARG = 1024;
 
 __global__ void __launch_bounds__(NT_ARG) argmax_kernel(const float* x, int n, int32_t* out) {
@@ -348,6 +357,13 @@ hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_row
   if (pos_b <= pos_a) return hipSuccess;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
                      kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_zero_cols(uint16_t* vf, int64_t f_rows, int B, int n_kv, int dh, int64_t c0,
+                               int64_t c1, hipStream_t st) {
+  if (c1 <= c0) return hipSuccess;
+  hipLaunchKernelGGL(vt_zero_cols_kernel, dim3(n_kv, B), dim3(dh), 0, st, vf, f_rows, n_kv, dh, c0, c1);
   return hipGetLastError();
 }
 

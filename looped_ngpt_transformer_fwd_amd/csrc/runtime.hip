@@ -316,6 +316,13 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
       HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh, base,
                             w.s_qk, c.qh(), kd, c.gate(), c.st));
     }
+    {
+      // the attention reads whole 8-key V chunks: zero the columns past the
+      // step's last key up to the chunk boundary
+      const int64_t vend = c.p0 + c.T - f_origin;
+      PROF(c, DORY_K_KV_WRITE);
+      HIPCHK(launch_vt_zero_cols(c.vf(), c.L.f_rows, c.B, s.nkv, s.dh, vend, (vend + 7) / 8 * 8, c.st));
+    }
     if (c.p0 > f_origin) {
       PROF(c, DORY_K_KV_WRITE);
       HIPCHK(launch_prefix_copy(sp.k, sp.v, sp.rows, sp.ring, c.B, s.nkv, s.dh, f_origin, c.p0,
