@@ -61,16 +61,40 @@ attn_prefill_kernel(AttnArgs a) {
   constexpr int KRPB = 1024 / (DH * 2);  // key rows per DMA block
   constexpr int NT = PF_WAVES * 64;
 
+  // Three LDS stages (two tiles in flight), as separate arrays: every LDS
+  // read below names its stage statically, so the compiler can tell it
+  // apart from the DMA still landing in the other stages and does not drain
+  // that DMA before the read.
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t ks1[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[VT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vs1[VT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[VT_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // heaviest query tiles (most keys under the causal mask) start first
-  const int qt = gridDim.x - 1 - blockIdx.x;
-  const int g = blockIdx.y, b = blockIdx.z;
+  // Work order: heaviest query tiles (most keys under the causal mask) first.
+  // Workgroups are dispatched round-robin over the 8 XCDs; when the (batch,
+  // KV head) pairs split evenly, XCD x serves pairs x, x+8, ... only, so the
+  // K/V of a pair is shared through one XCD's L2.
+  const int ntq = gridDim.x, npairs = gridDim.y * gridDim.z;
+  int qt, g, b;
+  {
+    const int lin = blockIdx.x + ntq * (blockIdx.y + gridDim.y * blockIdx.z);
+    if ((npairs & 7) == 0) {
+      const int x = lin & 7, j = lin >> 3;
+      const int ppx = npairs >> 3;
+      const int pair = x + 8 * (j % ppx);
+      qt = ntq - 1 - j / ppx;
+      g = pair % gridDim.y;
+      b = pair / gridDim.y;
+    } else {
+      qt = ntq - 1 - blockIdx.x;
+      g = blockIdx.y;
+      b = blockIdx.z;
+    }
+  }
   const int qb = wave / GRP, head = g * GRP + (wave % GRP);
   const int C = a.C;
   const int t0 = qt * BQ + qb * 32;
@@ -78,14 +102,6 @@ attn_prefill_kernel(AttnArgs a) {
   const int hl = lane >> 5;
   const int64_t bg = (int64_t)b * a.n_kv + g;
   const int64_t pq = a.p0 + tq;
-
-  // V^T stages start zeroed: lanes whose keys lie past the last key skip
-  // their DMA, and the probabilities (exactly 0) of those keys must meet
-  // finite values
-  for (int i = tid; i < VT_BYTES / 16; i += NT) {
-    reinterpret_cast<uint4*>(vs0)[i] = make_uint4(0, 0, 0, 0);
-    reinterpret_cast<uint4*>(vs1)[i] = make_uint4(0, 0, 0, 0);
-  }
 
   bf16x8 qf[DH / 16];
   {
@@ -137,7 +153,10 @@ attn_prefill_kernel(AttnArgs a) {
       }
 
   auto issue = [&](int64_t kt, uint8_t* kst, uint8_t* vst) {
-    for (int blk = wave; blk < K_BLOCKS; blk += PF_WAVES) {
+#pragma unroll
+    for (int j = 0; j < (K_BLOCKS + PF_WAVES - 1) / PF_WAVES; ++j) {
+      const int blk = wave + j * PF_WAVES;
+      if (K_BLOCKS % PF_WAVES != 0 && blk >= K_BLOCKS) break;
       const int r = blk * KRPB + lane / KCH;
       const int c = (lane % KCH) ^ kswz<DH>(r);
       const int64_t u = kt + r;
@@ -151,41 +170,57 @@ attn_prefill_kernel(AttnArgs a) {
       }
       dma16_flat(src + c * 8, kst + blk * 1024);
     }
-    for (int blk = wave; blk < V_BLOCKS; blk += PF_WAVES) {
+#pragma unroll
+    for (int j = 0; j < (V_BLOCKS + PF_WAVES - 1) / PF_WAVES; ++j) {
+      const int blk = wave + j * PF_WAVES;
+      if (V_BLOCKS % PF_WAVES != 0 && blk >= V_BLOCKS) break;
       const int d = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ (d & 7);
-      const int64_t u = kt + c * 8;
-      if (u < k_end) {
-        const uint16_t* src;
-        if (u < a.f_origin) {
-          const int64_t col = a.ring > 0 ? u % a.ring : u;
-          src = a.vc + (bg * DH + d) * a.c_rows + col;
-        } else {
-          src = a.vf + (bg * DH + d) * a.f_rows + (u - a.f_origin);
-        }
-        dma16_flat(src, vst + blk * 1024);
+      // chunks at or past the last key load the row's first chunk instead:
+      // finite values that meet probabilities of exactly 0 (the loads stay
+      // unconditional so every wave issues a fixed number per tile)
+      int64_t u = kt + c * 8;
+      const uint16_t* src;
+      if (u >= k_end) {
+        src = a.f_origin > 0 ? a.vc + (bg * DH + d) * a.c_rows : a.vf + (bg * DH + d) * a.f_rows;
+      } else if (u < a.f_origin) {
+        const int64_t col = a.ring > 0 ? u % a.ring : u;
+        src = a.vc + (bg * DH + d) * a.c_rows + col;
+      } else {
+        src = a.vf + (bg * DH + d) * a.f_rows + (u - a.f_origin);
       }
+      dma16_flat(src, vst + blk * 1024);
     }
   };
+  // DMA instructions issued per tile by this wave
+  const int per_tile = (K_BLOCKS > wave ? (K_BLOCKS - wave + PF_WAVES - 1) / PF_WAVES : 0) +
+                       (V_BLOCKS > wave ? (V_BLOCKS - wave + PF_WAVES - 1) / PF_WAVES : 0);
 
-  __syncthreads();  // zeroed V^T stages visible before any DMA lands
+  // the query fragments must have landed before the DMA stream starts: the
+  // vmcnt waits in the loop count DMA only
+  wait_vm0_attn();
   issue(kt_first, ks0, vs0);
-  for (int it = 0; it < ntiles; ++it) {
+  if (ntiles > 1) issue(kt_first + BN, ks1, vs1);
+
+  auto tile = [&](int it, const uint8_t* kst, const uint8_t* vst, uint8_t* kn, uint8_t* vn) {
     const int64_t kt = kt_first + (int64_t)it * BN;
-    wait_vm0_attn();
-    __syncthreads();
-    const bool odd = it & 1;
+    // this wave's loads of tile `it` are done once at most the next tile's
+    // loads are outstanding
     if (it + 1 < ntiles) {
-      if (odd) issue(kt + BN, ks0, vs0);
-      else issue(kt + BN, ks1, vs1);
+      if (per_tile == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+      else if (per_tile == 2) __builtin_amdgcn_s_waitcnt(0x0F72);
+      else if (per_tile == 1) __builtin_amdgcn_s_waitcnt(0x0F71);
+      else wait_vm0_attn();
+    } else {
+      wait_vm0_attn();
     }
-    const uint8_t* kst = odd ? ks1 : ks0;
-    const uint8_t* vst = odd ? vs1 : vs0;
+    barrier_lds();
+    if (it + 2 < ntiles) issue(kt + 2 * BN, kn, vn);
 
     // tile class for this wave
     const bool dead = !wave_live || kt > wq_hi ||
                       (a.window > 0 && wq_lo - (kt + BN - 1) >= a.window);
-    if (dead) continue;
+    if (dead) return;
     const bool interior = kt + BN - 1 <= wq_lo && (a.window == 0 || wq_hi - kt < a.window);
 
     floatx16 sacc[BN / 32];
@@ -220,7 +255,7 @@ attn_prefill_kernel(AttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = exp2f((m_run - m_use) * sl2);
+    const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * sl2);
     m_run = m_new;
     if (__ballot(corr != 1.f)) {
       l_run *= corr;
@@ -235,7 +270,7 @@ attn_prefill_kernel(AttnArgs a) {
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(fmaf(sacc[kb][e], sl2, nm));
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, nm));
         l_run += p;
         pf[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
       }
@@ -254,6 +289,15 @@ attn_prefill_kernel(AttnArgs a) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, pf[kb][kc], o[db], 0, 0, 0);
         }
     }
+  };
+
+  // stage of tile t is t % 3; the tile two ahead goes into stage (t + 2) % 3.
+  // At the loop header the compiler cannot count the DMA in flight and
+  // drains it before the first LDS read, once per 3 tiles.
+  for (int it = 0; it < ntiles; it += 3) {
+    tile(it, ks0, vs0, ks2, vs2);
+    if (it + 1 < ntiles) tile(it + 1, ks1, vs1, ks0, vs0);
+    if (it + 2 < ntiles) tile(it + 2, ks2, vs2, ks1, vs1);
   }
 
   // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]

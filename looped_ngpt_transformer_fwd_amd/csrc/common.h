@@ -58,6 +58,15 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 
 namespace dory {
 
+// Workgroup barrier that waits only for this wave's own LDS operations.
+// Pipelines that stage tiles with global->LDS DMA wait for the DMA they need
+// with an explicit vmcnt before calling it, so that younger DMA (the next
+// tiles) stays in flight across the barrier; __syncthreads() would drain it.
+// The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Attention visibility: a query at position p sees key u iff u <= p and, for
 // a sliding-window layer (window > 0), p - u < window.
 __device__ __forceinline__ bool key_visible(int64_t p, int64_t u, int window) {
