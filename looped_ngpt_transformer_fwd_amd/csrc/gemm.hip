@@ -327,7 +327,66 @@ gemm_big_kernel(GemmArgs g) {
 
   const int rbase = m0 + wm * BIG_WM + (lane >> 5) * 4;
   const int cbase = n0 + wn * BIG_WN + (lane & 31);
-  if (EPI == EPI_F32 || EPI == EPI_LOGITS) {
+  if (EPI == EPI_QKV) {
+    // Each wave's 128 columns are one head of q, k, v or the gate. Lane holds
+    // head dims d = 32 j + (lane & 31), j = 0..3, for 32 rows; RoPE pairs
+    // (d, d + 64) are (j, j + 2) of the same lane; the per-head norm sums the
+    // lane's 4 values and reduces over the 32 lanes that share its rows.
+    const QkvEpi& q = g.qkv;
+    const int dq = q.nq * 128, dkv = q.nkv * 128;
+    const int c0 = n0 + wn * BIG_WN;
+    const int dl = lane & 31;
+    int kind, hh;
+    if (c0 < dq) { kind = 0; hh = c0 >> 7; }
+    else if (c0 < dq + dkv) { kind = 1; hh = (c0 - dq) >> 7; }
+    else if (c0 < dq + 2 * dkv) { kind = 2; hh = (c0 - dq - dkv) >> 7; }
+    else { kind = 3; hh = (c0 - dq - 2 * dkv) >> 7; }
+    if (c0 >= g.N) kind = 4;
+    float sq0 = 0.f, sq1 = 0.f;
+    if (kind <= 1) { sq0 = q.s_qk[dl]; sq1 = q.s_qk[dl + 32]; }
+    float sq2 = kind <= 1 ? q.s_qk[dl + 64] : 0.f, sq3 = kind <= 1 ? q.s_qk[dl + 96] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
+        const bool ok = row < g.M;
+        const int b = row / q.T, t = row - b * q.T;
+        float x0 = acc[i][0][e], x1 = acc[i][1][e], x2 = acc[i][2][e], x3 = acc[i][3][e];
+        if (kind <= 1) {
+          const int tr = ok ? t : 0;
+          const float c0f = q.cs[tr * 64 + dl], s0f = q.sn[tr * 64 + dl];
+          const float c1f = q.cs[tr * 64 + 32 + dl], s1f = q.sn[tr * 64 + 32 + dl];
+          const float r0 = x0 * c0f - x2 * s0f, r2 = x2 * c0f + x0 * s0f;
+          const float r1 = x1 * c1f - x3 * s1f, r3 = x3 * c1f + x1 * s1f;
+          float ss = r0 * r0 + r1 * r1 + r2 * r2 + r3 * r3;
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+          const float inv = 1.0f / sqrtf(ss);
+          x0 = r0 * inv * sq0; x1 = r1 * inv * sq1; x2 = r2 * inv * sq2; x3 = r3 * inv * sq3;
+          if (ok) {
+            uint16_t* dst = kind == 0
+                ? q.qh + (((int64_t)b * q.nq + hh) * q.T + t) * 128
+                : q.kf + (((int64_t)b * q.nkv + hh) * q.f_rows + t + q.row_off) * 128;
+            dst[dl] = f2bf(x0); dst[dl + 32] = f2bf(x1); dst[dl + 64] = f2bf(x2); dst[dl + 96] = f2bf(x3);
+          }
+        } else if (kind == 2) {
+          if (ok) {
+            uint16_t* dst = q.vf + (((int64_t)b * q.nkv + hh) * 128 + dl) * q.f_rows + t + q.row_off;
+            const int64_t cstep = 32 * q.f_rows;
+            dst[0] = f2bf(x0); dst[cstep] = f2bf(x1); dst[2 * cstep] = f2bf(x2); dst[3 * cstep] = f2bf(x3);
+          }
+        } else if (kind == 3) {
+          if (ok) {
+            uint16_t* dst = q.gate + (int64_t)row * dq + hh * 128;
+            dst[dl] = f2bf(1.f / (1.f + __expf(-x0)));
+            dst[dl + 32] = f2bf(1.f / (1.f + __expf(-x1)));
+            dst[dl + 64] = f2bf(1.f / (1.f + __expf(-x2)));
+            dst[dl + 96] = f2bf(1.f / (1.f + __expf(-x3)));
+          }
+        }
+      }
+  } else if (EPI == EPI_F32 || EPI == EPI_LOGITS) {
     float* C = g.C;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -372,6 +431,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, hipStream_t st) {
     case EPI_F32: hipLaunchKernelGGL((gemm_big_kernel<EPI_F32>), grid, block, 0, st, a); break;
     case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big_kernel<EPI_SWIGLU>), grid, block, 0, st, a); break;
     case EPI_LOGITS: hipLaunchKernelGGL((gemm_big_kernel<EPI_LOGITS>), grid, block, 0, st, a); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_big_kernel<EPI_QKV>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -408,6 +468,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.K % BK != 0 || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi != EPI_F32 && a.nsplit != 1) return hipErrorInvalidValue;
   if (a.M >= kLargeM) return launch_big(a, epi, st);
+  if (epi == EPI_QKV) return hipErrorInvalidValue;
   return launch_cfg<64, 128, 32, 64>(a, epi, st);
 }
 

@@ -16,6 +16,24 @@ enum GemmEpi {
   EPI_SWIGLU = 1,  // B = [W_up; W_gate] (2F rows); C16[m, f] =
                    //   bf16(SiLU(s2[f] * gate) * s1[f] * up); N = 2F; no split
   EPI_LOGITS = 2,  // C[m, n] = s1[n] * acc; no split
+  EPI_QKV = 3,     // fused query/key transform (large-M path, head_dim 128):
+                   // columns of B = w_qkvg; writes q_hat, fresh K, fresh V^T
+                   // and sigma(gate) as qk_prep does (see QkvEpi)
+};
+
+// Destinations of the fused q/k/v/gate epilogue. Row m = b * T + t is the
+// token at position p0 + t; cs/sn hold cos/sin of RoPE angle (p0 + t) *
+// theta_i as [T][64].
+struct QkvEpi {
+  uint16_t* qh = nullptr;     // [B][n_q][T][128]
+  uint16_t* kf = nullptr;     // [B][n_kv][f_rows][128], row t + row_off
+  uint16_t* vf = nullptr;     // [B][n_kv][128][f_rows], column t + row_off
+  uint16_t* gate = nullptr;   // [B*T][n_q*128]
+  const float* cs = nullptr;
+  const float* sn = nullptr;
+  const float* s_qk = nullptr;
+  int T = 0, nq = 0, nkv = 0;
+  int64_t f_rows = 0, row_off = 0;
 };
 
 struct GemmArgs {
@@ -33,6 +51,7 @@ struct GemmArgs {
   const float* s1 = nullptr;
   const float* s2 = nullptr;
   int F = 0;
+  QkvEpi qkv;
 };
 
 // Picks a tile configuration and split factor; `max_split` bounds the split
@@ -83,6 +102,11 @@ hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int 
                           int64_t p0, int n_q, int n_kv, int dh, double rope_base,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
                           hipStream_t st);
+
+// RoPE table for positions p0 .. p0 + T - 1: cs/sn [T][dh/2] fp32 from fp64
+// angles (p0 + t) * base^(-2i/dh).
+hipError_t launch_rope_table(int64_t p0, int T, int dh, double base, float* cs, float* sn,
+                             hipStream_t st);
 
 // Copy cached K / V^T entries of positions [pos_a, pos_b) into the fresh
 // buffers (layout as QkDest with pos_origin = pos_a, no ring).

@@ -246,6 +246,18 @@ __global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t 
   vc[(bg * dh + d) * c_rows + crow] = vf[(bg * dh + d) * f_rows + frow];
 }
 
+__global__ void rope_table_kernel(int64_t p0, int T, int half, int dh, double base, float* cs,
+                                  float* sn) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * half) return;
+  const int t = (int)(idx / half), i = (int)(idx % half);
+  const double invf = pow(base, -2.0 * (double)i / (double)dh);
+  double s, c;
+  sincos((double)(p0 + t) * invf, &s, &c);
+  cs[idx] = (float)c;
+  sn[idx] = (float)s;
+}
+
 // Zero V^T columns [c0, c1) of every (b, g, d) row of the fresh buffer.
 __global__ void vt_zero_cols_kernel(uint16_t* vf, int64_t f_rows, int nkv, int dh, int64_t c0,
                                     int64_t c1) {
@@ -357,6 +369,15 @@ hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_row
   if (pos_b <= pos_a) return hipSuccess;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
                      kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(int64_t p0, int T, int dh, double base, float* cs, float* sn,
+                             hipStream_t st) {
+  const int half = dh / 2;
+  const int64_t n = (int64_t)T * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p0, T,
+                     half, dh, base, cs, sn);
   return hipGetLastError();
 }
 

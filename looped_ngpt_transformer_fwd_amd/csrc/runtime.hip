@@ -107,7 +107,7 @@ size_t slot_bytes(const Shape& s, int kind, int batch, int64_t max_seq) {
 
 // Workspace layout for B sequences of T tokens.
 struct WsLayout {
-  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, total;
+  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, rope, total;
   int64_t f_rows;
 };
 
@@ -135,6 +135,8 @@ WsLayout plan_ws(const Shape& s, int B, int T) {
   L.P = take((size_t)nsplit * M * ncols * 4);
   L.part = take((size_t)decode_attn_part_floats(B, s.nq, s.dh, kMaxDecodeSplits) * 4);
   L.logits = s.lm ? take((size_t)B * s.V * 4) : 0;
+  // cos / sin tables of the step's positions for the two RoPE bases
+  L.rope = take((size_t)4 * T * (s.dh / 2) * 4);
   L.total = off;
   return L;
 }
@@ -236,6 +238,13 @@ struct Ctx {
   float* P() const { return reinterpret_cast<float*>(ws + L.P); }
   float* part() const { return reinterpret_cast<float*>(ws + L.part); }
   float* logits_scratch() const { return reinterpret_cast<float*>(ws + L.logits); }
+  // table 0 = sliding-window base, 1 = full-attention base
+  float* rope_cs(int full) const {
+    return reinterpret_cast<float*>(ws + L.rope) + (size_t)(2 * full) * T * (s.dh / 2);
+  }
+  float* rope_sn(int full) const { return rope_cs(full) + (size_t)T * (s.dh / 2); }
+  // prefill projections take the fused q/k/v/gate epilogue
+  bool fused_qkv() const { return T > 1 && M >= kLargeM && s.dh == 128; }
   Profiler* prof() const { return &m->prof; }
 };
 
@@ -279,8 +288,25 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
   const double base = full ? s.base_full : s.base_swa;
   const SlotPtr sp = slot_ptr(c.kv, i, slot);
   int ns = 1;
-  dory_status st = gemm_f32(c, c.h16(), s.d, w.w_qkvg, s.nqkvg(), s.d, c.M, &ns, DORY_K_GEMM_QKVG);
-  if (st != DORY_OK) return st;
+  dory_status st = DORY_OK;
+  const int64_t f_origin = c.p0 / 8 * 8;
+  if (c.fused_qkv()) {
+    // projections with RoPE / per-head norm / s_qk / K-V placement / gate in
+    // the GEMM epilogue
+    PROF(c, DORY_K_GEMM_QKVG);
+    GemmArgs g;
+    g.A = c.h16(); g.lda = s.d;
+    g.B = reinterpret_cast<const uint16_t*>(w.w_qkvg); g.ldb = s.d;
+    g.M = (int)c.M; g.N = s.nqkvg(); g.K = s.d; g.nsplit = 1;
+    g.qkv.qh = c.qh(); g.qkv.kf = c.kf(); g.qkv.vf = c.vf(); g.qkv.gate = c.gate();
+    g.qkv.cs = c.rope_cs(full ? 1 : 0); g.qkv.sn = c.rope_sn(full ? 1 : 0);
+    g.qkv.s_qk = w.s_qk; g.qkv.T = c.T; g.qkv.nq = s.nq; g.qkv.nkv = s.nkv;
+    g.qkv.f_rows = c.L.f_rows; g.qkv.row_off = c.p0 - f_origin;
+    HIPCHK(launch_gemm(g, EPI_QKV, c.st));
+  } else {
+    st = gemm_f32(c, c.h16(), s.d, w.w_qkvg, s.nqkvg(), s.d, c.M, &ns, DORY_K_GEMM_QKVG);
+    if (st != DORY_OK) return st;
+  }
   const int64_t split_stride = c.M * s.nqkvg();
 
   AttnArgs aa{};
@@ -309,9 +335,8 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     // prefill: fresh K/V of the step live in the workspace, rows counted from
     // f_origin (the step's first position rounded down to a multiple of 8);
     // cached positions [f_origin, p0) are copied in front of them
-    const int64_t f_origin = c.p0 / 8 * 8;
-    QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
-    {
+    if (!c.fused_qkv()) {
+      QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
       PROF(c, DORY_K_QK);
       HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh, base,
                             w.s_qk, c.qh(), kd, c.gate(), c.st));
@@ -390,6 +415,11 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   const Shape& s = c.s;
   const int64_t Md = c.M * s.d;
   const bool per_loop = c.kv->mode == DORY_CACHE_PER_LOOP;
+  if (c.fused_qkv()) {
+    PROF(c, DORY_K_QK);
+    HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_swa, c.rope_cs(0), c.rope_sn(0), c.st));
+    HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_full, c.rope_cs(1), c.rope_sn(1), c.st));
+  }
   {
     PROF(c, DORY_K_OTHER);
     HIPCHK(launch_embed(tokens, c.m->embed, s.V, (int)c.M, s.d, c.h32(), c.h16(),

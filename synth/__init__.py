@@ -78,6 +78,12 @@ MID = Shape(d_model=192, n_q_heads=4, n_kv_heads=2, head_dim=32, d_ff=320,
             vocab=300, n_input=2, n_recurrent=4, n_output=2, window=64,
             layer_kinds=(KIND_SWA, KIND_MLP, KIND_SWA, KIND_MLP, KIND_FULL, KIND_MLP,
                          KIND_FULL, KIND_MLP))
+# Mid-size model with 128-wide heads: its prefill projections take the fused
+# q/k/v/gate GEMM epilogue (one head per 128 output columns).
+MID128 = Shape(d_model=256, n_q_heads=2, n_kv_heads=1, head_dim=128, d_ff=512,
+               vocab=300, n_input=2, n_recurrent=4, n_output=2, window=64,
+               layer_kinds=(KIND_SWA, KIND_MLP, KIND_SWA, KIND_MLP, KIND_FULL, KIND_MLP,
+                            KIND_FULL, KIND_MLP))
 # Full-size shape: d=2304, 16 query / 4 KV heads of 128, SwiGLU 6144,
 # vocab 131072, 16 input + 40 recurrent + 16 output sublayers, window 1024.
 FULL = Shape(d_model=2304, n_q_heads=16, n_kv_heads=4, head_dim=128, d_ff=6144,

@@ -23,19 +23,20 @@ def M():
     return model
 
 
+@pytest.mark.parametrize("shape_name", ["mid", "mid128"])
 @pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
-def test_mid_model_large_gemm_path(M, mode):
-    shape = synth.MID
+def test_mid_model_large_gemm_path(M, mode, shape_name):
+    shape = {"mid": synth.MID, "mid128": synth.MID128}[shape_name]
     k = 2
-    log(f"mid {mode}")
+    log(f"{shape_name} {mode}")
     W = synth.Weights(shape, ref.layer_kinds(shape), 3)
     gm = M.Model(shape, upload(W))
     om = oracle_model(shape, W)
     B = 1
-    toks = synth.tokens(9, B, 1300, shape.vocab)
-    kv = gm.kv_cache(mode, k, B, 1400)
+    toks = synth.tokens(9, B, 2213, shape.vocab)
+    kv = gm.kv_cache(mode, k, B, 2300)
     oc = ref.Cache(shape, mode, B)
-    for a, b in [(0, 1100), (1100, 1300)]:
+    for a, b in [(0, 1100), (1100, 2213)]:
         out = gm.prefill(kv, torch.from_numpy(toks[:, a:b].copy()).cuda(), k, hidden=True,
                          states=True)
         torch.cuda.synchronize()
