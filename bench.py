@@ -200,6 +200,11 @@ def main():
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--no-extra", action="store_true", help="skip k-sweep and decode table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode table (B=64, 32768 cached tokens), for profiling")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 4 GiB device-to-device copy first (reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -210,12 +215,23 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     from looped_ngpt_transformer_fwd_amd import model as M
+    if args.calibrate_copy:
+        # 2^30 fp32 = 4 GiB read and 4 GiB written by one copy kernel
+        src = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     shape = synth.FULL
     B, T, k = 4, 8192, args.k
     kinds = M.schedule(shape)
     weights = gpu_weights(shape, kinds)
     gm = M.Model(shape, weights)
+    if args.decode_only:
+        print(json.dumps({"decode_tok_s": decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))}),
+              flush=True)
+        return
     ws = gm.workspace(B, T)
     g = torch.Generator(device="cuda")
     g.manual_seed(0)

@@ -300,20 +300,58 @@ attn_prefill_kernel(AttnArgs a) {
     if (it + 2 < ntiles) tile(it + 2, ks2, vs2, ks1, vs1);
   }
 
-  // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]
+  // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]. The O^T
+  // registers hold one query per lane, so the 32 x DH tile of a wave is
+  // transposed through LDS (the stage buffers, free after the loop) and
+  // written as contiguous 16-byte pieces of each query row. Waves 0-5 use
+  // one stage buffer each, then waves 6-7.
   l_run += __shfl_xor(l_run, 32, 64);
-  if (tq < C) {
-    const float il = 1.0f / l_run;
-    const int dq = a.n_q * DH;
-    const int64_t zrow = ((int64_t)b * C + tq) * dq + head * DH;
+  const float il = l_run > 0.f ? 1.0f / l_run : 0.f;
+  constexpr int EP_ROW = DH * 2 + 16;   // padded LDS row (16-byte aligned)
+  constexpr int CPR = DH / 8;           // 16-byte chunks per query row
+  static_assert(32 * EP_ROW <= KT_BYTES && 32 * EP_ROW <= VT_BYTES, "epilogue staging");
+  const int dq = a.n_q * DH;
+  __syncthreads();
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
+  for (int round = 0; round < 2; ++round) {
+    const bool active = round == 0 ? wave < 6 : wave >= 6;
+    const int slot = wave % 6;
+    uint8_t* buf = slot == 0 ? ks0 : slot == 1 ? ks1 : slot == 2 ? ks2 : slot == 3 ? vs0 : slot == 4 ? vs1 : vs2;
+    if (active) {
+      const int q = lane & 31;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int d = db * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-        const float gv = bf2f(a.gate[zrow + d]);
-        a.z[zrow + d] = f2bf(o[db][e] * il * gv);
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int eq = 0; eq < 4; ++eq) {
+          const int d0 = db * 32 + eq * 8 + hl * 4;
+          bf16x4 v4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(o[db][eq * 4 + j] * il);
+          *reinterpret_cast<bf16x4*>(buf + q * EP_ROW + d0 * 2) = v4;
+        }
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 32 * CPR / 64; ++j) {
+        const int c = lane + 64 * j;
+        const int q = c / CPR, cc = c % CPR;
+        const int t = t0 + q;
+        if (t < C) {
+          const uint4 ov = *reinterpret_cast<const uint4*>(buf + q * EP_ROW + cc * 16);
+          const int64_t off = ((int64_t)b * C + t) * dq + head * DH + cc * 8;
+          const uint4 gv = *reinterpret_cast<const uint4*>(a.gate + off);
+          const uint16_t* oe = reinterpret_cast<const uint16_t*>(&ov);
+          const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
+          uint4 zv;
+          uint16_t* ze = reinterpret_cast<uint16_t*>(&zv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) ze[k] = f2bf(bf2f(oe[k]) * bf2f(ge[k]));
+          *reinterpret_cast<uint4*>(a.z + off) = zv;
+        }
       }
+    }
+    __syncthreads();
   }
 }
 

@@ -197,8 +197,7 @@ gemm_nt_kernel(GemmArgs g) {
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives
 // each XCD a contiguous range of tiles, traversed in groups of 8 row panels,
 // so concurrently running tiles of one XCD share A and B panels in its L2.
-constexpr int BIG_BM = 256, BIG_BN = 256, BIG_WM = 64, BIG_WN = 128;
-constexpr int BIG_NT = 512;
+constexpr int BIG_BM = 256, BIG_BN = 256;
 constexpr int BIG_TILE_BYTES = 256 * 128;  // one operand tile of one stage
 
 __device__ __forceinline__ void big_tile_coords(int bid, int ntm, int ntn, int* tm, int* tn) {
@@ -231,28 +230,34 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // vmcnt(0), expcnt/lgkmcnt untouched
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+template <int FM, int FN>
 __device__ __forceinline__ void big_compute(const uint8_t* sa, const uint8_t* sb,
-                                            const int (&loff)[4], floatx16 (&acc)[2][4]) {
+                                            const int (&loff)[4], floatx16 (&acc)[FM][FN]) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 af[2], bfr[4];
+    bf16x8 af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
       af[i] = *reinterpret_cast<const bf16x8*>(sa + i * 32 * 128 + loff[kk]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
       bfr[j] = *reinterpret_cast<const bf16x8*>(sb + j * 32 * 128 + loff[kk]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   }
 }
 
-template <int EPI>
-__global__ void __launch_bounds__(BIG_NT, 1)
+template <int EPI, int WAVES_M, int WAVES_N>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
 gemm_big_kernel(GemmArgs g) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int BIG_WM = BIG_BM / WAVES_M, BIG_WN = BIG_BN / WAVES_N;
+  constexpr int FM = BIG_WM / 32, FN = BIG_WN / 32;
+  constexpr int BPW = 32 / NW;               // DMA blocks per wave per operand
+  static_assert(BIG_WN == 128, "epilogues assume 128 columns per wave");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[BIG_TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[BIG_TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[BIG_TILE_BYTES];
@@ -260,7 +265,7 @@ gemm_big_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int ntm = (g.M + BIG_BM - 1) / BIG_BM, ntn = (g.N + BIG_BN - 1) / BIG_BN;
   int tm, tn;
   big_tile_coords(blockIdx.x, ntm, ntn, &tm, &tn);
@@ -271,13 +276,13 @@ gemm_big_kernel(GemmArgs g) {
   const int brows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)(brows - 1) * g.ldb * 2 + g.K * 2));
 
-  // DMA sources: wave w fills blocks w, w+8, w+16, w+24 of each operand tile
+  // DMA sources: wave w fills blocks w, w+NW, w+2NW, ... of each operand tile
   const int lr = lane >> 3;                 // row within the block
   const int lc = (lane & 7) ^ lr;           // logical chunk fetched by this lane
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[BPW], boff[BPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave + 8 * i) * 8 + lr;
+  for (int i = 0; i < BPW; ++i) {
+    const int r = (wave + NW * i) * 8 + lr;
     aoff[i] = (uint32_t)((int64_t)min(m0 + r, g.M - 1) * g.lda * 2 + lc * 16);
     int v = min(n0 + r, g.N - 1);
     int row = v;
@@ -295,20 +300,20 @@ gemm_big_kernel(GemmArgs g) {
   for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ (fr & 7)) << 4);
   const int a_wave = wm * BIG_WM * 128, b_wave = wn * BIG_WN * 128;
 
-  floatx16 acc[2][4];
+  floatx16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
 #define DORY_ISSUE(KS, SA, SB)                                              \
   do {                                                                      \
     const uint32_t ko_ = (uint32_t)(KS) * (BK * 2);                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                      \
-      dma16(ra, aoff[i_], ko_, (SA) + (wave + 8 * i_) * 1024);              \
-      dma16(rb, boff[i_], ko_, (SB) + (wave + 8 * i_) * 1024);              \
+    _Pragma("unroll") for (int i_ = 0; i_ < BPW; ++i_) {                    \
+      dma16(ra, aoff[i_], ko_, (SA) + (wave + NW * i_) * 1024);             \
+      dma16(rb, boff[i_], ko_, (SB) + (wave + NW * i_) * 1024);             \
     }                                                                       \
   } while (0)
 
@@ -346,7 +351,7 @@ gemm_big_kernel(GemmArgs g) {
     if (kind <= 1) { sq0 = q.s_qk[dl]; sq1 = q.s_qk[dl + 32]; }
     float sq2 = kind <= 1 ? q.s_qk[dl + 64] : 0.f, sq3 = kind <= 1 ? q.s_qk[dl + 96] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
@@ -394,7 +399,7 @@ gemm_big_kernel(GemmArgs g) {
       if (col >= g.N) continue;
       const float sc = (EPI == EPI_LOGITS) ? g.s1[col] : 1.f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
@@ -409,7 +414,7 @@ gemm_big_kernel(GemmArgs g) {
       const int f = ((v >> 6) << 5) | (v & 31);
       const float su = g.s1[f], sv = g.s2[f];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
@@ -424,14 +429,19 @@ gemm_big_kernel(GemmArgs g) {
   }
 }
 
+// Tile shape of the large-M kernel: 8 waves of 64 x 128 (two waves per SIMD)
+// or 4 waves of 128 x 128 (one wave per SIMD, accumulators in AGPRs, a
+// third less LDS fragment traffic per MFMA).
+constexpr int BIG_WAVES_M = 4, BIG_WAVES_N = 2;
+
 hipError_t launch_big(const GemmArgs& a, int epi, hipStream_t st) {
   const int tiles = ((a.M + BIG_BM - 1) / BIG_BM) * ((a.N + BIG_BN - 1) / BIG_BN);
-  dim3 grid(tiles), block(BIG_NT);
+  dim3 grid(tiles), block(64 * BIG_WAVES_M * BIG_WAVES_N);
   switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL((gemm_big_kernel<EPI_F32>), grid, block, 0, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big_kernel<EPI_SWIGLU>), grid, block, 0, st, a); break;
-    case EPI_LOGITS: hipLaunchKernelGGL((gemm_big_kernel<EPI_LOGITS>), grid, block, 0, st, a); break;
-    case EPI_QKV: hipLaunchKernelGGL((gemm_big_kernel<EPI_QKV>), grid, block, 0, st, a); break;
+    case EPI_F32: hipLaunchKernelGGL((gemm_big_kernel<EPI_F32, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big_kernel<EPI_SWIGLU, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_big_kernel<EPI_LOGITS, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_big_kernel<EPI_QKV, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
