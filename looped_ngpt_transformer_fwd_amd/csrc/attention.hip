@@ -357,16 +357,21 @@ attn_prefill_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ decode
 constexpr int DEC_NT = 256;
-constexpr int DEC_MAXK = 512;  // keys per split
+constexpr int DEC_MAXK = 512;  // keys per split, a multiple of 64
 
+// One workgroup per (split, KV head, sequence). The keys of the query at
+// position p are [lo, p] (lo = p - W + 1 for sliding-window layers); splits
+// are windows of DEC_MAXK keys aligned to 64-key blocks starting at
+// floor(lo / 64) * 64, so that V^T rows are read as aligned 16-byte chunks.
+// Keys outside [lo, p] inside a window get probability 0 and are never read
+// (cache rows past p may not be written yet).
 template <int DH, int GRP>
 __global__ void __launch_bounds__(DEC_NT)
 attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   __shared__ float qs[GRP][DH];
   __shared__ float sc[GRP][DEC_MAXK];
   __shared__ float red[GRP][DEC_NT / 64];
-  constexpr int HALVES = DEC_NT / DH;   // threads per head dim in the V pass
-  __shared__ float ostage[HALVES][GRP][DH];
+  __shared__ float ostage[GRP][DH];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -374,11 +379,9 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   const int64_t p = a.p0;  // query position; cache rows hold keys 0..p
   int64_t lo = 0;
   if (a.window > 0) lo = max((int64_t)0, p - a.window + 1);
-  const int64_t nkeys = p - lo + 1;
-  const int64_t per = (nkeys + nsplit - 1) / nsplit;
-  const int64_t ka = lo + split * per;
-  const int64_t kb_ = min(p + 1, ka + per);
-  const int nk = (int)max((int64_t)0, kb_ - ka);
+  const int64_t A = (lo / 64) * 64 + (int64_t)split * DEC_MAXK;
+  const int64_t ua = max(lo, A), ub = min(p + 1, A + DEC_MAXK);
+  const int nloc = (int)max((int64_t)0, ub - A);  // local keys [0, nloc) examined
 
   for (int i = tid; i < GRP * DH; i += DEC_NT) {
     const int h = i / DH, d = i % DH;
@@ -386,22 +389,24 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   }
   __syncthreads();
 
-  // ---- scores: 16 lanes per key row (8 dims each), 4 keys per wave pass
-  constexpr int LPK = DH / 8;            // lanes per key
-  constexpr int KPW = 64 / LPK;          // keys per wave pass
+  // ---- scores: DH/8 lanes per 2*DH-byte key row (8 dims each)
+  constexpr int LPK = DH / 8;
+  constexpr int KPW = 64 / LPK;
   const int sub = lane % LPK, kl = lane / LPK;
   float qreg[GRP][8];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
 #pragma unroll
     for (int j = 0; j < 8; ++j) qreg[h][j] = qs[h][sub * 8 + j];
-  for (int k0 = wave * KPW; k0 < nk; k0 += (DEC_NT / 64) * KPW) {
+  const float sl2 = a.scale * kLog2e;
+  for (int k0 = wave * KPW; k0 < nloc; k0 += (DEC_NT / 64) * KPW) {
     const int kk = k0 + kl;
+    const int64_t u = A + kk;
+    const bool valid = kk < nloc && u >= ua;
     float acc[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) acc[h] = 0.f;
-    if (kk < nk) {
-      const int64_t u = ka + kk;
+    if (valid) {
       const int64_t row = a.ring > 0 ? u % a.ring : u;
       const uint4 raw = *reinterpret_cast<const uint4*>(a.kc + (bg * a.c_rows + row) * DH + sub * 8);
       const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
@@ -417,19 +422,19 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 #pragma unroll
       for (int o = LPK / 2; o > 0; o >>= 1) acc[h] += __shfl_xor(acc[h], o, 64);
     }
-    if (sub == 0 && kk < nk) {
+    if (sub == 0 && kk < nloc) {
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) sc[h][kk] = acc[h] * a.scale * kLog2e;
+      for (int h = 0; h < GRP; ++h) sc[h][kk] = valid ? acc[h] * sl2 : -INFINITY;
     }
   }
   __syncthreads();
 
-  // ---- softmax pieces per head
+  // ---- softmax pieces per head (base-2 domain)
   float mh[GRP], lh[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
     float m = -INFINITY;
-    for (int i = tid; i < nk; i += DEC_NT) m = fmaxf(m, sc[h][i]);
+    for (int i = tid; i < nloc; i += DEC_NT) m = fmaxf(m, sc[h][i]);
     m = wave_max(m);
     if (lane == 0) red[h][wave] = m;
   }
@@ -445,7 +450,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   for (int h = 0; h < GRP; ++h) {
     const float mu = mh[h] == -INFINITY ? 0.f : mh[h];
     float l = 0.f;
-    for (int i = tid; i < nk; i += DEC_NT) {
+    for (int i = tid; i < nloc; i += DEC_NT) {
       const float e = exp2f(sc[h][i] - mu);
       sc[h][i] = e;
       l += e;
@@ -461,32 +466,83 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
     lh[h] = l;
   }
 
-  // ---- o[h][d] = sum_u p[h][u] V^T[d][u]; thread = (d, key slice)
+  // ---- o[h][d] = sum_u p[h][u] V^T[d][u]. Thread (r = tid / 8, c = tid % 8)
+  // reads 8-key chunk c of every 64-key block for dims r, r + 32, ...: eight
+  // lanes cover 128 contiguous bytes of a V^T row.
   {
-    const int d = tid % DH;
-    const int half = tid / DH;
-    float acc[GRP];
+    constexpr int RPT = DH / 32;   // dims per thread
+    const int c = tid & 7, r = tid >> 3;
+    float acc[RPT][GRP];
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) acc[h] = 0.f;
-    const uint16_t* vrow = a.vc + (bg * DH + d) * a.c_rows;
-    for (int kk = half; kk < nk; kk += HALVES) {
-      const int64_t u = ka + kk;
-      const int64_t col = a.ring > 0 ? u % a.ring : u;
-      const float v = bf2f(vrow[col]);
+    for (int i = 0; i < RPT; ++i)
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) acc[h] += sc[h][kk] * v;
+      for (int h = 0; h < GRP; ++h) acc[i][h] = 0.f;
+    for (int j0 = c * 8; j0 < nloc; j0 += 64) {
+      const int64_t u0 = A + j0;
+      if (u0 + 7 < ua) continue;  // chunk wholly below the window
+      float pw[GRP][8];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        const float4 x = *reinterpret_cast<const float4*>(&sc[h][j0]);
+        const float4 y = *reinterpret_cast<const float4*>(&sc[h][j0 + 4]);
+        pw[h][0] = x.x; pw[h][1] = x.y; pw[h][2] = x.z; pw[h][3] = x.w;
+        pw[h][4] = y.x; pw[h][5] = y.y; pw[h][6] = y.z; pw[h][7] = y.w;
+      }
+      const bool whole = u0 >= ua && u0 + 7 < ub;
+      if (!whole) {
+        // score slots past the last key were never written this launch
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int64_t u = u0 + k;
+          if (u < ua || u >= ub) {
+#pragma unroll
+            for (int h = 0; h < GRP; ++h) pw[h][k] = 0.f;
+          }
+        }
+      }
+      const int64_t col = a.ring > 0 ? u0 % a.ring : u0;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int d = r + 32 * i;
+        const uint16_t* vrow = a.vc + (bg * DH + d) * a.c_rows;
+        float v[8];
+        if (whole) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(vrow + col);
+          const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = bf2f(e[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int64_t u = u0 + k;
+            v[k] = (u >= ua && u < ub) ? bf2f(vrow[a.ring > 0 ? u % a.ring : u]) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+          float s_ = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) s_ += pw[h][k] * v[k];
+          acc[i][h] += s_;
+        }
+      }
     }
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) ostage[half][h][d] = acc[h];
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        float x = acc[i][h];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        if (c == 0) ostage[h][r + 32 * i] = x;
+      }
   }
   __syncthreads();
   for (int i = tid; i < GRP * DH; i += DEC_NT) {
     const int h = i / DH, d = i % DH;
-    float v = 0.f;
-#pragma unroll
-    for (int j = 0; j < HALVES; ++j) v += ostage[j][h][d];
     float* dst = part + (((int64_t)b * a.n_q + g * GRP + h) * nsplit + split) * (DH + 2);
-    dst[2 + d] = v;
+    dst[2 + d] = ostage[h][d];
     if (d == 0) {
       dst[0] = mh[h];
       dst[1] = lh[h];
@@ -549,8 +605,9 @@ int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit) {
   return (int64_t)B * n_q * nsplit * (dh + 2);
 }
 
-int decode_attn_pick_split(int B, int n_kv, int64_t keys) {
-  int64_t s = (keys + DEC_MAXK - 1) / DEC_MAXK;
+int decode_attn_pick_split(int64_t lo, int64_t p) {
+  const int64_t base = lo / 64 * 64;
+  const int64_t s = (p + 1 - base + DEC_MAXK - 1) / DEC_MAXK;
   return (int)(s < 1 ? 1 : s);
 }
 

@@ -327,7 +327,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                           w.s_qk, c.qh(), kd, c.gate(), c.st));
     }
     const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
-    int nsd = decode_attn_pick_split(c.B, s.nkv, c.p0 - lo + 1);
+    int nsd = decode_attn_pick_split(lo, c.p0);
     if (nsd > kMaxDecodeSplits) return fail(DORY_ERR_UNSUPPORTED, "context too long for decode splits");
     PROF(c, DORY_K_ATTN);
     HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
