@@ -399,32 +399,45 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) qreg[h][j] = qs[h][sub * 8 + j];
   const float sl2 = a.scale * kLog2e;
-  for (int k0 = wave * KPW; k0 < nloc; k0 += (DEC_NT / 64) * KPW) {
-    const int kk = k0 + kl;
-    const int64_t u = A + kk;
-    const bool valid = kk < nloc && u >= ua;
-    float acc[GRP];
+  // four keys per lane group per iteration: their loads are issued together
+  constexpr int UNR = 4;
+  constexpr int KSTEP = (DEC_NT / 64) * KPW;
+  for (int k0 = wave * KPW; k0 < nloc; k0 += KSTEP * UNR) {
+    uint4 raw[UNR];
+    bool val[UNR];
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) acc[h] = 0.f;
-    if (valid) {
-      const int64_t row = a.ring > 0 ? u % a.ring : u;
-      const uint4 raw = *reinterpret_cast<const uint4*>(a.kc + (bg * a.c_rows + row) * DH + sub * 8);
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+    for (int x = 0; x < UNR; ++x) {
+      const int kk = k0 + kl + x * KSTEP;
+      const int64_t u = A + kk;
+      val[x] = kk < nloc && u >= ua;
+      raw[x] = make_uint4(0, 0, 0, 0);
+      if (val[x]) {
+        const int64_t row = a.ring > 0 ? u % a.ring : u;
+        raw[x] = *reinterpret_cast<const uint4*>(a.kc + (bg * a.c_rows + row) * DH + sub * 8);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < UNR; ++x) {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[x]);
+      float acc[GRP];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) acc[h] = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float kv = bf2f(e[j]);
 #pragma unroll
         for (int h = 0; h < GRP; ++h) acc[h] += qreg[h][j] * kv;
       }
-    }
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) {
+      for (int h = 0; h < GRP; ++h) {
 #pragma unroll
-      for (int o = LPK / 2; o > 0; o >>= 1) acc[h] += __shfl_xor(acc[h], o, 64);
-    }
-    if (sub == 0 && kk < nloc) {
+        for (int o = LPK / 2; o > 0; o >>= 1) acc[h] += __shfl_xor(acc[h], o, 64);
+      }
+      const int kk = k0 + kl + x * KSTEP;
+      if (sub == 0 && kk < nloc) {
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) sc[h][kk] = valid ? acc[h] * sl2 : -INFINITY;
+        for (int h = 0; h < GRP; ++h) sc[h][kk] = val[x] ? acc[h] * sl2 : -INFINITY;
+      }
     }
   }
   __syncthreads();
@@ -477,6 +490,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
     for (int i = 0; i < RPT; ++i)
 #pragma unroll
       for (int h = 0; h < GRP; ++h) acc[i][h] = 0.f;
+#pragma unroll 2
     for (int j0 = c * 8; j0 < nloc; j0 += 64) {
       const int64_t u0 = A + j0;
       if (u0 + 7 < ua) continue;  // chunk wholly below the window

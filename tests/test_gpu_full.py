@@ -73,3 +73,27 @@ def test_recurrent_pair_full_width(pair, k):
         c, m = per_token_check(st[i], o["states"][i], f"s_{i + 1}")
         log(f"  s_{i + 1}: min cos {c:.6f} max abs {m:.2e}")
     per_token_check(out["hidden"].cpu().numpy(), o["hidden"], "hidden")
+
+
+@pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
+def test_recurrent_pair_decode_full_width(pair, mode):
+    """Decode at full width after a 1100-token prefill: the sliding-window
+    ring has wrapped and the full-attention keys span several 128-key decode
+    blocks; k=2 under both cache policies."""
+    shape, W, gm, om = pair
+    log(f"pair decode {mode}")
+    B, k, T0, steps = 2, 2, 1100, 3
+    toks = synth.tokens(4, B, T0 + steps, shape.vocab)
+    kv = gm.kv_cache(mode, k, B, T0 + steps)
+    oc = ref.Cache(shape, mode, B)
+    gm.prefill(kv, torch.from_numpy(toks[:, :T0].copy()).cuda(), k, logits=False)
+    om.step(oc, toks[:, :T0], k, logits=None)
+    for t in range(T0, T0 + steps):
+        out = gm.decode_step(kv, torch.from_numpy(toks[:, t].copy()).cuda(), k, logits=False,
+                             next_token=False, hidden=True, states=True)
+        torch.cuda.synchronize()
+        o = om.step(oc, toks[:, t:t + 1], k, logits=None)
+        st = out["states"].cpu().numpy()
+        for i in range(k):
+            per_token_check(st[i].reshape(B, 1, -1), o["states"][i], f"decode {t} s_{i + 1}")
+        per_token_check(out["hidden"].cpu().numpy().reshape(B, 1, -1), o["hidden"], f"decode {t} hidden")
