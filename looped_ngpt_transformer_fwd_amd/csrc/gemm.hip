@@ -447,6 +447,102 @@ hipError_t launch_big(const GemmArgs& a, int epi, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel for M <= 64 (decode, the LM head of a prefill): the weight
+// stream dominates, so the goal is bytes in flight. 64 x 64 x 64 tiles, 4
+// waves of 32 x 32, two LDS stages filled by buffer DMA (the same XOR-
+// swizzled 128-byte rows as the large kernel), 32 KiB of LDS so that four
+// workgroups share a CU, and split-K for enough workgroups.
+template <int EPI>
+__global__ void __launch_bounds__(256)
+gemm_skinny_kernel(GemmArgs g) {
+  constexpr int SB = 64 * 128;  // one operand tile of one stage
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * 64;
+  const int ksteps = g.K / BK;
+  const int per = (ksteps + g.nsplit - 1) / g.nsplit;
+  const int ks0 = blockIdx.z * per;
+  const int ks1 = min(ksteps, ks0 + per);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)(g.N - 1) * g.ldb * 2 + g.K * 2));
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ lr;
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave + 4 * i) * 8 + lr;
+    aoff[i] = (uint32_t)((int64_t)min(r, g.M - 1) * g.lda * 2 + lc * 16);
+    boff[i] = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldb * 2 + lc * 16);
+  }
+  const int fr = lane & 31, fh = lane >> 5;
+  int loff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ (fr & 7)) << 4);
+
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+#define DORY_SISSUE(KS, SA, SB_)                                            \
+  do {                                                                      \
+    const uint32_t ko_ = (uint32_t)(KS) * (BK * 2);                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_) {                      \
+      dma16(ra, aoff[i_], ko_, (SA) + (wave + 4 * i_) * 1024);              \
+      dma16(rb, boff[i_], ko_, (SB_) + (wave + 4 * i_) * 1024);             \
+    }                                                                       \
+  } while (0)
+
+  if (ks0 < ks1) DORY_SISSUE(ks0, sA0, sB0);
+  for (int ks = ks0; ks < ks1; ++ks) {
+    wait_vm0();
+    __syncthreads();
+    const bool odd = (ks - ks0) & 1;
+    if (ks + 1 < ks1) {
+      if (odd) DORY_SISSUE(ks + 1, sA0, sB0);
+      else DORY_SISSUE(ks + 1, sA1, sB1);
+    }
+    const uint8_t* sa = (odd ? sA1 : sA0) + wm * 32 * 128;
+    const uint8_t* sb = (odd ? sB1 : sB0) + wn * 32 * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(sa + loff[kk]);
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(sb + loff[kk]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+    }
+  }
+#undef DORY_SISSUE
+
+  const int col = n0 + wn * 32 + (lane & 31);
+  if (col < g.N) {
+    const float sc = (EPI == EPI_LOGITS) ? g.s1[col] : 1.f;
+    float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
+    const int rbase = wm * 32 + (lane >> 5) * 4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = rbase + (e >> 2) * 8 + (e & 3);
+      if (row < g.M) C[(int64_t)row * g.ldc + col] = acc[e] * sc;
+    }
+  }
+}
+
+hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t st) {
+  dim3 grid((a.N + 63) / 64, 1, a.nsplit), block(256);
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL((gemm_skinny_kernel<EPI_F32>), grid, block, 0, st, a); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny_kernel<EPI_LOGITS>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmArgs& a, int epi, hipStream_t st) {
   constexpr int NT = 64 * (BM / WM) * (BN / WN);
@@ -467,8 +563,15 @@ constexpr int kLargeM = 1024;
 
 int gemm_pick_split(int M, int N, int K, int max_split) {
   if (M >= kLargeM) return 1;
-  const int tiles = ((M + 63) / 64) * ((N + 127) / 128);
   const int ksteps = K / BK;
+  if (M <= 64) {
+    // skinny path: aim for about four workgroups per CU, >= 2 K steps each
+    const int tiles = (N + 63) / 64;
+    int s = 1;
+    while (s * 2 <= max_split && tiles * s < 1024 && ksteps / (s * 2) >= 2) s *= 2;
+    return s;
+  }
+  const int tiles = ((M + 63) / 64) * ((N + 127) / 128);
   int s = 1;
   while (s * 2 <= max_split && tiles * s < 512 && ksteps / (s * 2) >= 4) s *= 2;
   return s;
@@ -479,6 +582,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (epi != EPI_F32 && a.nsplit != 1) return hipErrorInvalidValue;
   if (a.M >= kLargeM) return launch_big(a, epi, st);
   if (epi == EPI_QKV) return hipErrorInvalidValue;
+  if (a.M <= 64 && (epi == EPI_F32 || epi == EPI_LOGITS)) return launch_skinny(a, epi, st);
   return launch_cfg<64, 128, 32, 64>(a, epi, st);
 }
 

@@ -84,7 +84,8 @@ hipError_t launch_swiglu_partials(const float* p, int nsplit, int64_t split_stri
                                   const float* s_u, const float* s_v, uint16_t* a, hipStream_t st);
 
 // Query/key transform. P = [nsplit][M][d_q + 2 d_kv + d_q] projections
-// (rows m = b * C + t, position p0 + t). Writes
+// (rows m = b * C + t, position p0 + t); cs/sn: RoPE table of the layer's
+// base for the step's positions ([C][dh/2], see launch_rope_table). Writes
 //   q_hat [B][n_q][C][dh] bf16 = s_qk * N(RoPE(q))
 //   k_hat to kdst, v to vdst (see QkDest), sigma(g) [M][d_q] bf16.
 struct QkDest {
@@ -99,7 +100,7 @@ struct QkDest {
   int64_t ring;
 };
 hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
-                          int64_t p0, int n_q, int n_kv, int dh, double rope_base,
+                          int64_t p0, int n_q, int n_kv, int dh, const float* cs, const float* sn,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
                           hipStream_t st);
 

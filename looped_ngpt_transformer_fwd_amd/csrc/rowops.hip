@@ -45,11 +45,27 @@ update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss,
     const int c = threadIdx.x + i * NT_ROW;
     if (c < nv) {
       hv[i] = reinterpret_cast<const float4*>(h32 + (int64_t)m * d)[c];
-      float4 acc = reinterpret_cast<const float4*>(y + (int64_t)m * ldy)[c];
-      for (int s = 1; s < nsplit; ++s) {
-        const float4 t = reinterpret_cast<const float4*>(y + s * ss + (int64_t)m * ldy)[c];
-        acc.x += t.x; acc.y += t.y; acc.z += t.z; acc.w += t.w;
+      // split-K partials: four independent accumulators keep loads in flight
+      float4 a4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      int s = 0;
+      for (; s + 4 <= nsplit; s += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 t = reinterpret_cast<const float4*>(y + (s + j) * ss + (int64_t)m * ldy)[c];
+          a4[j].x += t.x; a4[j].y += t.y; a4[j].z += t.z; a4[j].w += t.w;
+        }
       }
+      for (; s < nsplit; ++s) {
+        const float4 t = reinterpret_cast<const float4*>(y + s * ss + (int64_t)m * ldy)[c];
+        a4[0].x += t.x; a4[0].y += t.y; a4[0].z += t.z; a4[0].w += t.w;
+      }
+      float4 acc;
+      acc.x = (a4[0].x + a4[1].x) + (a4[2].x + a4[3].x);
+      acc.y = (a4[0].y + a4[1].y) + (a4[2].y + a4[3].y);
+      acc.z = (a4[0].z + a4[1].z) + (a4[2].z + a4[3].z);
+      acc.w = (a4[0].w + a4[1].w) + (a4[2].w + a4[3].w);
       yv[i] = acc;
       syy += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
     }
@@ -160,12 +176,15 @@ __global__ void swiglu_partials_kernel(const float* p, int nsplit, int64_t ss, i
   a[idx] = f2bf(gt / (1.f + __expf(-gt)) * up);
 }
 
-// One block per token row. dh/2 threads per head (dh in {32, 64, 128}).
+// Grid (token rows, head groups + v/gate groups). Blocks y < n_groups rotate,
+// normalize and scale `heads_per_block` q/k heads (dh/2 threads per head, dh
+// in {32, 64, 128}); the remaining blocks write v (as V^T) and sigma(gate),
+// NT_ROW columns each. cos/sin of the row's angles come from the step's RoPE
+// table ([C][dh/2]).
 __global__ void __launch_bounds__(NT_ROW)
 qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq, int nkv,
-               int dh, double base, const float* s_qk, uint16_t* qh, QkDest kv,
-               uint16_t* gate) {
-  __shared__ float cs[128], sn[128];
+               int dh, const float* cs_tab, const float* sn_tab, const float* s_qk, uint16_t* qh,
+               QkDest kv, uint16_t* gate) {
   const int m = blockIdx.x;
   const int b = m / C, t = m - b * C;
   const int64_t pos = p0 + t;
@@ -173,51 +192,52 @@ qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq
   const int dq = nq * dh, dkv = nkv * dh;
   const int N = 2 * dq + 2 * dkv;
   const float* row = P + (int64_t)m * N;
-  for (int i = threadIdx.x; i < half; i += NT_ROW) {
-    const double invf = pow(base, -2.0 * (double)i / (double)dh);
-    double s, c;
-    sincos((double)pos * invf, &s, &c);
-    cs[i] = (float)c;
-    sn[i] = (float)s;
-  }
-  __syncthreads();
   int64_t krow = pos - kv.pos_origin;
   if (kv.ring > 0) krow %= kv.ring;
-  const int per_pass = NT_ROW / half;
-  const int i = threadIdx.x % half;
-  for (int hh = threadIdx.x / half; hh < nq + nkv; hh += per_pass) {
+  const int per_block = NT_ROW / half;
+  const int ngroups = (nq + nkv + per_block - 1) / per_block;
+  if ((int)blockIdx.y < ngroups) {
+    const int i = threadIdx.x % half;
+    const int hh = blockIdx.y * per_block + threadIdx.x / half;
+    if (hh >= nq + nkv) return;  // whole head groups exit together
+    const float c = cs_tab[(int64_t)t * half + i], sn = sn_tab[(int64_t)t * half + i];
     const int col = hh < nq ? hh * dh : dq + (hh - nq) * dh;
     float x1 = 0.f, x2 = 0.f;
     for (int s = 0; s < nsplit; ++s) {
       x1 += row[s * ss + col + i];
       x2 += row[s * ss + col + i + half];
     }
-    const float r1 = x1 * cs[i] - x2 * sn[i];
-    const float r2 = x2 * cs[i] + x1 * sn[i];
+    const float r1 = x1 * c - x2 * sn;
+    const float r2 = x2 * c + x1 * sn;
     float sq = r1 * r1 + r2 * r2;
     for (int o = half >> 1; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
     const float inv = 1.0f / sqrtf(sq);
-    const uint16_t o1 = f2bf(s_qk[i] * r1 * inv);
-    const uint16_t o2 = f2bf(s_qk[i + half] * r2 * inv);
     uint16_t* dst;
     if (hh < nq) {
       dst = qh + (((int64_t)b * nq + hh) * C + t) * dh;
     } else {
       dst = kv.kbase + (((int64_t)b * nkv + (hh - nq)) * kv.k_rows + krow) * dh;
     }
-    dst[i] = o1;
-    dst[i + half] = o2;
+    dst[i] = f2bf(s_qk[i] * r1 * inv);
+    dst[i + half] = f2bf(s_qk[i + half] * r2 * inv);
+    return;
   }
-  for (int idx = threadIdx.x; idx < dkv; idx += NT_ROW) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += row[s * ss + dq + dkv + idx];
+  // v and gate columns: NT_ROW consecutive columns per block
+  const int idx = ((int)blockIdx.y - ngroups) * NT_ROW + threadIdx.x;
+  if (idx >= dkv + dq) return;
+  float v0 = 0.f, v1 = 0.f;
+  int s = 0;
+  for (; s + 2 <= nsplit; s += 2) {
+    v0 += row[s * ss + dq + dkv + idx];
+    v1 += row[(s + 1) * ss + dq + dkv + idx];
+  }
+  if (s < nsplit) v0 += row[s * ss + dq + dkv + idx];
+  const float v = v0 + v1;
+  if (idx < dkv) {
     const int g = idx / dh, d = idx - g * dh;
     kv.vbase[(((int64_t)b * nkv + g) * dh + d) * kv.v_cols + krow] = f2bf(v);
-  }
-  for (int idx = threadIdx.x; idx < dq; idx += NT_ROW) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += row[s * ss + dq + 2 * dkv + idx];
-    gate[(int64_t)m * dq + idx] = f2bf(1.0f / (1.0f + __expf(-v)));
+  } else {
+    gate[(int64_t)m * dq + (idx - dkv)] = f2bf(1.0f / (1.0f + __expf(-v)));
   }
 }
 
@@ -343,12 +363,15 @@ hipError_t launch_swiglu_partials(const float* p, int nsplit, int64_t split_stri
 }
 
 hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
-                          int64_t p0, int n_q, int n_kv, int dh, double rope_base,
+                          int64_t p0, int n_q, int n_kv, int dh, const float* cs, const float* sn,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
                           hipStream_t st) {
   if (dh != 32 && dh != 64 && dh != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qk_prep_kernel, dim3(B * C), dim3(NT_ROW), 0, st, P, nsplit, split_stride, C,
-                     p0, n_q, n_kv, dh, rope_base, s_qk, q_hat, kv, gate);
+  const int per_block = NT_ROW / (dh / 2);
+  const int ngroups = (n_q + n_kv + per_block - 1) / per_block;
+  const int nvg = (n_kv * dh + n_q * dh + NT_ROW - 1) / NT_ROW;
+  hipLaunchKernelGGL(qk_prep_kernel, dim3(B * C, ngroups + nvg), dim3(NT_ROW), 0, st, P, nsplit,
+                     split_stride, C, p0, n_q, n_kv, dh, cs, sn, s_qk, q_hat, kv, gate);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 constexpr int kMaxDecodeSplits = 1024;
-constexpr int kMaxGemmSplit = 8;
+constexpr int kMaxGemmSplit = 16;
 constexpr int64_t kLargeM = 1024;  // GEMMs at or above this many rows run unsplit
 
 struct Shape {
@@ -285,7 +285,6 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
   const dory_sublayer_weights& w = c.m->sub[i];
   const int kind = c.m->kinds[i];
   const bool full = kind == DORY_LAYER_ATTN_FULL;
-  const double base = full ? s.base_full : s.base_swa;
   const SlotPtr sp = slot_ptr(c.kv, i, slot);
   int ns = 1;
   dory_status st = DORY_OK;
@@ -323,8 +322,9 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     QkDest kd{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring};
     {
       PROF(c, DORY_K_QK);
-      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh, base,
-                          w.s_qk, c.qh(), kd, c.gate(), c.st));
+      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh,
+                          c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
+                          c.gate(), c.st));
     }
     const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
     int nsd = decode_attn_pick_split(lo, c.p0);
@@ -338,8 +338,9 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     if (!c.fused_qkv()) {
       QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
       PROF(c, DORY_K_QK);
-      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh, base,
-                            w.s_qk, c.qh(), kd, c.gate(), c.st));
+      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh,
+                            c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
+                            c.gate(), c.st));
     }
     {
       // the attention reads whole 8-key V chunks: zero the columns past the
@@ -415,7 +416,8 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   const Shape& s = c.s;
   const int64_t Md = c.M * s.d;
   const bool per_loop = c.kv->mode == DORY_CACHE_PER_LOOP;
-  if (c.fused_qkv()) {
+  {
+    // cos / sin of the step's positions for both RoPE bases
     PROF(c, DORY_K_QK);
     HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_swa, c.rope_cs(0), c.rope_sn(0), c.st));
     HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_full, c.rope_cs(1), c.rope_sn(1), c.st));
