@@ -140,6 +140,21 @@ def tokens(seed: int, batch: int, length: int, vocab: int, name: str = "tokens")
     return g.integers(0, vocab, size=(batch, length), dtype=np.int64).astype(np.int32)
 
 
+def kv_context(seed: int, sublayer: int, slot: int, row: int, n_kv: int, n_pos: int,
+               dh: int):
+    """Synthetic cached keys and values of `n_pos` positions for one
+    (sublayer, cache slot, sequence), as bf16 bits [n_kv, n_pos, dh]: keys
+    N(0, 1/dh) per entry (rows of about unit length, the scale of normalized
+    keys), values N(0, 0.02^2) (the scale of a unit row projected on unit
+    rows at d = 2304)."""
+    g = np.random.default_rng([seed & 0xFFFFFFFF, sublayer, slot, row, 0x4B56])
+    k = g.standard_normal((n_kv, n_pos, dh), dtype=np.float32)
+    k *= np.float32(1.0 / np.sqrt(dh))
+    v = g.standard_normal((n_kv, n_pos, dh), dtype=np.float32)
+    v *= np.float32(0.02)
+    return bf16_bits_from_f32(k), bf16_bits_from_f32(v)
+
+
 def layer_kind_list(shape: Shape):
     """Kinds as data: the explicit tuple if given, else None (each side derives
     the default interleave itself)."""
