@@ -100,6 +100,42 @@ def class_work(shape, M):
     }
 
 
+# Source files whose kernels make up each timed class; a counter record is
+# valid only for the sources it was taken on.
+CLASS_SOURCES = {
+    "gemm_qkvg": ("gemm.hip", "common.h"), "gemm_o": ("gemm.hip", "common.h"),
+    "gemm_upgate": ("gemm.hip", "common.h"), "gemm_down": ("gemm.hip", "common.h"),
+    "update": ("rowops.hip", "common.h"), "attn": ("attention.hip", "common.h"),
+}
+
+
+def source_digest(cls):
+    import hashlib
+    h = hashlib.sha256()
+    for f in CLASS_SOURCES[cls]:
+        with open(os.path.join(ROOT, "looped_ngpt_transformer_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(cls):
+    """HBM bytes per launch of the class from the hardware counter record in
+    profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size), or None if none was taken on the current
+    kernel sources."""
+    import glob
+    import re
+    want = source_digest(cls)
+    pat = re.compile(r"traffic-record: class=(\S+) sources=(\S+) bytes_per_launch=(\S+)")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                m = pat.search(line)
+                if m and m.group(1) == cls and m.group(2) == want:
+                    return float(m.group(3))
+    return None
+
+
 def run_prefill(gm, kv, toks, k, ws):
     kv.reset()
     return gm.prefill(kv, toks, k, ws=ws, logits=True, next_token=True)
@@ -271,7 +307,8 @@ def main():
     peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS
     roofline = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": traffic_record(dom),
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "work_per_launch": amt, "work_unit": unit}
 
     result = {

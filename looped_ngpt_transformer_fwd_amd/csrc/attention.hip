@@ -40,12 +40,17 @@ __device__ __forceinline__ void wait_vm0_attn() { __builtin_amdgcn_s_waitcnt(0x0
 // tile's loads are in flight during the current tile's MFMAs). Both tiles are
 // stored XOR-swizzled by row so that the MFMA fragment reads of consecutive
 // rows hit distinct bank groups:
-//   K tile   [BN keys][DH]   row = DH*2 bytes, chunk c of row r stored at c ^ key(r)
+//   K tile   [BN keys][DH]   row = DH*2 bytes, chunk c of row r stored at c ^ kswz(r)
 //   V^T tile [DH][BN keys]   row = BN*2 = 128 bytes, chunk c of row d at c ^ (d & 7)
+// The LDS serves a 16-byte read for 16 lanes per cycle from 64 banks (256
+// bytes): the 16 key rows of one K fragment read must fall in 16 distinct
+// 16-byte bank groups, so rows at the same offset within 256 bytes get
+// distinct chunk XORs.
 template <int DH>
 __device__ __forceinline__ int kswz(int r) {
-  constexpr int KCH = DH / 8;
-  return r & ((KCH < 8 ? KCH : 8) - 1);
+  constexpr int KCH = DH / 8;         // 16-byte chunks per row
+  constexpr int RP = 256 / (DH * 2);  // rows per 256 bytes
+  return (r / RP) & (KCH - 1);
 }
 
 template <int DH, int GRP>

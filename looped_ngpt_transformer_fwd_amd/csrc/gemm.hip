@@ -188,9 +188,11 @@ gemm_nt_kernel(GemmArgs g) {
 // LDS stages filled by direct global->LDS DMA (global_load_lds_dwordx4), so
 // no VGPRs stage the operands. Each 1 KiB DMA block holds 8 rows x 128 B;
 // lane l of a block writes LDS bytes [16 l, 16 l + 16) and fetches logical
-// 16-byte chunk (l % 8) ^ (row % 8) of its row, i.e. the tile is stored
-// XOR-swizzled and fragment reads of 8 consecutive rows hit 8 distinct bank
-// groups. One barrier per K step: after it, the loads of step k+1 are issued
+// 16-byte chunk (l % 8) ^ ((row / 2) % 8) of its row, i.e. the tile is
+// stored XOR-swizzled. The LDS serves a 16-byte read for 16 lanes per cycle
+// from its 64 banks (256 B); fragment reads of 16 consecutive rows then hit
+// 16 distinct 16-byte bank groups (rows 2j and 2j + 1 differ by 128 B, rows
+// 2j and 2j + 2 in their chunk). One barrier per K step: after it, the loads of step k+1 are issued
 // into the other stage and stay in flight during the MFMAs of step k. The
 // loop has a single body (stage chosen at run time): a body unrolled per
 // stage with an exit between the copies doubles the live accumulators.
@@ -278,11 +280,11 @@ gemm_big_kernel(GemmArgs g) {
 
   // DMA sources: wave w fills blocks w, w+NW, w+2NW, ... of each operand tile
   const int lr = lane >> 3;                 // row within the block
-  const int lc = (lane & 7) ^ lr;           // logical chunk fetched by this lane
   uint32_t aoff[BPW], boff[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int r = (wave + NW * i) * 8 + lr;
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);  // logical chunk fetched by this lane
     aoff[i] = (uint32_t)((int64_t)min(m0 + r, g.M - 1) * g.lda * 2 + lc * 16);
     int v = min(n0 + r, g.N - 1);
     int row = v;
@@ -293,11 +295,12 @@ gemm_big_kernel(GemmArgs g) {
     boff[i] = (uint32_t)((int64_t)row * g.ldb * 2 + lc * 16);
   }
   // LDS lane offsets of the fragment reads for the 4 k-steps of 16; rows of
-  // every fragment are multiples of 32 apart, so row & 7 = lane & 7
+  // every fragment are multiples of 32 apart, so the swizzle of a lane's row
+  // depends on lane & 31 only
   const int fr = lane & 31, fh = lane >> 5;
   int loff[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ (fr & 7)) << 4);
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ ((fr >> 1) & 7)) << 4);
   const int a_wave = wm * BIG_WM * 128, b_wave = wn * BIG_WN * 128;
 
   floatx16 acc[FM][FN];
@@ -474,18 +477,18 @@ gemm_skinny_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)(g.N - 1) * g.ldb * 2 + g.K * 2));
   const int lr = lane >> 3;
-  const int lc = (lane & 7) ^ lr;
   uint32_t aoff[2], boff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = (wave + 4 * i) * 8 + lr;
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);
     aoff[i] = (uint32_t)((int64_t)min(r, g.M - 1) * g.lda * 2 + lc * 16);
     boff[i] = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldb * 2 + lc * 16);
   }
   const int fr = lane & 31, fh = lane >> 5;
   int loff[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ (fr & 7)) << 4);
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ ((fr >> 1) & 7)) << 4);
 
   floatx16 acc;
 #pragma unroll
