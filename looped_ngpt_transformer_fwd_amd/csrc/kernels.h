@@ -51,6 +51,7 @@ struct GemmArgs {
   const float* s1 = nullptr;
   const float* s2 = nullptr;
   int F = 0;
+  int order = 0;  // large-M tile order, set by the launcher
   QkvEpi qkv;
 };
 
