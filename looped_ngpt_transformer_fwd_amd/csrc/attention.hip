@@ -41,11 +41,13 @@ __device__ __forceinline__ void wait_vm0_attn() { __builtin_amdgcn_s_waitcnt(0x0
 // stored XOR-swizzled by row so that the MFMA fragment reads of consecutive
 // rows hit distinct bank groups:
 //   K tile   [BN keys][DH]   row = DH*2 bytes, chunk c of row r stored at c ^ kswz(r)
-//   V^T tile [DH][BN keys]   row = BN*2 = 128 bytes, chunk c of row d at c ^ (d & 7)
+//   V^T tile [DH][BN keys]   row = BN*2 = 128 bytes, chunk c of row d at c ^ ((d / 2) & 7)
 // The LDS serves a 16-byte read for 16 lanes per cycle from 64 banks (256
 // bytes): the 16 key rows of one K fragment read must fall in 16 distinct
 // 16-byte bank groups, so rows at the same offset within 256 bytes get
-// distinct chunk XORs.
+// distinct chunk XORs. The 8-byte V^T fragment reads conflict least with
+// the chunk XORed by (d / 2) & 7 (measured with the LDS conflict counters:
+// half the LDS cycles of the (d & 7) swizzle).
 template <int DH>
 __device__ __forceinline__ int kswz(int r) {
   constexpr int KCH = DH / 8;         // 16-byte chunks per row
@@ -154,7 +156,7 @@ attn_prefill_kernel(AttnArgs a) {
       for (int h = 0; h < 2; ++h) {
         const int d = lane & 31;
         const int c = kb * 4 + kc * 2 + h;
-        voff[kb][kc][h] = d * (BN * 2) + ((c ^ (d & 7)) << 4) + hl * 8;
+        voff[kb][kc][h] = d * (BN * 2) + ((c ^ ((d >> 1) & 7)) << 4) + hl * 8;
       }
 
   auto issue = [&](int64_t kt, uint8_t* kst, uint8_t* vst) {
@@ -180,7 +182,7 @@ attn_prefill_kernel(AttnArgs a) {
       const int blk = wave + j * PF_WAVES;
       if (V_BLOCKS % PF_WAVES != 0 && blk >= V_BLOCKS) break;
       const int d = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (d & 7);
+      const int c = (lane & 7) ^ ((d >> 1) & 7);
       // chunks at or past the last key load the row's first chunk instead:
       // finite values that meet probabilities of exactly 0 (the loads stay
       // unconditional so every wave issues a fixed number per tile)
