@@ -364,209 +364,195 @@ attn_prefill_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ decode
 constexpr int DEC_NT = 256;
-constexpr int DEC_MAXK = 512;  // keys per split, a multiple of 64
+constexpr int DEC_MAXK = 512;                      // keys per split, a multiple of 64
+constexpr int DEC_WKEYS = DEC_MAXK / (DEC_NT / 64);  // keys per wave
 
-// One workgroup per (split, KV head, sequence). The keys of the query at
-// position p are [lo, p] (lo = p - W + 1 for sliding-window layers); splits
-// are windows of DEC_MAXK keys aligned to 64-key blocks starting at
-// floor(lo / 64) * 64, so that V^T rows are read as aligned 16-byte chunks.
-// Keys outside [lo, p] inside a window get probability 0 and are never read
-// (cache rows past p may not be written yet).
+__device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
+  bf16x8 v;
+  if (ok) {
+    v = *reinterpret_cast<const bf16x8*>(p);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (__bf16)0.f;
+  }
+  return v;
+}
+
+// One workgroup per (split, KV head, sequence); the keys of the query at
+// position p are [lo, p] (lo = p - W + 1 for sliding-window layers), splits
+// are windows of DEC_MAXK keys aligned to 64 starting at floor(lo / 64) * 64,
+// and each wave takes DEC_WKEYS consecutive keys of its split in blocks of 32.
+// Both contractions run on v_mfma_f32_16x16x32_bf16 with the GRP query heads
+// of the KV group as the (zero-padded) 16-wide dimension:
+//   S^T block = K Q^T: A = 16 key rows (lane l: row l % 16, dims 8 (l / 16)
+//     .. + 7 of each 32-dim slice), B = Q^T (lane l: head l % 16). Tile t of
+//     a 32-key block puts key u0 + 8 (r / 4) + 4 t + r % 4 in row r, so the
+//     output lane (G = l / 16, head l % 16) holds the scores of keys
+//     u0 + 8 G + j, j = 0..7: exactly the A operand of the P V product.
+//   O += P V: A = P (lane: head l % 16, keys 8 (l / 16) .. + 7), B = V^T rows
+//     (lane: dim l % 16 of a 16-dim block, the same 8 keys, one 16-byte read).
+// Online softmax per wave in base 2; P is rounded to bf16 for the product.
+// Keys outside [lo, p] are never read (cache rows past p may not be written)
+// and enter as zero K/V rows with probability 0. The four waves merge their
+// (max, sum, o) in LDS into the split's partial.
 template <int DH, int GRP>
 __global__ void __launch_bounds__(DEC_NT)
 attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
-  __shared__ float qs[GRP][DH];
-  __shared__ float sc[GRP][DEC_MAXK];
-  __shared__ float red[GRP][DEC_NT / 64];
-  __shared__ float ostage[GRP][DH];
+  constexpr int NS = DH / 32;   // 32-dim slices of the q.k contraction
+  constexpr int NB = DH / 16;   // 16-dim blocks of the output
+  static_assert(GRP <= 16, "query heads per KV head must fit the 16-wide MFMA side");
+  __shared__ float wmax[DEC_NT / 64][GRP];
+  __shared__ float wsum[DEC_NT / 64][GRP];
+  __shared__ float wout[DEC_NT / 64][GRP][DH];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = lane >> 4, r = lane & 15;
   const int64_t bg = (int64_t)b * a.n_kv + g;
-  const int64_t p = a.p0;  // query position; cache rows hold keys 0..p
+  const int64_t p = a.p0;
   int64_t lo = 0;
   if (a.window > 0) lo = max((int64_t)0, p - a.window + 1);
   const int64_t A = (lo / 64) * 64 + (int64_t)split * DEC_MAXK;
   const int64_t ua = max(lo, A), ub = min(p + 1, A + DEC_MAXK);
-  const int nloc = (int)max((int64_t)0, ub - A);  // local keys [0, nloc) examined
+  const int64_t w0 = A + (int64_t)wave * DEC_WKEYS;
 
-  for (int i = tid; i < GRP * DH; i += DEC_NT) {
-    const int h = i / DH, d = i % DH;
-    qs[h][d] = bf2f(a.q[((int64_t)b * a.n_q + g * GRP + h) * DH + d]);
-  }
-  __syncthreads();
-
-  // ---- scores: DH/8 lanes per 2*DH-byte key row (8 dims each)
-  constexpr int LPK = DH / 8;
-  constexpr int KPW = 64 / LPK;
-  const int sub = lane % LPK, kl = lane / LPK;
-  float qreg[GRP][8];
+  bf16x8 qb[NS];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h)
+  for (int s = 0; s < NS; ++s)
+    qb[s] = load16_or_zero(a.q + ((int64_t)b * a.n_q + g * GRP + (r < GRP ? r : 0)) * DH + 32 * s + 8 * G,
+                           r < GRP);
+  floatx4 o[NB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qreg[h][j] = qs[h][sub * 8 + j];
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[nb][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-  // four keys per lane group per iteration: their loads are issued together
-  constexpr int UNR = 4;
-  constexpr int KSTEP = (DEC_NT / 64) * KPW;
-  for (int k0 = wave * KPW; k0 < nloc; k0 += KSTEP * UNR) {
-    uint4 raw[UNR];
-    bool val[UNR];
+  // buffer resources over this (sequence, KV head)'s K rows and V^T rows:
+  // 32-bit offsets, and an offset past the end reads zeros
+  const uint32_t kbytes = (uint32_t)(a.c_rows * DH * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.kc + bg * a.c_rows * DH), (short)0, (int)kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.vc + bg * DH * a.c_rows), (short)0, (int)kbytes, 0x00020000);
+  const uint32_t OOB = 0xFFFFFFF0u;
+
+  for (int blk = 0; blk < DEC_WKEYS / 32; ++blk) {
+    const int64_t u0 = w0 + 32 * blk;
+    if (u0 + 31 < ua || u0 >= ub) continue;  // the whole block is outside [lo, p]
+    bf16x8 kf[2][NS];
 #pragma unroll
-    for (int x = 0; x < UNR; ++x) {
-      const int kk = k0 + kl + x * KSTEP;
-      const int64_t u = A + kk;
-      val[x] = kk < nloc && u >= ua;
-      raw[x] = make_uint4(0, 0, 0, 0);
-      if (val[x]) {
-        const int64_t row = a.ring > 0 ? u % a.ring : u;
-        raw[x] = *reinterpret_cast<const uint4*>(a.kc + (bg * a.c_rows + row) * DH + sub * 8);
+    for (int t = 0; t < 2; ++t) {
+      const int64_t u = u0 + 8 * (r >> 2) + 4 * t + (r & 3);
+      const int64_t row = a.ring > 0 ? u % a.ring : u;
+      const uint32_t off = (u >= ua && u < ub) ? (uint32_t)(row * DH + 8 * G) * 2u : OOB;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 64 * s, 0);
+        kf[t][s] = __builtin_bit_cast(bf16x8, v);
       }
     }
+    // V^T chunks of 8 keys are aligned to 8 and lie inside the slot whenever
+    // their first key is a cached position; keys outside [lo, p] are zeroed
+    const int64_t uv = u0 + 8 * G;
+    const bool vany = uv + 7 >= ua && uv < ub;
+    const uint32_t voff = vany ? (uint32_t)((a.ring > 0 ? uv % a.ring : uv) * 2 + r * a.c_rows * 2) : OOB;
+    bf16x8 vf[NB];
 #pragma unroll
-    for (int x = 0; x < UNR; ++x) {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw[x]);
-      float acc[GRP];
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) acc[h] = 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, (int)(16 * nb * a.c_rows * 2), 0);
+      vf[nb] = __builtin_bit_cast(bf16x8, v);
+    }
+    if (!(uv >= ua && uv + 7 < ub)) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float kv = bf2f(e[j]);
+        const int64_t u = uv + j;
+        if (u < ua || u >= ub) {
 #pragma unroll
-        for (int h = 0; h < GRP; ++h) acc[h] += qreg[h][j] * kv;
-      }
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-#pragma unroll
-        for (int o = LPK / 2; o > 0; o >>= 1) acc[h] += __shfl_xor(acc[h], o, 64);
-      }
-      const int kk = k0 + kl + x * KSTEP;
-      if (sub == 0 && kk < nloc) {
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) sc[h][kk] = val[x] ? acc[h] * sl2 : -INFINITY;
+          for (int nb = 0; nb < NB; ++nb) vf[nb][j] = (__bf16)0.f;
+        }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- softmax pieces per head (base-2 domain)
-  float mh[GRP], lh[GRP];
+    floatx4 sacc[2];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    float m = -INFINITY;
-    for (int i = tid; i < nloc; i += DEC_NT) m = fmaxf(m, sc[h][i]);
-    m = wave_max(m);
-    if (lane == 0) red[h][wave] = m;
-  }
-  __syncthreads();
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    float m = red[h][0];
-    for (int w = 1; w < DEC_NT / 64; ++w) m = fmaxf(m, red[h][w]);
-    mh[h] = m;
-  }
-  __syncthreads();
+      for (int e = 0; e < 4; ++e) sacc[t][e] = 0.f;
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const float mu = mh[h] == -INFINITY ? 0.f : mh[h];
-    float l = 0.f;
-    for (int i = tid; i < nloc; i += DEC_NT) {
-      const float e = exp2f(sc[h][i] - mu);
-      sc[h][i] = e;
-      l += e;
+      for (int s = 0; s < NS; ++s)
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], qb[s], sacc[t], 0, 0, 0);
     }
-    l = wave_sum(l);
-    if (lane == 0) red[h][wave] = l;
-  }
-  __syncthreads();
+    float sv[8];
+    float mb = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    float l = 0.f;
-    for (int w = 0; w < DEC_NT / 64; ++w) l += red[h][w];
-    lh[h] = l;
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t u = uv + 4 * t + e;
+        const float x = (u >= ua && u < ub) ? sacc[t][e] * sl2 : -INFINITY;
+        sv[4 * t + e] = x;
+        mb = fmaxf(mb, x);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float m_new = fmaxf(m_run, mb);      // finite: the block holds a key
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    bf16x8 pf;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(sv[j] - m_new);
+      ps += pj;
+      pf[j] = (__bf16)pj;
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // o rows are heads 4 (l / 16) + e; their rescale factors sit in lanes 0..15
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ae = __shfl(alpha, 4 * G + e, 64);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb][e] *= ae;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf[nb], o[nb], 0, 0, 0);
   }
 
-  // ---- o[h][d] = sum_u p[h][u] V^T[d][u]. Thread (r = tid / 8, c = tid % 8)
-  // reads 8-key chunk c of every 64-key block for dims r, r + 32, ...: eight
-  // lanes cover 128 contiguous bytes of a V^T row.
-  {
-    constexpr int RPT = DH / 32;   // dims per thread
-    const int c = tid & 7, r = tid >> 3;
-    float acc[RPT][GRP];
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (G == 0 && r < GRP) {
+    wmax[wave][r] = m_run;
+    wsum[wave][r] = l_run;
+  }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
+  for (int e = 0; e < 4; ++e) {
+    const int h = 4 * G + e;
+    if (h < GRP) {
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) acc[i][h] = 0.f;
-#pragma unroll 2
-    for (int j0 = c * 8; j0 < nloc; j0 += 64) {
-      const int64_t u0 = A + j0;
-      if (u0 + 7 < ua) continue;  // chunk wholly below the window
-      float pw[GRP][8];
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        const float4 x = *reinterpret_cast<const float4*>(&sc[h][j0]);
-        const float4 y = *reinterpret_cast<const float4*>(&sc[h][j0 + 4]);
-        pw[h][0] = x.x; pw[h][1] = x.y; pw[h][2] = x.z; pw[h][3] = x.w;
-        pw[h][4] = y.x; pw[h][5] = y.y; pw[h][6] = y.z; pw[h][7] = y.w;
-      }
-      const bool whole = u0 >= ua && u0 + 7 < ub;
-      if (!whole) {
-        // score slots past the last key were never written this launch
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int64_t u = u0 + k;
-          if (u < ua || u >= ub) {
-#pragma unroll
-            for (int h = 0; h < GRP; ++h) pw[h][k] = 0.f;
-          }
-        }
-      }
-      const int64_t col = a.ring > 0 ? u0 % a.ring : u0;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int d = r + 32 * i;
-        const uint16_t* vrow = a.vc + (bg * DH + d) * a.c_rows;
-        float v[8];
-        if (whole) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(vrow + col);
-          const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = bf2f(e[k]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int64_t u = u0 + k;
-            v[k] = (u >= ua && u < ub) ? bf2f(vrow[a.ring > 0 ? u % a.ring : u]) : 0.f;
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          float s_ = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) s_ += pw[h][k] * v[k];
-          acc[i][h] += s_;
-        }
-      }
+      for (int nb = 0; nb < NB; ++nb) wout[wave][h][16 * nb + r] = o[nb][e];
     }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        float x = acc[i][h];
-        x += __shfl_xor(x, 1, 64);
-        x += __shfl_xor(x, 2, 64);
-        x += __shfl_xor(x, 4, 64);
-        if (c == 0) ostage[h][r + 32 * i] = x;
-      }
   }
   __syncthreads();
   for (int i = tid; i < GRP * DH; i += DEC_NT) {
     const int h = i / DH, d = i % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < DEC_NT / 64; ++w) M = fmaxf(M, wmax[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < DEC_NT / 64; ++w) {
+        const float f = __builtin_amdgcn_exp2f(wmax[w][h] - M);
+        L += wsum[w][h] * f;
+        O += wout[w][h][d] * f;
+      }
+    }
     float* dst = part + (((int64_t)b * a.n_q + g * GRP + h) * nsplit + split) * (DH + 2);
-    dst[2 + d] = ostage[h][d];
+    dst[2 + d] = O;
     if (d == 0) {
-      dst[0] = mh[h];
-      dst[1] = lh[h];
+      dst[0] = M;
+      dst[1] = L;
     }
   }
 }
