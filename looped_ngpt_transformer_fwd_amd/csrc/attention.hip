@@ -437,10 +437,9 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
       const_cast<uint16_t*>(a.vc + bg * DH * a.c_rows), (short)0, (int)kbytes, 0x00020000);
   const uint32_t OOB = 0xFFFFFFF0u;
 
-  for (int blk = 0; blk < DEC_WKEYS / 32; ++blk) {
+  // loads of block blk into (kf, vf): keys outside [lo, p] read as zeros
+  auto load = [&](int blk, bf16x8 (&kf)[2][NS], bf16x8 (&vf)[NB]) {
     const int64_t u0 = w0 + 32 * blk;
-    if (u0 + 31 < ua || u0 >= ub) continue;  // the whole block is outside [lo, p]
-    bf16x8 kf[2][NS];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int64_t u = u0 + 8 * (r >> 2) + 4 * t + (r & 3);
@@ -453,17 +452,22 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
       }
     }
     // V^T chunks of 8 keys are aligned to 8 and lie inside the slot whenever
-    // their first key is a cached position; keys outside [lo, p] are zeroed
+    // their first key is a cached position
     const int64_t uv = u0 + 8 * G;
     const bool vany = uv + 7 >= ua && uv < ub;
     const uint32_t voff = vany ? (uint32_t)((a.ring > 0 ? uv % a.ring : uv) * 2 + r * a.c_rows * 2) : OOB;
-    bf16x8 vf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       auto v = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, (int)(16 * nb * a.c_rows * 2), 0);
       vf[nb] = __builtin_bit_cast(bf16x8, v);
     }
+  };
+  auto compute = [&](int blk, const bf16x8 (&kf)[2][NS], bf16x8 (&vf)[NB]) {
+    const int64_t u0 = w0 + 32 * blk;
+    if (u0 + 31 < ua || u0 >= ub) return;  // the whole block is outside [lo, p]
+    const int64_t uv = u0 + 8 * G;
     if (!(uv >= ua && uv + 7 < ub)) {
+      // keys outside [lo, p] in this lane's V chunk are zeroed
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t u = uv + j;
@@ -517,7 +521,20 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf[nb], o[nb], 0, 0, 0);
-  }
+  };
+
+  // two register sets: the loads of block blk + 1 are in flight while block
+  // blk computes
+  static_assert(DEC_WKEYS / 32 == 4, "the pipeline below is written for 4 blocks per wave");
+  bf16x8 kfa[2][NS], vfa[NB], kfb[2][NS], vfb[NB];
+  load(0, kfa, vfa);
+  load(1, kfb, vfb);
+  compute(0, kfa, vfa);
+  load(2, kfa, vfa);
+  compute(1, kfb, vfb);
+  load(3, kfb, vfb);
+  compute(2, kfa, vfa);
+  compute(3, kfb, vfb);
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
