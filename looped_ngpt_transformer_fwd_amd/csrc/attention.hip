@@ -574,21 +574,48 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   }
 }
 
-// grid B * n_q, block DH
-__global__ void attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh,
-                                           const uint16_t* gate, uint16_t* z) {
+// grid B * n_q, block DH. The split maxima go through LDS once; the weighted
+// sums keep eight splits' loads in flight per thread.
+__global__ void __launch_bounds__(128)
+attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const uint16_t* gate,
+                           uint16_t* z) {
+  __shared__ float wsc[1024];  // 2^(m_s - M) per split (nsplit <= 1024)
+  __shared__ float pm[128];    // per-thread partial maxima (blockDim = dh <= 128)
   const int bh = blockIdx.x, d = threadIdx.x;
   const int b = bh / n_q, h = bh % n_q;
-  const float* pp = part + (int64_t)bh * nsplit * (dh + 2);
+  const int64_t stride = dh + 2;
+  const float* pp = part + (int64_t)bh * nsplit * stride;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (dh + 2)]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float m = pp[s * (dh + 2)];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += pp[s * (dh + 2) + 1] * w;
-    acc += pp[s * (dh + 2) + 2 + d] * w;
+  for (int s = d; s < nsplit; s += blockDim.x) M = fmaxf(M, pp[s * stride]);
+  pm[d] = M;
+  __syncthreads();
+  M = -INFINITY;
+  for (int t = 0; t < (int)blockDim.x; ++t) M = fmaxf(M, pm[t]);
+  float L = 0.f;
+  for (int s = d; s < nsplit; s += blockDim.x) {
+    const float m = pp[s * stride];
+    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+    wsc[s] = w;
+  }
+  __syncthreads();
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    float o[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      o[j] = pp[(s + j) * stride + 2 + d];
+      l[j] = pp[(s + j) * stride + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc += o[j] * wsc[s + j];
+      L += l[j] * wsc[s + j];
+    }
+  }
+  for (; s < nsplit; ++s) {
+    acc += pp[s * stride + 2 + d] * wsc[s];
+    L += pp[s * stride + 1] * wsc[s];
   }
   const int64_t idx = (int64_t)b * n_q * dh + h * dh + d;
   z[idx] = f2bf(acc / L * bf2f(gate[idx]));
