@@ -364,8 +364,8 @@ attn_prefill_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ decode
 constexpr int DEC_NT = 256;
-constexpr int DEC_MAXK = 512;                      // keys per split, a multiple of 64
-constexpr int DEC_WKEYS = DEC_MAXK / (DEC_NT / 64);  // keys per wave
+constexpr int DEC_MAXK = 512;   // keys per split of full-attention layers, a multiple of 64
+constexpr int DEC_SWAK = 256;   // keys per split of sliding-window layers (more workgroups)
 
 __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
   bf16x8 v;
@@ -380,8 +380,9 @@ __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
 
 // One workgroup per (split, KV head, sequence); the keys of the query at
 // position p are [lo, p] (lo = p - W + 1 for sliding-window layers), splits
-// are windows of DEC_MAXK keys aligned to 64 starting at floor(lo / 64) * 64,
-// and each wave takes DEC_WKEYS consecutive keys of its split in blocks of 32.
+// are windows of SPLITK keys (DEC_MAXK for full attention, DEC_SWAK for the
+// short sliding-window ranges) aligned to 64 starting at floor(lo / 64) * 64,
+// and each wave takes SPLITK / 4 consecutive keys of its split in blocks of 32.
 // Both contractions run on v_mfma_f32_16x16x32_bf16 with the GRP query heads
 // of the KV group as the (zero-padded) 16-wide dimension:
 //   S^T block = K Q^T: A = 16 key rows (lane l: row l % 16, dims 8 (l / 16)
@@ -395,9 +396,10 @@ __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
 // Keys outside [lo, p] are never read (cache rows past p may not be written)
 // and enter as zero K/V rows with probability 0. The four waves merge their
 // (max, sum, o) in LDS into the split's partial.
-template <int DH, int GRP>
+template <int DH, int GRP, int SPLITK>
 __global__ void __launch_bounds__(DEC_NT)
 attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
+  constexpr int DEC_WKEYS = SPLITK / (DEC_NT / 64);  // keys per wave
   constexpr int NS = DH / 32;   // 32-dim slices of the q.k contraction
   constexpr int NB = DH / 16;   // 16-dim blocks of the output
   static_assert(GRP <= 16, "query heads per KV head must fit the 16-wide MFMA side");
@@ -412,8 +414,8 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   const int64_t p = a.p0;
   int64_t lo = 0;
   if (a.window > 0) lo = max((int64_t)0, p - a.window + 1);
-  const int64_t A = (lo / 64) * 64 + (int64_t)split * DEC_MAXK;
-  const int64_t ua = max(lo, A), ub = min(p + 1, A + DEC_MAXK);
+  const int64_t A = (lo / 64) * 64 + (int64_t)split * SPLITK;
+  const int64_t ua = max(lo, A), ub = min(p + 1, A + SPLITK);
   const int64_t w0 = A + (int64_t)wave * DEC_WKEYS;
 
   bf16x8 qb[NS];
@@ -525,16 +527,18 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 
   // two register sets: the loads of block blk + 1 are in flight while block
   // blk computes
-  static_assert(DEC_WKEYS / 32 == 4, "the pipeline below is written for 4 blocks per wave");
+  constexpr int NBLK = DEC_WKEYS / 32;
+  static_assert(NBLK % 2 == 0, "blocks per wave come in pairs");
   bf16x8 kfa[2][NS], vfa[NB], kfb[2][NS], vfb[NB];
   load(0, kfa, vfa);
   load(1, kfb, vfb);
-  compute(0, kfa, vfa);
-  load(2, kfa, vfa);
-  compute(1, kfb, vfb);
-  load(3, kfb, vfb);
-  compute(2, kfa, vfa);
-  compute(3, kfb, vfb);
+#pragma unroll
+  for (int blk = 0; blk < NBLK; blk += 2) {
+    compute(blk, kfa, vfa);
+    if (blk + 2 < NBLK) load(blk + 2, kfa, vfa);
+    compute(blk + 1, kfb, vfb);
+    if (blk + 3 < NBLK) load(blk + 3, kfb, vfb);
+  }
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -632,7 +636,10 @@ hipError_t prefill_cfg(const AttnArgs& a, hipStream_t st) {
 template <int DH, int GRP>
 hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st) {
   dim3 grid(nsplit, a.n_kv, a.B);
-  hipLaunchKernelGGL((attn_decode_kernel<DH, GRP>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
+  if (a.window > 0)
+    hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_SWAK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_MAXK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q), dim3(DH), 0, st, part, nsplit,
@@ -656,9 +663,10 @@ int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit) {
   return (int64_t)B * n_q * nsplit * (dh + 2);
 }
 
-int decode_attn_pick_split(int64_t lo, int64_t p) {
+int decode_attn_pick_split(int64_t lo, int64_t p, bool window) {
   const int64_t base = lo / 64 * 64;
-  const int64_t s = (p + 1 - base + DEC_MAXK - 1) / DEC_MAXK;
+  const int64_t sk = window ? DEC_SWAK : DEC_MAXK;
+  const int64_t s = (p + 1 - base + sk - 1) / sk;
   return (int)(s < 1 ? 1 : s);
 }
 

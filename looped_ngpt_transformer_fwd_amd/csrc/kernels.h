@@ -159,8 +159,9 @@ hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 // Decode attention over cache rows only (current token already stored);
 // split over keys with `part` scratch of decode_attn_part_floats() floats.
 int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit);
-// Splits for a decode query at position p whose keys are [lo, p].
-int decode_attn_pick_split(int64_t lo, int64_t p);
+// Splits for a decode query at position p whose keys are [lo, p]; window:
+// a sliding-window layer (shorter splits).
+int decode_attn_pick_split(int64_t lo, int64_t p, bool window);
 hipError_t launch_attn_decode(const AttnArgs& a, int nsplit, float* part, hipStream_t st);
 
 }  // namespace dory

@@ -327,7 +327,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                           c.gate(), c.st));
     }
     const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
-    const int nsd = decode_attn_pick_split(lo, c.p0);  // <= kMaxDecodeSplits (checked up front)
+    const int nsd = decode_attn_pick_split(lo, c.p0, !full);  // <= kMaxDecodeSplits (checked up front)
     PROF(c, DORY_K_ATTN);
     HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
   } else {
@@ -498,8 +498,12 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
   if (B > kv->batch) return fail(DORY_ERR_CAPACITY, "B exceeds the bound batch");
   if (B < kv->batch) return fail(DORY_ERR_ARG, "B must equal the bound batch");
   if (kv->len + T > kv->max_seq) return fail(DORY_ERR_CAPACITY, "cache capacity exceeded");
-  if (T == 1 && decode_attn_pick_split(0, kv->len) > kMaxDecodeSplits)
-    return fail(DORY_ERR_UNSUPPORTED, "context too long for decode attention splits");
+  if (T == 1) {
+    const int64_t lo_w = std::max<int64_t>(0, kv->len - m->s.W + 1);
+    if (decode_attn_pick_split(0, kv->len, false) > kMaxDecodeSplits ||
+        decode_attn_pick_split(lo_w, kv->len, true) > kMaxDecodeSplits)
+      return fail(DORY_ERR_UNSUPPORTED, "context too long for decode attention splits");
+  }
   if (!ws) return fail(DORY_ERR_ARG, "workspace is NULL");
   const Shape& s = m->s;
   WsLayout L = plan_ws(s, B, T);
