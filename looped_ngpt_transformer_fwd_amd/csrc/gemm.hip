@@ -582,10 +582,14 @@ hipError_t launch_big(const GemmArgs& a0, int epi, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Skinny kernel for M <= 64 (decode, the LM head of a prefill): the weight
-// stream dominates, so the goal is bytes in flight. 64 x 64 x 64 tiles, 4
-// waves of 32 x 32, two LDS stages filled by buffer DMA (the same XOR-
-// swizzled 128-byte rows as the large kernel), 32 KiB of LDS so that four
-// workgroups share a CU, and split-K for enough workgroups.
+// stream dominates, so the goal is bytes in flight. A ring of four LDS
+// stages (one K step of 64 each, the same XOR-swizzled 128-byte rows as the
+// large kernel) filled by DMA three steps ahead; every step issues exactly
+// four DMA per wave (the last steps reload the final step into a stage no
+// one reads again), so the wait before each step is vmcnt(8).
+// 64 x 64 output tiles, 4 waves of 32 x 32, split-K over blockIdx.z.
+constexpr int SK_MAX = 4;
+
 template <int EPI>
 __global__ void __launch_bounds__(256)
 gemm_skinny_kernel(GemmArgs g) {
@@ -594,6 +598,10 @@ gemm_skinny_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA3[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB3[SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -602,7 +610,7 @@ gemm_skinny_kernel(GemmArgs g) {
   const int ksteps = g.K / BK;
   const int per = (ksteps + g.nsplit - 1) / g.nsplit;
   const int ks0 = blockIdx.z * per;
-  const int ks1 = min(ksteps, ks0 + per);
+  const int n = max(0, min(ksteps, ks0 + per) - ks0);
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)(g.N - 1) * g.ldb * 2 + g.K * 2));
@@ -624,34 +632,45 @@ gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 
-#define DORY_SISSUE(KS, SA, SB_)                                            \
-  do {                                                                      \
-    const uint32_t ko_ = (uint32_t)(KS) * (BK * 2);                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_) {                      \
-      dma16(ra, aoff[i_], ko_, (SA) + (wave + 4 * i_) * 1024);              \
-      dma16(rb, boff[i_], ko_, (SB_) + (wave + 4 * i_) * 1024);             \
-    }                                                                       \
-  } while (0)
-
-  if (ks0 < ks1) DORY_SISSUE(ks0, sA0, sB0);
-  for (int ks = ks0; ks < ks1; ++ks) {
-    wait_vm0();
-    __syncthreads();
-    const bool odd = (ks - ks0) & 1;
-    if (ks + 1 < ks1) {
-      if (odd) DORY_SISSUE(ks + 1, sA0, sB0);
-      else DORY_SISSUE(ks + 1, sA1, sB1);
+  // 4 DMA instructions per wave per step
+  auto issue = [&](int ks, uint8_t* sa, uint8_t* sb) {
+    const uint32_t ko = (uint32_t)ks * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      dma16(ra, aoff[i], ko, sa + (wave + 4 * i) * 1024);
+      dma16(rb, boff[i], ko, sb + (wave + 4 * i) * 1024);
     }
-    const uint8_t* sa = (odd ? sA1 : sA0) + wm * 32 * 128;
-    const uint8_t* sb = (odd ? sB1 : sB0) + wn * 32 * 128;
+  };
+  auto compute = [&](const uint8_t* sa0, const uint8_t* sb0) {
+    const uint8_t* sa = sa0 + wm * 32 * 128;
+    const uint8_t* sb = sb0 + wn * 32 * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(sa + loff[kk]);
       const bf16x8 bf = *reinterpret_cast<const bf16x8*>(sb + loff[kk]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
     }
+  };
+  if (n > 0) {
+    issue(ks0, sA0, sB0);
+    issue(ks0 + min(1, n - 1), sA1, sB1);
+    issue(ks0 + min(2, n - 1), sA2, sB2);
+    // the ring runs a multiple of 4 steps; steps past n only keep the wait
+    // and load pattern uniform (no branch around the DMA) and compute nothing
+    auto step = [&](int i, const uint8_t* ca, const uint8_t* cb, uint8_t* na, uint8_t* nb) {
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): steps i + 1, i + 2 stay in flight
+      barrier_lds();                        // all parts of step i landed; stage (i + 3) % 4 is free
+      issue(ks0 + min(i + 3, n - 1), na, nb);
+      if (i < n) compute(ca, cb);
+    };
+    for (int i = 0; i < n; i += 4) {
+      step(i, sA0, sB0, sA3, sB3);
+      step(i + 1, sA1, sB1, sA0, sB0);
+      step(i + 2, sA2, sB2, sA1, sB1);
+      step(i + 3, sA3, sB3, sA2, sB2);
+    }
+    wait_vm0();  // no DMA may outlive the workgroup's LDS
   }
-#undef DORY_SISSUE
 
   const int col = n0 + wn * 32 + (lane & 31);
   if (col < g.N) {
@@ -698,10 +717,11 @@ int gemm_pick_split(int M, int N, int K, int max_split) {
   if (M >= kLargeM) return 1;
   const int ksteps = K / BK;
   if (M <= 64) {
-    // skinny path: aim for about four workgroups per CU, >= 2 K steps each
+    // skinny path: the most workgroups that fit one round (2 per CU, 512),
+    // at least SK_MAX K steps each, within max_split
     const int tiles = (N + 63) / 64;
     int s = 1;
-    while (s * 2 <= max_split && tiles * s < 1024 && ksteps / (s * 2) >= 2) s *= 2;
+    while (s < max_split && tiles * (s + 1) <= 512 && ksteps / (s + 1) >= SK_MAX) ++s;
     return s;
   }
   const int tiles = ((M + 63) / 64) * ((N + 127) / 128);

@@ -34,8 +34,14 @@ int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 constexpr int kMaxDecodeSplits = 1024;
-constexpr int kMaxGemmSplit = 16;
+constexpr int kMaxGemmSplit = 16;   // split-K partials for 64 < M < kLargeM
+constexpr int kMaxSkinnySplit = 32; // and for M <= 64 (weight-streaming path)
+
 constexpr int64_t kLargeM = 1024;  // GEMMs at or above this many rows run unsplit
+// Split-K bound of a projection with M token rows (1: no split).
+int max_split_for(int64_t M) {
+  return M <= 64 ? kMaxSkinnySplit : (M < kLargeM ? kMaxGemmSplit : 1);
+}
 
 struct Shape {
   int d, nq, nkv, dh, F, V, nin, nrec, nout, W, full_every, lm;
@@ -127,11 +133,8 @@ WsLayout plan_ws(const Shape& s, int B, int T) {
   L.z = take(M * s.dq() * 2);
   L.a = take(M * s.F * 2);
   int64_t ncols = std::max<int64_t>(s.nqkvg(), s.d);
-  int64_t nsplit = 1;
-  if (M < kLargeM) {
-    ncols = std::max<int64_t>(ncols, 2 * (int64_t)s.F);
-    nsplit = kMaxGemmSplit;
-  }
+  const int64_t nsplit = max_split_for(M);
+  if (M < kLargeM) ncols = std::max<int64_t>(ncols, 2 * (int64_t)s.F);
   L.P = take((size_t)nsplit * M * ncols * 4);
   L.part = take((size_t)decode_attn_part_floats(B, s.nq, s.dh, kMaxDecodeSplits) * 4);
   L.logits = s.lm ? take((size_t)B * s.V * 4) : 0;
@@ -267,7 +270,7 @@ dory_status gemm_f32(Ctx& c, const uint16_t* A, int64_t lda, const void* W, int 
   g.A = A; g.lda = lda;
   g.B = reinterpret_cast<const uint16_t*>(W); g.ldb = K;
   g.M = (int)M; g.N = N; g.K = K;
-  g.nsplit = gemm_pick_split((int)M, N, K, M < kLargeM ? kMaxGemmSplit : 1);
+  g.nsplit = gemm_pick_split((int)M, N, K, max_split_for(M));
   g.C = c.P(); g.ldc = N; g.split_stride = M * N;
   HIPCHK(launch_gemm(g, EPI_F32, c.st));
   *nsplit_out = g.nsplit;
@@ -379,7 +382,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
 dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
   const Shape& s = c.s;
   const dory_sublayer_weights& w = c.m->sub[i];
-  const int ns_up = gemm_pick_split((int)c.M, 2 * s.F, s.d, c.M < kLargeM ? kMaxGemmSplit : 1);
+  const int ns_up = gemm_pick_split((int)c.M, 2 * s.F, s.d, max_split_for(c.M));
   if (ns_up == 1) {
     PROF(c, DORY_K_GEMM_UPGATE);
     GemmArgs g;
