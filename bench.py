@@ -177,6 +177,25 @@ def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4):
             out[f"{mode}_k{k}_kv_gb"] = round(kv.buffer.numel() / 1e9, 2)
             del kv, buf
             torch.cuda.empty_cache()
+    if "last_loop" in modes and max(ks) >= 4:
+        # one batch whose sequences run different loop counts, 4:1:1:1 over
+        # k = 1, 2, 3, 4 (36 / 9 / 9 / 10 of 64 sequences)
+        k_rows = [1] * 36 + [2] * 9 + [3] * 9 + [4] * 10
+        kv = gm.kv_cache("last_loop", 4, B, ctx + 1)
+        buf = kv.buffer.view(torch.bfloat16)
+        chunk = 1 << 28
+        for o in range(0, buf.numel(), chunk):
+            n = min(chunk, buf.numel() - o)
+            buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
+
+        def mixed():
+            kv.set_length(ctx)
+            gm.decode_step(kv, toks, k_rows, ws=ws, logits=True, next_token=True)
+        mixed()
+        dt = time_steps(mixed, steps)
+        out["last_loop_mixed_k1k2k3k4_4111"] = round(B * steps / dt, 1)
+        del kv, buf
+        torch.cuda.empty_cache()
     return out
 
 
@@ -336,7 +355,8 @@ def main():
         del kv, ws
         torch.cuda.empty_cache()
         result["decode_tok_s"] = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
-        result["decode_config"] = "B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each"
+        result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each; "
+                                   "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences")
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(k)
     print(json.dumps(result), flush=True)

@@ -192,6 +192,30 @@ dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, 
                              float* logits, int32_t* next, float* hidden, float* states,
                              void* stream);
 
+/* Steps whose sequences run different loop counts (one checkpoint served at
+ * any loop count per request, section Introduction; rollouts of one batch
+ * routed to different loop counts, section Post-Training, RLVR with a
+ * difficulty-aware loop curriculum). k_rows: host int32 [B], each >= 1, read
+ * before the call returns. Sequence b runs k_rows[b] loops of the recurrent
+ * block and then the output block; the step executes max k_rows loops and a
+ * sequence past its own count keeps its state (it is not updated, gets no
+ * loop boundary and stores no K/V). Each sequence's K/V of the recurrent
+ * attention sublayers is cached from its own last loop, so mode must be
+ * DORY_CACHE_LAST_LOOP (else DORY_ERR_MODE); a model without a recurrent
+ * block returns DORY_ERR_UNSUPPORTED. states[i] is written only for the
+ * sequences with k_rows[b] > i. Results equal those of running each
+ * sequence alone at its own loop count. Other arguments and errors as for
+ * dory_prefill / dory_decode_step; the per-sequence counts are copied into
+ * the workspace on the stream. */
+dory_status dory_prefill_rows(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                              int32_t T, const int32_t* k_rows, dory_cache_mode mode, void* ws,
+                              size_t ws_bytes, float* logits, int32_t* next, float* hidden,
+                              float* states, void* stream);
+dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                                  const int32_t* k_rows, dory_cache_mode mode, void* ws,
+                                  size_t ws_bytes, float* logits, int32_t* next, float* hidden,
+                                  float* states, void* stream);
+
 /* Declares that the first `length` positions of every sequence in the bound
  * buffer already hold valid K/V (for example a cache restored by the caller),
  * so that the next step starts at that position. 0 <= length <= max_seq;

@@ -80,6 +80,8 @@ SIGNATURES = {
     "dory_kv_slot": (_I32, [_P, _I32, _I32, ctypes.POINTER(dory_kv_slot_info)]),
     "dory_prefill": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_decode_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
+    "dory_prefill_rows": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
+    "dory_decode_step_rows": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_debug_mask": (_I32, [_I32, _I64, _I32, _P, _P]),
     "dory_kv_set_length": (_I32, [_P, _I64]),
     "dory_profile_begin": (_I32, [_P, _I32]),
@@ -172,6 +174,18 @@ def dory_prefill(m, kv, tokens, B, T, k, mode, ws, ws_bytes, logits, nxt, hidden
 def dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidden, states, stream):
     return lib().dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidden,
                                   states, stream)
+
+
+def dory_prefill_rows(m, kv, tokens, B, T, k_rows, mode, ws, ws_bytes, logits, nxt, hidden, states,
+                      stream):
+    return lib().dory_prefill_rows(m, kv, tokens, B, T, k_rows, mode, ws, ws_bytes, logits, nxt,
+                                   hidden, states, stream)
+
+
+def dory_decode_step_rows(m, kv, tokens, B, k_rows, mode, ws, ws_bytes, logits, nxt, hidden,
+                          states, stream):
+    return lib().dory_decode_step_rows(m, kv, tokens, B, k_rows, mode, ws, ws_bytes, logits, nxt,
+                                       hidden, states, stream)
 
 
 def dory_debug_mask(window, L, T, out, stream):

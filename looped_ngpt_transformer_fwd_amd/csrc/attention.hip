@@ -102,6 +102,9 @@ attn_prefill_kernel(AttnArgs a) {
       b = blockIdx.z;
     }
   }
+  // a sequence that has left the loop needs no attention output (its state
+  // is not updated); the whole workgroup leaves before any barrier
+  if (a.rl.k_rows && a.rl.loop >= a.rl.k_rows[b]) return;
   const int qb = wave / GRP, head = g * GRP + (wave % GRP);
   const int C = a.C;
   const int t0 = qt * BQ + qb * 32;
@@ -408,6 +411,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   __shared__ float wout[DEC_NT / 64][GRP][DH];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (a.rl.k_rows && a.rl.loop >= a.rl.k_rows[b]) return;  // left the loop (merge writes zeros)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 4, r = lane & 15;
   const int64_t bg = (int64_t)b * a.n_kv + g;
@@ -582,11 +586,15 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 // sums keep eight splits' loads in flight per thread.
 __global__ void __launch_bounds__(128)
 attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const uint16_t* gate,
-                           uint16_t* z) {
+                           uint16_t* z, RowLoops rl) {
   __shared__ float wsc[1024];  // 2^(m_s - M) per split (nsplit <= 1024)
   __shared__ float pm[128];    // per-thread partial maxima (blockDim = dh <= 128)
   const int bh = blockIdx.x, d = threadIdx.x;
   const int b = bh / n_q, h = bh % n_q;
+  if (rl.k_rows && rl.loop >= rl.k_rows[b]) {  // left the loop: no partials were written
+    z[(int64_t)b * n_q * dh + h * dh + d] = 0;
+    return;
+  }
   const int64_t stride = dh + 2;
   const float* pp = part + (int64_t)bh * nsplit * stride;
   float M = -INFINITY;
@@ -643,7 +651,7 @@ hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q), dim3(DH), 0, st, part, nsplit,
-                     a.n_q, DH, a.gate, a.z);
+                     a.n_q, DH, a.gate, a.z, a.rl);
   return hipGetLastError();
 }
 

@@ -60,6 +60,16 @@ struct GemmArgs {
 int gemm_pick_split(int M, int N, int K, int max_split);
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 
+// Loop counts per sequence for a step whose sequences run different k (the
+// loop-count-per-request property of the looped model). k_rows == nullptr:
+// every sequence runs every loop. Token row m belongs to sequence m / T; in
+// recurrent loop `loop` a sequence is active iff loop < k_rows[b].
+struct RowLoops {
+  const int32_t* k_rows = nullptr;  // device [B]
+  int loop = 0;
+  int T = 1;
+};
+
 // ---------------------------------------------------------------- row ops
 // h32/h16[m, :] = E[tok[m], :]; out-of-range ids give NaN rows.
 hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M, int d,
@@ -68,9 +78,12 @@ hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M,
 // nGPT update h <- N(h + alpha (N(y) - h)), y = sum of nsplit partials.
 // If x != null, additionally applies the loop boundary to the result:
 //   state_out (optional) = result; h <- N(result + x).
+// With rl.k_rows: rows of sequences that have left the loop are untouched,
+// and a sequence in its last loop gets no boundary.
 hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
                          int64_t split_stride, int64_t ldy, const float* alpha, int M, int d,
-                         const float* x, float* state_out, float* copy_out, hipStream_t st);
+                         const float* x, float* state_out, float* copy_out, hipStream_t st,
+                         RowLoops rl = RowLoops());
 
 // Loop boundary h <- N(h + x) (also writes the bf16 shadow).
 hipError_t launch_boundary(float* h32, uint16_t* h16, const float* x, int M, int d,
@@ -100,10 +113,11 @@ struct QkDest {
   int64_t pos_origin;
   int64_t ring;
 };
+// With rl.k_rows, sequences that have left the loop store no K/V.
 hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
                           int64_t p0, int n_q, int n_kv, int dh, const float* cs, const float* sn,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
-                          hipStream_t st);
+                          hipStream_t st, RowLoops rl = RowLoops());
 
 // RoPE table for positions p0 .. p0 + T - 1: cs/sn [T][dh/2] fp32 from fp64
 // angles (p0 + t) * base^(-2i/dh).
@@ -118,11 +132,13 @@ hipError_t launch_prefix_copy(const uint16_t* kc, const uint16_t* vc, int64_t c_
                               hipStream_t st);
 
 // Persistent-cache store of positions [pos_a, pos_b) from fresh buffers
-// (origin f_origin) into the cache (ring slots if ring > 0).
+// (origin f_origin) into the cache (ring slots if ring > 0). With
+// rl.k_rows, only sequences in their last loop (rl.loop == k_rows[b] - 1)
+// store.
 hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
                            int64_t f_origin, int B, int n_kv, int dh, int64_t pos_a,
                            int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
-                           int64_t ring, hipStream_t st);
+                           int64_t ring, hipStream_t st, RowLoops rl = RowLoops());
 
 // Zero columns [c0, c1) of every row of a fresh V^T buffer
 // ([B][n_kv][dh][f_rows]); the prefill attention reads whole 8-key chunks.
@@ -153,6 +169,8 @@ struct AttnArgs {
   int64_t p0;            // position of query row 0
   int window;            // 0 = full (causal) else sliding window
   float scale;           // logit scale (sqrt(dh))
+  RowLoops rl;           // sequences past their loop count are skipped (z rows
+                         // left as they are in prefill, zero in decode)
 };
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 

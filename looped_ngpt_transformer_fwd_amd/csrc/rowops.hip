@@ -34,9 +34,14 @@ embed_kernel(const int32_t* tok, const uint16_t* E, int vocab, int d, float* h32
 // boundary h <- N(result + x).
 __global__ void __launch_bounds__(NT_ROW)
 update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss, int64_t ldy,
-              const float* alpha, int d, const float* x, float* aux) {
+              const float* alpha, int d, const float* x, float* aux, RowLoops rl) {
   __shared__ float red[NT_ROW / 64];
   const int m = blockIdx.x;
+  if (rl.k_rows) {
+    const int kb = rl.k_rows[m / rl.T];
+    if (rl.loop >= kb) return;           // the sequence has left the loop: keep its state
+    if (rl.loop == kb - 1) x = nullptr;  // its last loop: no boundary into another one
+  }
   const int nv = d >> 2;
   float4 hv[MAXV], yv[MAXV];
   float syy = 0.f;
@@ -184,7 +189,7 @@ __global__ void swiglu_partials_kernel(const float* p, int nsplit, int64_t ss, i
 __global__ void __launch_bounds__(NT_ROW)
 qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq, int nkv,
                int dh, const float* cs_tab, const float* sn_tab, const float* s_qk, uint16_t* qh,
-               QkDest kv, uint16_t* gate) {
+               QkDest kv, uint16_t* gate, RowLoops rl) {
   const int m = blockIdx.x;
   const int b = m / C, t = m - b * C;
   const int64_t pos = p0 + t;
@@ -216,6 +221,7 @@ qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq
     if (hh < nq) {
       dst = qh + (((int64_t)b * nq + hh) * C + t) * dh;
     } else {
+      if (rl.k_rows && rl.loop >= rl.k_rows[b]) return;  // left the loop: no K/V store
       dst = kv.kbase + (((int64_t)b * nkv + (hh - nq)) * kv.k_rows + krow) * dh;
     }
     dst[i] = f2bf(s_qk[i] * r1 * inv);
@@ -234,6 +240,7 @@ qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq
   if (s < nsplit) v0 += row[s * ss + dq + dkv + idx];
   const float v = v0 + v1;
   if (idx < dkv) {
+    if (rl.k_rows && rl.loop >= rl.k_rows[b]) return;  // left the loop: no K/V store
     const int g = idx / dh, d = idx - g * dh;
     kv.vbase[(((int64_t)b * nkv + g) * dh + d) * kv.v_cols + krow] = f2bf(v);
   } else {
@@ -256,9 +263,10 @@ __global__ void prefix_copy_kernel(const uint16_t* kc, const uint16_t* vc, int64
 
 __global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
                                 int64_t f_origin, int nkv, int dh, int64_t pos_a, uint16_t* kc,
-                                uint16_t* vc, int64_t c_rows, int64_t ring) {
+                                uint16_t* vc, int64_t c_rows, int64_t ring, RowLoops rl) {
   const int64_t pos = pos_a + blockIdx.x;
   const int g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  if (rl.k_rows && rl.k_rows[b] != rl.loop + 1) return;  // not this sequence's last loop
   const int64_t bg = (int64_t)b * nkv + g;
   const int64_t crow = ring > 0 ? pos % ring : pos;
   const int64_t frow = pos - f_origin;
@@ -332,12 +340,13 @@ hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M,
 
 hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
                          int64_t split_stride, int64_t ldy, const float* alpha, int M, int d,
-                         const float* x, float* state_out, float* copy_out, hipStream_t st) {
+                         const float* x, float* state_out, float* copy_out, hipStream_t st,
+                         RowLoops rl) {
   if (d % 4 != 0 || d > 4 * MAXV * NT_ROW) return hipErrorInvalidValue;
   float* aux = state_out ? state_out : copy_out;
   if (state_out && copy_out) return hipErrorInvalidValue;
   hipLaunchKernelGGL(update_kernel, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
-                     split_stride, ldy, alpha, d, x, aux);
+                     split_stride, ldy, alpha, d, x, aux, rl);
   return hipGetLastError();
 }
 
@@ -365,13 +374,13 @@ hipError_t launch_swiglu_partials(const float* p, int nsplit, int64_t split_stri
 hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
                           int64_t p0, int n_q, int n_kv, int dh, const float* cs, const float* sn,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
-                          hipStream_t st) {
+                          hipStream_t st, RowLoops rl) {
   if (dh != 32 && dh != 64 && dh != 128) return hipErrorInvalidValue;
   const int per_block = NT_ROW / (dh / 2);
   const int ngroups = (n_q + n_kv + per_block - 1) / per_block;
   const int nvg = (n_kv * dh + n_q * dh + NT_ROW - 1) / NT_ROW;
   hipLaunchKernelGGL(qk_prep_kernel, dim3(B * C, ngroups + nvg), dim3(NT_ROW), 0, st, P, nsplit,
-                     split_stride, C, p0, n_q, n_kv, dh, cs, sn, s_qk, q_hat, kv, gate);
+                     split_stride, C, p0, n_q, n_kv, dh, cs, sn, s_qk, q_hat, kv, gate, rl);
   return hipGetLastError();
 }
 
@@ -388,10 +397,10 @@ hipError_t launch_prefix_copy(const uint16_t* kc, const uint16_t* vc, int64_t c_
 hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
                            int64_t f_origin, int B, int n_kv, int dh, int64_t pos_a,
                            int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
-                           int64_t ring, hipStream_t st) {
+                           int64_t ring, hipStream_t st, RowLoops rl) {
   if (pos_b <= pos_a) return hipSuccess;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
-                     kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring);
+                     kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring, rl);
   return hipGetLastError();
 }
 

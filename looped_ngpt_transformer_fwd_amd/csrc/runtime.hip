@@ -113,7 +113,7 @@ size_t slot_bytes(const Shape& s, int kind, int batch, int64_t max_seq) {
 
 // Workspace layout for B sequences of T tokens.
 struct WsLayout {
-  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, rope, total;
+  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, rope, krows, total;
   int64_t f_rows;
 };
 
@@ -140,6 +140,8 @@ WsLayout plan_ws(const Shape& s, int B, int T) {
   L.logits = s.lm ? take((size_t)B * s.V * 4) : 0;
   // cos / sin tables of the step's positions for the two RoPE bases
   L.rope = take((size_t)4 * T * (s.dh / 2) * 4);
+  // per-sequence loop counts of a mixed-k step
+  L.krows = take((size_t)B * 4);
   L.total = off;
   return L;
 }
@@ -249,6 +251,9 @@ struct Ctx {
   // prefill projections take the fused q/k/v/gate epilogue
   bool fused_qkv() const { return T > 1 && M >= kLargeM && s.dh == 128; }
   Profiler* prof() const { return &m->prof; }
+  int32_t* krows() const { return reinterpret_cast<int32_t*>(ws + L.krows); }
+  bool mixed = false;  // sequences run different loop counts (krows on the device)
+  RowLoops rl;         // loop masks while in the recurrent block of a mixed step
 };
 
 #define PROF(c, cls) ProfScope prof_scope_##__LINE__((c).prof(), (c).st, (cls))
@@ -317,6 +322,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
   aa.gate = c.gate(); aa.z = c.z();
   aa.B = c.B; aa.C = c.T; aa.n_q = s.nq; aa.n_kv = s.nkv; aa.dh = s.dh;
   aa.p0 = c.p0; aa.window = full ? 0 : s.W; aa.scale = (float)s.scale;
+  aa.rl = c.rl;
 
   if (c.T == 1) {
     // decode: the current token's K/V go straight into the cache slot (the
@@ -327,7 +333,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
       PROF(c, DORY_K_QK);
       HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh,
                           c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
-                          c.gate(), c.st));
+                          c.gate(), c.st, c.rl));
     }
     const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
     const int nsd = decode_attn_pick_split(lo, c.p0, !full);  // <= kMaxDecodeSplits (checked up front)
@@ -368,14 +374,14 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
       int64_t pa = c.p0;
       if (sp.ring > 0) pa = std::max<int64_t>(pa, c.p0 + c.T - sp.ring);
       HIPCHK(launch_kv_write(c.kf(), c.vf(), c.L.f_rows, f_origin, c.B, s.nkv, s.dh, pa,
-                             c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st));
+                             c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st, c.rl));
     }
   }
   st = gemm_f32(c, c.z(), s.dq(), w.w_o, s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O);
   if (st != DORY_OK) return st;
   PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
-                       uo.aux, nullptr, c.st));
+                       uo.aux, nullptr, c.st, c.rl));
   return DORY_OK;
 }
 
@@ -404,7 +410,7 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
   if (st != DORY_OK) return st;
   PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
-                       uo.aux, nullptr, c.st));
+                       uo.aux, nullptr, c.st, c.rl));
   return DORY_OK;
 }
 
@@ -443,7 +449,13 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   }
   for (int it = 0; it < k; ++it) {
     const int slot = per_loop ? it : 0;
-    const bool write = per_loop || it == k - 1;
+    // a mixed step stores each sequence's K/V at its own last loop
+    const bool write = per_loop || it == k - 1 || c.mixed;
+    if (c.mixed) {
+      c.rl.k_rows = c.krows();
+      c.rl.loop = it;
+      c.rl.T = c.T;
+    }
     float* st_out = states ? states + (int64_t)it * Md : nullptr;
     if (s.nrec == 0) {
       if (it > 0) HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
@@ -460,6 +472,7 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
       if (st != DORY_OK) return st;
     }
   }
+  c.rl = RowLoops();
   for (int i = s.nin + s.nrec; i < s.nsub(); ++i) {
     dory_status st = run_sublayer(c, i, 0, true, UpdateOpts());
     if (st != DORY_OK) return st;
@@ -485,11 +498,23 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
 }
 
 dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
-                        int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes, float* logits,
-                        int32_t* next, float* hidden, float* states, void* stream) {
+                        int32_t k, const int32_t* k_rows, dory_cache_mode mode, void* ws,
+                        size_t ws_bytes, float* logits, int32_t* next, float* hidden,
+                        float* states, void* stream) {
   if (!m || !kv || !tokens) return fail(DORY_ERR_ARG, "model, cache and tokens must be non-NULL");
   if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
   if (B <= 0 || T <= 0) return fail(DORY_ERR_ARG, "B and T must be >= 1");
+  if (k_rows) {
+    // per-sequence loop counts: the step runs max k_b loops
+    k = 0;
+    for (int b = 0; b < B; ++b) {
+      if (k_rows[b] < 1) return fail(DORY_ERR_ARG, "every per-sequence loop count must be >= 1");
+      k = std::max(k, k_rows[b]);
+    }
+    if (mode != DORY_CACHE_LAST_LOOP)
+      return fail(DORY_ERR_MODE, "per-sequence loop counts need the last-loop cache");
+    if (m->s.nrec == 0) return fail(DORY_ERR_UNSUPPORTED, "per-sequence loop counts need a recurrent block");
+  }
   if (k < 1) return fail(DORY_ERR_ARG, "loop count k must be >= 1");
   if (kv->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure; call dory_kv_reset");
   if (mode != kv->mode) return fail(DORY_ERR_MODE, "cache mode differs from the bound mode");
@@ -514,6 +539,11 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
   if ((logits || next) && !s.lm) return fail(DORY_ERR_ARG, "model has no LM head");
   Ctx c{m, kv, s, B, T, (int64_t)B * T, kv->len, reinterpret_cast<uint8_t*>(ws), L,
         reinterpret_cast<hipStream_t>(stream)};
+  if (k_rows) {
+    c.mixed = true;
+    if (hipMemcpyAsync(c.krows(), k_rows, (size_t)B * 4, hipMemcpyHostToDevice, c.st) != hipSuccess)
+      return fail(DORY_ERR_HIP, "copy of the per-sequence loop counts failed");
+  }
   dory_status st = run_step(c, tokens, k, logits, next, hidden, states);
   if (st != DORY_OK) {
     if (st == DORY_ERR_HIP) kv->invalid = true;
@@ -665,7 +695,7 @@ dory_status dory_prefill(dory_model* m, dory_kv* kv, const int32_t* tokens, int3
                          int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
                          float* logits, int32_t* next, float* hidden, float* states,
                          void* stream) {
-  return step_common(m, kv, tokens, B, T, k, mode, ws, ws_bytes, logits, next, hidden, states,
+  return step_common(m, kv, tokens, B, T, k, nullptr, mode, ws, ws_bytes, logits, next, hidden, states,
                      stream);
 }
 
@@ -673,8 +703,26 @@ dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, 
                              int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
                              float* logits, int32_t* next, float* hidden, float* states,
                              void* stream) {
-  return step_common(m, kv, tokens, B, 1, k, mode, ws, ws_bytes, logits, next, hidden, states,
+  return step_common(m, kv, tokens, B, 1, k, nullptr, mode, ws, ws_bytes, logits, next, hidden, states,
                      stream);
+}
+
+dory_status dory_prefill_rows(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                              int32_t T, const int32_t* k_rows, dory_cache_mode mode, void* ws,
+                              size_t ws_bytes, float* logits, int32_t* next, float* hidden,
+                              float* states, void* stream) {
+  if (!k_rows) return fail(DORY_ERR_ARG, "k_rows is NULL");
+  return step_common(m, kv, tokens, B, T, 0, k_rows, mode, ws, ws_bytes, logits, next, hidden,
+                     states, stream);
+}
+
+dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                                  const int32_t* k_rows, dory_cache_mode mode, void* ws,
+                                  size_t ws_bytes, float* logits, int32_t* next, float* hidden,
+                                  float* states, void* stream) {
+  if (!k_rows) return fail(DORY_ERR_ARG, "k_rows is NULL");
+  return step_common(m, kv, tokens, B, 1, 0, k_rows, mode, ws, ws_bytes, logits, next, hidden,
+                     states, stream);
 }
 
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length) {

@@ -127,8 +127,10 @@ class Model:
 
     def prefill(self, kv, tokens, k, ws=None, logits=True, next_token=False, hidden=False,
                 states=False):
-        """tokens: int32 device tensor [B, T]. Returns a dict of the requested
-        outputs (logits [B, V], next [B], hidden [B, T, d], states [k, B, T, d])."""
+        """tokens: int32 device tensor [B, T]; k: loop count, or one loop count
+        per sequence (list) for a mixed step. Returns a dict of the requested
+        outputs (logits [B, V], next [B], hidden [B, T, d], states [max k, B,
+        T, d])."""
         B, T = tokens.shape
         return self._step(kv, tokens, B, T, k, ws, logits, next_token, hidden, states, decode=False)
 
@@ -147,9 +149,27 @@ class Model:
         lg = torch.empty(B, sh.vocab, dtype=torch.float32, device=dev) if logits else None
         nx = torch.empty(B, dtype=torch.int32, device=dev) if next_token else None
         hd = torch.empty(B, T, sh.d_model, dtype=torch.float32, device=dev) if hidden else None
+        rows = None
+        if isinstance(k, (list, tuple)):
+            # per-sequence loop counts (host int32 array handed to the library)
+            if len(k) != B:
+                raise ValueError("one loop count per sequence")
+            rows = (ctypes.c_int32 * B)(*[int(x) for x in k])
+            k = max(int(x) for x in k)
         stt = torch.empty(k, B, T, sh.d_model, dtype=torch.float32, device=dev) if states else None
         mode = kv.mode_code
-        if decode:
+        if rows is not None:
+            if decode:
+                st = C.dory_decode_step_rows(self.handle, kv.handle, _ptr(tokens), B, rows, mode,
+                                             _ptr(ws), ws.numel(), _ptr(lg), _ptr(nx), _ptr(hd),
+                                             _ptr(stt), _stream())
+                where = "dory_decode_step_rows"
+            else:
+                st = C.dory_prefill_rows(self.handle, kv.handle, _ptr(tokens), B, T, rows, mode,
+                                         _ptr(ws), ws.numel(), _ptr(lg), _ptr(nx), _ptr(hd),
+                                         _ptr(stt), _stream())
+                where = "dory_prefill_rows"
+        elif decode:
             st = C.dory_decode_step(self.handle, kv.handle, _ptr(tokens), B, k, mode, _ptr(ws),
                                     ws.numel(), _ptr(lg), _ptr(nx), _ptr(hd), _ptr(stt), _stream())
             where = "dory_decode_step"

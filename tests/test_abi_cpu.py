@@ -121,6 +121,30 @@ def test_validation_errors_enqueue_nothing():
     C.dory_kv_destroy(kv)
 
 
+def _prefill_rows(m, kv, k_rows, B=2, T=8, mode=C.DORY_CACHE_LAST_LOOP, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = M.workspace_bytes(m.shape, B, T)
+    rows = (ctypes.c_int32 * len(k_rows))(*k_rows) if k_rows is not None else None
+    return C.dory_prefill_rows(m.handle, kv, ctypes.c_void_p(0x500000), B, T, rows, mode,
+                               ctypes.c_void_p(0x700000), ws_bytes, None, None, None, None, None)
+
+
+def test_mixed_loop_counts_validated_before_enqueue():
+    """Per-sequence loop counts: NULL or a count below 1 is an argument error,
+    a per-loop cache is a mode error (each sequence's cache comes from its own
+    last loop), and every rejection leaves the cache length unchanged."""
+    m, kv = _model_and_kv()
+    assert _prefill_rows(m, kv, None) == C.DORY_ERR_ARG
+    assert _prefill_rows(m, kv, [1, 0]) == C.DORY_ERR_ARG
+    assert _prefill_rows(m, kv, [2, 3], ws_bytes=16) == C.DORY_ERR_WORKSPACE
+    assert _prefill_rows(m, kv, [2, 3], mode=C.DORY_CACHE_PER_LOOP) == C.DORY_ERR_MODE
+    assert C.dory_kv_length(kv) == 0
+    C.dory_kv_destroy(kv)
+    m2, kv2 = _model_and_kv(mode="per_loop")
+    assert _prefill_rows(m2, kv2, [1, 2], mode=C.DORY_CACHE_PER_LOOP) == C.DORY_ERR_MODE
+    C.dory_kv_destroy(kv2)
+
+
 def test_per_loop_k_above_k_max_rejected():
     m, kv = _model_and_kv(mode="per_loop", k_max=2)
     assert _prefill(m, kv, k=3, mode=C.DORY_CACHE_PER_LOOP) == C.DORY_ERR_MODE
