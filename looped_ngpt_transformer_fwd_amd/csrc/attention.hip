@@ -36,6 +36,14 @@ __device__ __forceinline__ void dma16_flat(const void* src, uint8_t* lds_block) 
 
 __device__ __forceinline__ void wait_vm0_attn() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// A pointer held in scalar registers (the value is the same in every lane).
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
 // K/V tiles are staged by direct global->LDS DMA into two stages (the next
 // tile's loads are in flight during the current tile's MFMAs). Both tiles are
 // stored XOR-swizzled by row so that the MFMA fragment reads of consecutive
@@ -162,26 +170,49 @@ attn_prefill_kernel(AttnArgs a) {
         voff[kb][kc][h] = d * (BN * 2) + ((c ^ ((d >> 1) & 7)) << 4) + hl * 8;
       }
 
-  auto issue = [&](int64_t kt, uint8_t* kst, uint8_t* vst) {
+  // Source rows are chosen with selects, not branches: a branch between the
+  // DMA and the LDS reads makes the compiler drain the DMA in flight before
+  // the reads. A lane's row (K) or 8-key column group (V) within a tile is
+  // the same in every tile, so its remainder modulo the ring is taken once;
+  // per tile only the (uniform) remainder of the tile start is added, with
+  // one conditional subtraction. Positions fit 31 bits (checked on the
+  // host); a layer without a ring uses a divisor above every position.
+  const uint32_t ring_div = a.ring > 0 ? (uint32_t)a.ring : 0x7FFFFFFFu;
+  // the four base pointers as uniform values (a select between two fields of
+  // the argument block would become a per-lane load of the selected field)
+  const uint16_t* const kcb = uniform_ptr(a.kc + bg * a.c_rows * DH);
+  const uint16_t* const kfb = uniform_ptr(a.kf + bg * a.f_rows * DH);
+  const uint16_t* const vcb = uniform_ptr(a.vc + bg * DH * a.c_rows);
+  const uint16_t* const vfb = uniform_ptr(a.vf + bg * DH * a.f_rows);
+  constexpr int KJ = (K_BLOCKS + PF_WAVES - 1) / PF_WAVES;
+  constexpr int VJ = (V_BLOCKS + PF_WAVES - 1) / PF_WAVES;
+  uint32_t k_rm[KJ], v_cm[VJ];
 #pragma unroll
-    for (int j = 0; j < (K_BLOCKS + PF_WAVES - 1) / PF_WAVES; ++j) {
+  for (int j = 0; j < KJ; ++j) k_rm[j] = (uint32_t)((wave + j * PF_WAVES) * KRPB + lane / KCH) % ring_div;
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) {
+    const int d = (wave + j * PF_WAVES) * 8 + (lane >> 3);
+    v_cm[j] = (uint32_t)(((lane & 7) ^ ((d >> 1) & 7)) * 8) % ring_div;
+  }
+  auto issue = [&](int64_t kt, uint8_t* kst, uint8_t* vst) __attribute__((always_inline)) {
+    const uint32_t km = (uint32_t)kt % ring_div;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
       const int blk = wave + j * PF_WAVES;
       if (K_BLOCKS % PF_WAVES != 0 && blk >= K_BLOCKS) break;
       const int r = blk * KRPB + lane / KCH;
       const int c = (lane % KCH) ^ kswz<DH>(r);
       const int64_t u = kt + r;
-      const uint16_t* src;
-      if (u < a.f_origin) {
-        const int64_t row = a.ring > 0 ? u % a.ring : u;
-        src = a.kc + (bg * a.c_rows + row) * DH;
-      } else {
-        const int64_t row = min(u - a.f_origin, a.f_rows - 1);
-        src = a.kf + (bg * a.f_rows + row) * DH;
-      }
-      dma16_flat(src + c * 8, kst + blk * 1024);
+      uint32_t ci = km + k_rm[j];
+      ci = ci >= ring_div ? ci - ring_div : ci;
+      const bool in_cache = u < a.f_origin;
+      // per-lane parts in 32 bits (rows * DH stay below 2^31)
+      const uint32_t fr = (uint32_t)min(u - a.f_origin, a.f_rows - 1);
+      const uint32_t off = (in_cache ? ci : fr) * DH + c * 8;
+      dma16_flat((in_cache ? kcb : kfb) + off, kst + blk * 1024);
     }
 #pragma unroll
-    for (int j = 0; j < (V_BLOCKS + PF_WAVES - 1) / PF_WAVES; ++j) {
+    for (int j = 0; j < VJ; ++j) {
       const int blk = wave + j * PF_WAVES;
       if (V_BLOCKS % PF_WAVES != 0 && blk >= V_BLOCKS) break;
       const int d = blk * 8 + (lane >> 3);
@@ -189,17 +220,16 @@ attn_prefill_kernel(AttnArgs a) {
       // chunks at or past the last key load the row's first chunk instead:
       // finite values that meet probabilities of exactly 0 (the loads stay
       // unconditional so every wave issues a fixed number per tile)
-      int64_t u = kt + c * 8;
-      const uint16_t* src;
-      if (u >= k_end) {
-        src = a.f_origin > 0 ? a.vc + (bg * DH + d) * a.c_rows : a.vf + (bg * DH + d) * a.f_rows;
-      } else if (u < a.f_origin) {
-        const int64_t col = a.ring > 0 ? u % a.ring : u;
-        src = a.vc + (bg * DH + d) * a.c_rows + col;
-      } else {
-        src = a.vf + (bg * DH + d) * a.f_rows + (u - a.f_origin);
-      }
-      dma16_flat(src, vst + blk * 1024);
+      const int64_t u = kt + c * 8;
+      uint32_t ci = km + v_cm[j];
+      ci = ci >= ring_div ? ci - ring_div : ci;
+      // every candidate offset is computed, then selected (no branch);
+      // per-lane parts in 32 bits (DH * rows stays below 2^31)
+      const bool past = u >= k_end, in_cache = u < a.f_origin;
+      const bool use_c = past ? a.f_origin > 0 : in_cache;
+      const uint32_t col = past ? 0u : in_cache ? ci : (uint32_t)(u - a.f_origin);
+      const uint32_t off = (uint32_t)d * (use_c ? (uint32_t)a.c_rows : (uint32_t)a.f_rows) + col;
+      dma16_flat((use_c ? vcb : vfb) + off, vst + blk * 1024);
     }
   };
   // DMA instructions issued per tile by this wave
@@ -210,22 +240,27 @@ attn_prefill_kernel(AttnArgs a) {
   // vmcnt waits in the loop count DMA only
   wait_vm0_attn();
   issue(kt_first, ks0, vs0);
-  if (ntiles > 1) issue(kt_first + BN, ks1, vs1);
+  issue(kt_first + (int64_t)min(1, ntiles - 1) * BN, ks1, vs1);
 
+  // Every tile issues the loads of the tile two ahead, clamped to the last
+  // tile (a reload into a stage no one reads again), so the wait count is
+  // the same in every tile and no branch surrounds the DMA.
   auto tile = [&](int it, const uint8_t* kst, const uint8_t* vst, uint8_t* kn, uint8_t* vn) {
     const int64_t kt = kt_first + (int64_t)it * BN;
     // this wave's loads of tile `it` are done once at most the next tile's
     // loads are outstanding
-    if (it + 1 < ntiles) {
+    if constexpr (K_BLOCKS % PF_WAVES == 0 && V_BLOCKS % PF_WAVES == 0) {
+      constexpr int pt = K_BLOCKS / PF_WAVES + V_BLOCKS / PF_WAVES;
+      static_assert(pt == 1 || pt == 2 || pt == 4, "wait counts");
+      __builtin_amdgcn_s_waitcnt(pt == 4 ? 0x0F74 : pt == 2 ? 0x0F72 : 0x0F71);
+    } else {
       if (per_tile == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
       else if (per_tile == 2) __builtin_amdgcn_s_waitcnt(0x0F72);
       else if (per_tile == 1) __builtin_amdgcn_s_waitcnt(0x0F71);
       else wait_vm0_attn();
-    } else {
-      wait_vm0_attn();
     }
     barrier_lds();
-    if (it + 2 < ntiles) issue(kt + 2 * BN, kn, vn);
+    issue(kt_first + (int64_t)min(it + 2, ntiles - 1) * BN, kn, vn);
 
     // tile class for this wave
     const bool dead = !wave_live || kt > wq_hi ||
@@ -301,14 +336,22 @@ attn_prefill_kernel(AttnArgs a) {
     }
   };
 
-  // stage of tile t is t % 3; the tile two ahead goes into stage (t + 2) % 3.
-  // At the loop header the compiler cannot count the DMA in flight and
-  // drains it before the first LDS read, once per 3 tiles.
-  for (int it = 0; it < ntiles; it += 3) {
+  // stage of tile t is t % 3; the tile two ahead goes into stage (t + 2) % 3
+  for (int it = 0;; it += 6) {
     tile(it, ks0, vs0, ks2, vs2);
-    if (it + 1 < ntiles) tile(it + 1, ks1, vs1, ks0, vs0);
-    if (it + 2 < ntiles) tile(it + 2, ks2, vs2, ks1, vs1);
+    if (it + 1 >= ntiles) break;
+    tile(it + 1, ks1, vs1, ks0, vs0);
+    if (it + 2 >= ntiles) break;
+    tile(it + 2, ks2, vs2, ks1, vs1);
+    if (it + 3 >= ntiles) break;
+    tile(it + 3, ks0, vs0, ks2, vs2);
+    if (it + 4 >= ntiles) break;
+    tile(it + 4, ks1, vs1, ks0, vs0);
+    if (it + 5 >= ntiles) break;
+    tile(it + 5, ks2, vs2, ks1, vs1);
+    if (it + 6 >= ntiles) break;
   }
+  wait_vm0_attn();  // the clamped reloads have landed before the stages are reused
 
   // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]. The O^T
   // registers hold one query per lane, so the 32 x DH tile of a wave is

@@ -192,11 +192,12 @@ gemm_nt_kernel(GemmArgs g) {
 // full load, which one step of 64 (about 2000 cycles) did not.
 // A stage holds the A tile (256 rows x 64 B) and then the B tile. Each 1 KiB
 // DMA block holds 16 rows; lane l writes LDS bytes [16 l, 16 l + 16) and
-// fetches logical 16-byte chunk (l % 4) ^ ((row / 4) % 4) of its row, i.e.
-// the tile is stored XOR-swizzled. The LDS serves a 16-byte read for 16 lanes
-// per cycle from its 64 banks (256 B); fragment reads of 16 consecutive rows
-// then hit 16 distinct 16-byte bank groups (rows 4j .. 4j + 3 differ in their
-// offset within 256 B, rows 4j and 4j + 4 in their chunk).
+// fetches logical 16-byte chunk (l % 4) ^ ((row / 2) % 4) of its row, i.e.
+// the tile is stored XOR-swizzled. With this XOR the 16-byte fragment reads
+// (16 consecutive rows, one chunk each) run free of bank conflicts on this
+// part; the XOR by (row / 4) % 4, which keeps the 16 rows in 16 distinct
+// 16-byte bank groups, still conflicted on half of the LDS cycles (measured
+// with the LDS bank-conflict counters).
 // One LDS-only barrier per step; the four stages are separate arrays and the
 // loop body is unrolled over them, so that the compiler sees which stage a
 // DMA writes and waits for in-flight DMA only through the explicit counts.
@@ -311,7 +312,7 @@ gemm_big_kernel(GemmArgs g) {
 
   // DMA sources: wave w fills blocks w, w + NW of each operand tile
   const int lr = lane >> 2;                  // row within the block
-  const int lc = (lane & 3) ^ ((lr >> 2) & 3);  // logical chunk (block rows are 16-aligned)
+  const int lc = (lane & 3) ^ ((lr >> 1) & 3);  // logical chunk (block rows are 16-aligned)
   uint32_t aoff[BPW], boff[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
@@ -328,7 +329,7 @@ gemm_big_kernel(GemmArgs g) {
   // LDS lane offset of the fragment reads; fragment rows are multiples of 16
   // apart, so the swizzle of a lane's row depends on lane & 15 only
   const int fr = lane & 15, fc = lane >> 4;
-  const int loff = fr * 64 + ((fc ^ ((fr >> 2) & 3)) << 4);
+  const int loff = fr * 64 + ((fc ^ ((fr >> 1) & 3)) << 4);
   const int a_wave = wm * BIG_WM * 64, b_wave = BIG_OP_BYTES + wn * BIG_WN * 64;
 
   floatx4 acc[FM][FN];
@@ -360,7 +361,7 @@ gemm_big_kernel(GemmArgs g) {
     // Stage (s + 3) % 4 is last read by B's M(s - 1) in phase 2s - 1, so both
     // groups' M(s) may load it. The DMA of step t must be complete in every
     // wave before the barrier that opens phase 2t (A's M(t)): A waits at the
-    // end of C(t - 2), B at the end of M(t - 2). Each M issues exactly 4 DMA
+    // end of C(t - 1), B at the end of M(t - 1). Each M issues exactly 4 DMA
     // (the last steps reload the final step into a stage no one reads again),
     // so both waits are vmcnt(8) (the two younger steps stay in flight).
     auto mem = [&](int ks, const uint8_t* cur, uint8_t* nxt) {
