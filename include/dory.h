@@ -141,7 +141,8 @@ dory_status dory_schedule(const dory_config* cfg, int32_t* kinds_out, int32_t ca
  * rows; recurrent sublayers hold k_max slots under per-loop caching and one
  * otherwise; sliding-window slots hold min(max_seq, window) rows, rounded up
  * to a multiple of 8, as a ring; full-attention slots hold max_seq rows
- * rounded up to a multiple of 8). Returns 0 on invalid arguments. */
+ * rounded up to a multiple of 8). Returns 0 on invalid arguments
+ * (including max_seq above 2^24). */
 size_t dory_kv_bytes(const dory_config* cfg, dory_cache_mode mode, int32_t k_max,
                      int32_t batch, int64_t max_seq);
 
@@ -151,7 +152,7 @@ size_t dory_workspace_bytes(const dory_config* cfg, int32_t batch, int32_t token
 
 /* Binds a caller-owned device buffer of at least dory_kv_bytes() bytes as
  * the KV cache of `batch` sequences of at most max_seq tokens, in `mode`;
- * lengths start at 0. */
+ * lengths start at 0. max_seq is at most 2^24 (DORY_ERR_ARG otherwise). */
 dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dory_cache_mode mode,
                          int32_t k_max, int32_t batch, int64_t max_seq, dory_kv** out);
 void dory_kv_destroy(dory_kv* kv);

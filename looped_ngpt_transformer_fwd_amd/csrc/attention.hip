@@ -176,7 +176,8 @@ attn_prefill_kernel(AttnArgs a) {
   // the same in every tile, so its remainder modulo the ring is taken once;
   // per tile only the (uniform) remainder of the tile start is added, with
   // one conditional subtraction. Positions fit 31 bits (checked on the
-  // host); a layer without a ring uses a divisor above every position.
+  // host: at most 2^24); a layer without a ring uses a divisor above every
+  // position.
   const uint32_t ring_div = a.ring > 0 ? (uint32_t)a.ring : 0x7FFFFFFFu;
   // the four base pointers as uniform values (a select between two fields of
   // the argument block would become a per-lane load of the selected field)

@@ -102,6 +102,10 @@ dory_status build_schedule(const dory_config* c, const Shape& s, std::vector<int
 
 bool is_recurrent(const Shape& s, int i) { return i >= s.nin && i < s.nin + s.nrec; }
 
+// Longest cache: the attention kernels index a cached row within one
+// (sequence, KV head) slab, and head_dim x rows, in 32 bits.
+constexpr int64_t kMaxSeq = int64_t(1) << 24;
+
 int64_t slot_rows(const Shape& s, int kind, int64_t max_seq) {
   if (kind == DORY_LAYER_ATTN_SWA) return round8(std::min<int64_t>(max_seq, s.W));
   return round8(max_seq);
@@ -608,7 +612,7 @@ size_t dory_kv_bytes(const dory_config* cfg, dory_cache_mode mode, int32_t k_max
                      int64_t max_seq) {
   Shape s;
   if (read_shape(cfg, &s) != DORY_OK) return 0;
-  if (k_max < 1 || batch < 1 || max_seq < 1) return 0;
+  if (k_max < 1 || batch < 1 || max_seq < 1 || max_seq > kMaxSeq) return 0;
   if (mode != DORY_CACHE_LAST_LOOP && mode != DORY_CACHE_PER_LOOP) return 0;
   std::vector<int> kinds;
   if (build_schedule(cfg, s, &kinds) != DORY_OK) return 0;
@@ -636,6 +640,7 @@ dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dor
   if (mode != DORY_CACHE_LAST_LOOP && mode != DORY_CACHE_PER_LOOP)
     return fail(DORY_ERR_MODE, "unknown cache mode");
   if (k_max < 1 || batch < 1 || max_seq < 1) return fail(DORY_ERR_ARG, "k_max, batch, max_seq must be >= 1");
+  if (max_seq > kMaxSeq) return fail(DORY_ERR_ARG, "max_seq above 2^24");
   const Shape& s = m->s;
   dory_kv* kv = new dory_kv();
   kv->m = m; kv->base = reinterpret_cast<uint8_t*>(kv_dev); kv->bytes = kv_bytes;

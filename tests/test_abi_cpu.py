@@ -159,6 +159,12 @@ def test_bind_rejects_small_buffer_and_bad_mode():
     assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n - 1, 0, 1, 2, 64, h) == \
         C.DORY_ERR_CAPACITY
     assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n, 7, 1, 2, 64, h) == C.DORY_ERR_MODE
+    # the attention kernels index a slab of head_dim x rows in 32 bits
+    big = 1 << 24
+    assert M.kv_bytes(synth.TINY, "last_loop", 1, 1, big) > 0
+    assert M.kv_bytes(synth.TINY, "last_loop", 1, 1, big + 1) == 0
+    assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), 1 << 40, 0, 1, 1, big + 1, h) == \
+        C.DORY_ERR_ARG
 
 
 def test_model_create_rejects_bad_configs():
