@@ -151,24 +151,29 @@ attn_prefill_kernel(AttnArgs a) {
   const bool wave_live = t0 < C;
   const int64_t wq_lo = a.p0 + t0, wq_hi = a.p0 + min(t0 + 31, C - 1);
 
-  // fragment read offsets (lane parts)
+  // Fragment read offsets (lane parts). Row r of the S^T product's A operand
+  // is key row perm(r) of the K tile, perm swapping bits 2 and 3 of r: in the
+  // 32x32 accumulator layout lane l then holds, in elements 8 h .. 8 h + 7,
+  // the scores of keys 16 h + 8 (l / 32) + 0 .. 7 of each 32-key block,
+  // which is exactly the k-slice lane l supplies to the P V product. So the
+  // V^T operand of a lane is 8 consecutive keys of one head dimension: one
+  // 16-byte LDS read, and P needs no shuffle.
   int koff[DH / 16];
 #pragma unroll
   for (int s = 0; s < DH / 16; ++s) {
-    const int r = lane & 31;
+    const int r0 = lane & 31;
+    const int r = (r0 & 0x13) | ((r0 & 4) << 1) | ((r0 & 8) >> 1);
     koff[s] = r * DH * 2 + (((2 * s + hl) ^ kswz<DH>(r)) << 4);
   }
-  int voff[BN / 32][2][2];
+  int voff[BN / 32][2];
 #pragma unroll
   for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int d = lane & 31;
-        const int c = kb * 4 + kc * 2 + h;
-        voff[kb][kc][h] = d * (BN * 2) + ((c ^ ((d >> 1) & 7)) << 4) + hl * 8;
-      }
+    for (int kc = 0; kc < 2; ++kc) {
+      const int d = lane & 31;
+      const int c = kb * 4 + kc * 2 + hl;  // keys 8 c .. 8 c + 7 of the tile
+      voff[kb][kc] = d * (BN * 2) + ((c ^ ((d >> 1) & 7)) << 4);
+    }
 
   // Source rows are chosen with selects, not branches: a branch between the
   // DMA and the LDS reads makes the compiler drain the DMA in flight before
@@ -282,13 +287,13 @@ attn_prefill_kernel(AttnArgs a) {
     }
     if (!interior) {
       // relative positions fit 32 bits: |pq - u| < C + 64
-      const int rel0 = (int)(pq - kt) - hl * 4;  // pq - (key index within tile)
+      const int rel0 = (int)(pq - kt) - hl * 8;  // pq - (key index within tile)
       const bool qok = tq < C;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int dist = rel0 - (kb * 32 + (e >> 2) * 8 + (e & 3));  // pq - u
+          const int dist = rel0 - (kb * 32 + (e >> 3) * 16 + (e & 7));  // pq - u
           const bool vis = qok && dist >= 0 && (a.window == 0 || dist < a.window);
           if (!vis) sacc[kb][e] = -INFINITY;
         }
@@ -299,18 +304,23 @@ attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * sl2);
-    m_run = m_new;
-    if (__ballot(corr != 1.f)) {
+    // Lazy rescaling: the reference maximum m_run (that of the exponentials
+    // accumulated so far) moves only when a score exceeds it by more than 8
+    // in base-2 units, so probabilities stay below 2^8 and o and l are
+    // rescaled rarely; the final o / l is the same softmax either way. (From
+    // m_run = -inf the first visible score always moves it; all-masked
+    // queries keep -inf and contribute probabilities of 0.)
+    if (__ballot((mx - m_run) * sl2 > 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * sl2);
+      m_run = m_new;
       l_run *= corr;
 #pragma unroll
       for (int i = 0; i < DH / 32; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[i][e] *= corr;
     }
-    const float nm = -m_use * sl2;
+    const float nm = -(m_run == -INFINITY ? 0.f : m_run) * sl2;
     bf16x8 pf[BN / 32][2];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -327,11 +337,7 @@ attn_prefill_kernel(AttnArgs a) {
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + voff[kb][kc][0]);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + voff[kb][kc][1]);
-          bf16x8 vfr;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) { vfr[j] = lo[j]; vfr[j + 4] = hi[j]; }
+          const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(vrow + voff[kb][kc]);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, pf[kb][kc], o[db], 0, 0, 0);
         }
     }
