@@ -224,6 +224,46 @@ dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tok
  * by earlier ones after this call. */
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length);
 
+/* ---- MXFP8 weights (W8A16) ------------------------------------------------
+ * Section Quantization (Post-Training Quantization): an MXFP8 checkpoint made
+ * by post-training quantization with maximum scaling, weight-only, covering
+ * every weight matrix but the token embeddings and the LM head; vectors and
+ * scalars stay in full precision. Format: blocks of 32 consecutive elements
+ * of a weight row share a scale 2^(c - 127) stored as the byte c; elements
+ * are FP8 E4M3 codes (bias 7, 3 mantissa bits, largest finite 448). Scale
+ * rule: the block's shared exponent is floor(log2(max |w|)) - 8, at least
+ * -126; each w * 2^-shared is rounded to the nearest E4M3 value, ties to the
+ * even code, saturating at 448, the sign of a zero kept.
+ *
+ * Quantizes one bf16 matrix [rows][cols] (row-major, cols a positive
+ * multiple of 32): codes uint8 [rows][cols], scales uint8 [rows][cols / 32]
+ * and, if deq is not NULL, the dequantized values as bf16 [rows][cols] (an
+ * E4M3 value times a power of two is exact in bf16). Device pointers; w,
+ * codes and deq 16-byte aligned; asynchronous on `stream`. */
+dory_status dory_mxfp8_quantize(const void* w, int64_t rows, int32_t cols, void* codes,
+                                void* scales, void* deq, void* stream);
+
+/* Bytes of device memory that dory_model_quantize_mxfp8 needs: for every
+ * projection matrix in sublayer order (attention: w_qkvg then w_o; MLP:
+ * w_upgate then w_down) a region holding its codes, scales and bf16
+ * dequantized copy, each part starting at a multiple of 256 bytes. Returns 0
+ * on an invalid configuration. */
+size_t dory_mxfp8_bytes(const dory_config* cfg);
+
+/* Quantizes the model's projection matrices into the caller-owned device
+ * buffer `buf` (256-byte aligned, at least dory_mxfp8_bytes() bytes; layout
+ * as described there), asynchronously on `stream`, and enables them: from
+ * then on every projection computes with the dequantized weights (W8A16).
+ * Calls with at most 64 token rows (decode) stream the 8-bit codes through
+ * the small-M kernel; larger calls read the bf16 dequantized copy. The
+ * embedding and LM head stay bf16. The buffer must outlive the model's use
+ * of it. DORY_ERR_CAPACITY if the buffer is too small. */
+dory_status dory_model_quantize_mxfp8(dory_model* m, void* buf, size_t bytes, void* stream);
+
+/* Switches between the bf16 weights (on = 0) and the MXFP8 copy (on != 0,
+ * only after dory_model_quantize_mxfp8; DORY_ERR_ARG otherwise). */
+dory_status dory_model_use_mxfp8(dory_model* m, int32_t on);
+
 /* Kernel classes timed by the measurement hooks below. */
 typedef enum dory_kernel_class {
   DORY_K_GEMM_QKVG = 0,   /* q/k/v/gate projection */

@@ -86,6 +86,10 @@ SIGNATURES = {
     "dory_kv_set_length": (_I32, [_P, _I64]),
     "dory_profile_begin": (_I32, [_P, _I32]),
     "dory_profile_end": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
+    "dory_mxfp8_quantize": (_I32, [_P, _I64, _I32, _P, _P, _P, _P]),
+    "dory_mxfp8_bytes": (_SZ, [ctypes.POINTER(dory_config)]),
+    "dory_model_quantize_mxfp8": (_I32, [_P, _P, _SZ, _P]),
+    "dory_model_use_mxfp8": (_I32, [_P, _I32]),
     "dory_status_string": (ctypes.c_char_p, [_I32]),
     "dory_last_error": (ctypes.c_char_p, []),
 }
@@ -194,6 +198,22 @@ def dory_debug_mask(window, L, T, out, stream):
 
 def dory_kv_set_length(kv, length):
     return lib().dory_kv_set_length(kv, length)
+
+
+def dory_mxfp8_quantize(w, rows, cols, codes, scales, deq, stream):
+    return lib().dory_mxfp8_quantize(w, rows, cols, codes, scales, deq, stream)
+
+
+def dory_mxfp8_bytes(cfg):
+    return lib().dory_mxfp8_bytes(ctypes.byref(cfg))
+
+
+def dory_model_quantize_mxfp8(m, buf, nbytes, stream):
+    return lib().dory_model_quantize_mxfp8(m, buf, nbytes, stream)
+
+
+def dory_model_use_mxfp8(m, on):
+    return lib().dory_model_use_mxfp8(m, on)
 
 
 DORY_K_NUM_CLASSES = 10

@@ -686,6 +686,144 @@ gemm_skinny_kernel(GemmArgs g) {
   }
 }
 
+// Small-M kernel with MXFP8 weights (W8A16): the same 64 x 64 tiles, four
+// waves of 32 x 32 and four-stage DMA ring as the bf16 kernel, with the
+// weight tile held as E4M3 codes (64 columns x 64 bytes per step, half the
+// bytes) and converted to bf16 in registers by the hardware conversion
+// (v_cvt_scalef32_pk_bf16_fp8: two codes times the block scale per
+// instruction) just before the MFMA; the product is then the bf16 product
+// with the dequantized weights, which are exact in bf16. The block scales of
+// the workgroup's 64 columns and K range (two per step and column) are read
+// into LDS once, before the DMA stream starts. Every step issues exactly
+// three DMA per wave (two activation blocks, one code block), so the wait
+// before each step is vmcnt(6).
+constexpr int MX_MAX_STEPS = 96;  // K steps of 64 per workgroup (scale table size)
+
+template <int EPI>
+__global__ void __launch_bounds__(256)
+gemm_skinny_fp8_kernel(GemmArgs g) {
+  constexpr int SA = 64 * 128;  // activation tile of one stage: 64 rows x 64 k
+  constexpr int SB = 64 * 64;   // code tile: 64 columns x 64 k
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA3[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB3[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t ssc[64 * 2 * MX_MAX_STEPS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * 64;
+  const int ksteps = g.K / BK;
+  const int per = (ksteps + g.nsplit - 1) / g.nsplit;
+  const int ks0 = blockIdx.z * per;
+  const int n = max(0, min(ksteps, ks0 + per) - ks0);
+
+  // block scales: column c, block j of this workgroup's K range at c * 2n + j
+  {
+    const int nb = g.K / 32, w2 = 2 * n;
+    for (int idx = tid; idx < 64 * w2; idx += 256) {
+      const int c = idx / w2, j = idx - c * w2;
+      ssc[idx] = g.Bs[(int64_t)min(n0 + c, g.N - 1) * nb + 2 * ks0 + j];
+    }
+  }
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.Bq, (uint32_t)((int64_t)(g.N - 1) * g.K + g.K));
+  const int lr = lane >> 3;
+  uint32_t aoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave + 4 * i) * 8 + lr;
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);
+    aoff[i] = (uint32_t)((int64_t)min(r, g.M - 1) * g.lda * 2 + lc * 16);
+  }
+  // code block `wave`: 16 columns x 64 bytes; lane l writes LDS bytes
+  // [16 l, 16 l + 16) = chunk l % 4 of column l / 4, fetching logical chunk
+  // (l % 4) ^ ((column / 2) % 4)
+  uint32_t boff;
+  {
+    const int r = wave * 16 + (lane >> 2);
+    const int lc = (lane & 3) ^ ((r >> 1) & 3);
+    boff = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.K + lc * 16);
+  }
+  const int fr = lane & 31, fh = lane >> 5;
+  int aloff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) aloff[kk] = fr * 128 + (((2 * kk + fh) ^ ((fr >> 1) & 7)) << 4);
+  const int bcol = wn * 32 + fr;  // column of this lane's weight fragment within the tile
+  int bloff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) bloff[kk] = bcol * 64 + ((kk ^ ((bcol >> 1) & 3)) << 4) + fh * 8;
+  const uint8_t* sc_col = ssc + bcol * 2 * n;
+
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+  auto issue = [&](int ks, uint8_t* sa, uint8_t* sb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(ra, aoff[i], (uint32_t)ks * (BK * 2), sa + (wave + 4 * i) * 1024);
+    dma16(rb, boff, (uint32_t)ks * BK, sb + wave * 1024);
+  };
+  auto compute = [&](int i, const uint8_t* sa0, const uint8_t* sb) {
+    const uint8_t* sa = sa0 + wm * 32 * 128;
+    const float s0 = __uint_as_float((uint32_t)sc_col[2 * i] << 23);
+    const float s1 = __uint_as_float((uint32_t)sc_col[2 * i + 1] << 23);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(sa + aloff[kk]);
+      const uint2 cw = *reinterpret_cast<const uint2*>(sb + bloff[kk]);
+      const float sc = kk < 2 ? s0 : s1;
+      const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.x, sc, false);
+      const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.x, sc, true);
+      const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, sc, false);
+      const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, sc, true);
+      bf16x8 bf;
+      bf[0] = b0[0]; bf[1] = b0[1]; bf[2] = b1[0]; bf[3] = b1[1];
+      bf[4] = b2[0]; bf[5] = b2[1]; bf[6] = b3[0]; bf[7] = b3[1];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+    }
+  };
+  if (n > 0) {
+    issue(ks0, sA0, sB0);
+    issue(ks0 + min(1, n - 1), sA1, sB1);
+    issue(ks0 + min(2, n - 1), sA2, sB2);
+    // the ring runs a multiple of 4 steps; steps past n only keep the wait
+    // and load pattern uniform (no branch around the DMA) and compute nothing
+    auto step = [&](int i, const uint8_t* ca, const uint8_t* cb, uint8_t* na, uint8_t* nb) {
+      __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): steps i + 1, i + 2 stay in flight
+      barrier_lds();                        // all parts of step i landed; stage (i + 3) % 4 is free
+      issue(ks0 + min(i + 3, n - 1), na, nb);
+      if (i < n) compute(i, ca, cb);
+    };
+    for (int i = 0; i < n; i += 4) {
+      step(i, sA0, sB0, sA3, sB3);
+      step(i + 1, sA1, sB1, sA0, sB0);
+      step(i + 2, sA2, sB2, sA1, sB1);
+      step(i + 3, sA3, sB3, sA2, sB2);
+    }
+    wait_vm0();  // no DMA may outlive the workgroup's LDS
+  }
+
+  const int col = n0 + wn * 32 + (lane & 31);
+  if (col < g.N) {
+    float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
+    const int rbase = wm * 32 + (lane >> 5) * 4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = rbase + (e >> 2) * 8 + (e & 3);
+      if (row < g.M) C[(int64_t)row * g.ldc + col] = acc[e];
+    }
+  }
+}
+
 hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t st) {
   dim3 grid((a.N + 63) / 64, 1, a.nsplit), block(256);
   switch (epi) {
@@ -734,6 +872,16 @@ int gemm_pick_split(int M, int N, int K, int max_split) {
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (a.K % BK != 0 || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi != EPI_F32 && a.nsplit != 1) return hipErrorInvalidValue;
+  if (a.Bq) {
+    // MXFP8 weights: the small-M kernel with an fp32 output only
+    const int ksteps = a.K / BK;
+    if (a.M > 64 || epi != EPI_F32 || !a.Bs || a.nsplit < 1 ||
+        (ksteps + a.nsplit - 1) / a.nsplit > MX_MAX_STEPS)
+      return hipErrorInvalidValue;
+    dim3 grid((a.N + 63) / 64, 1, a.nsplit), block(256);
+    hipLaunchKernelGGL((gemm_skinny_fp8_kernel<EPI_F32>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   if (a.M >= kLargeM) return launch_big(a, epi, st);
   if (epi == EPI_QKV) return hipErrorInvalidValue;
   if (a.M <= 64 && (epi == EPI_F32 || epi == EPI_LOGITS)) return launch_skinny(a, epi, st);

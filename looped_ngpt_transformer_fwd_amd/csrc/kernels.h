@@ -53,12 +53,22 @@ struct GemmArgs {
   int F = 0;
   int order = 0;  // large-M tile order, set by the launcher
   QkvEpi qkv;
+  // MXFP8 weights (M <= 64, fp32 output): E4M3 codes [N][K] replace B, block
+  // scale codes [N][K / 32]
+  const uint8_t* Bq = nullptr;
+  const uint8_t* Bs = nullptr;
 };
 
 // Picks a tile configuration and split factor; `max_split` bounds the split
 // (the workspace holds that many partial outputs).
 int gemm_pick_split(int M, int N, int K, int max_split);
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+
+// MXFP8 quantization of a bf16 matrix [rows][cols] (cols a multiple of 32):
+// E4M3 codes [rows][cols], scale codes [rows][cols / 32] and, if deq is not
+// null, the dequantized values as bf16 [rows][cols]. 16-byte aligned rows.
+hipError_t launch_mx_quantize(const uint16_t* w, int64_t rows, int cols, uint8_t* codes,
+                              uint8_t* scales, uint16_t* deq, hipStream_t st);
 
 // Loop counts per sequence for a step whose sequences run different k (the
 // loop-count-per-request property of the looped model). k_rows == nullptr:

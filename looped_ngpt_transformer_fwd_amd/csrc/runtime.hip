@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <array>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -183,6 +184,14 @@ struct ProfScope {
 
 }  // namespace
 
+// MXFP8 copy of one projection matrix [N][K]: E4M3 codes, block scale codes
+// and the dequantized values in bf16 (exact).
+struct MxMat {
+  const uint8_t* q = nullptr;
+  const uint8_t* sc = nullptr;
+  const uint16_t* deq = nullptr;
+};
+
 struct dory_model {
   Shape s;
   Profiler prof;
@@ -191,6 +200,10 @@ struct dory_model {
   const uint16_t* embed;
   const uint16_t* lm_head;
   const float* s_z;
+  // per sublayer: [0] w_qkvg or w_upgate, [1] w_o or w_down
+  std::vector<std::array<MxMat, 2>> mx;
+  bool mx_ready = false;
+  bool use_mx = false;
   ~dory_model() { prof.clear(); }
 };
 
@@ -271,13 +284,33 @@ struct Ctx {
     }                                                                             \
   } while (0)
 
+// The weights a projection reads: the bf16 matrix, or with MXFP8 enabled its
+// quantized copy (E4M3 codes streamed by the small-M kernel, the exact bf16
+// dequantization elsewhere).
+struct WSel {
+  const uint16_t* b = nullptr;
+  const uint8_t* q = nullptr;
+  const uint8_t* sc = nullptr;
+};
+
+WSel wsel(const Ctx& c, int sub, int which, const void* w_bf16) {
+  WSel r;
+  r.b = reinterpret_cast<const uint16_t*>(w_bf16);
+  if (c.m->use_mx) {
+    const MxMat& x = c.m->mx[sub][which];
+    r.b = x.deq;
+    if (c.M <= 64) { r.q = x.q; r.sc = x.sc; }
+  }
+  return r;
+}
+
 // y = A W^T into P (split partials), returns the split used.
-dory_status gemm_f32(Ctx& c, const uint16_t* A, int64_t lda, const void* W, int N, int K,
+dory_status gemm_f32(Ctx& c, const uint16_t* A, int64_t lda, const WSel& W, int N, int K,
                      int64_t M, int* nsplit_out, int cls) {
   PROF(c, cls);
   GemmArgs g;
   g.A = A; g.lda = lda;
-  g.B = reinterpret_cast<const uint16_t*>(W); g.ldb = K;
+  g.B = W.b; g.ldb = K; g.Bq = W.q; g.Bs = W.sc;
   g.M = (int)M; g.N = N; g.K = K;
   g.nsplit = gemm_pick_split((int)M, N, K, max_split_for(M));
   g.C = c.P(); g.ldc = N; g.split_stride = M * N;
@@ -307,7 +340,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     PROF(c, DORY_K_GEMM_QKVG);
     GemmArgs g;
     g.A = c.h16(); g.lda = s.d;
-    g.B = reinterpret_cast<const uint16_t*>(w.w_qkvg); g.ldb = s.d;
+    g.B = wsel(c, i, 0, w.w_qkvg).b; g.ldb = s.d;
     g.M = (int)c.M; g.N = s.nqkvg(); g.K = s.d; g.nsplit = 1;
     g.qkv.qh = c.qh(); g.qkv.kf = c.kf(); g.qkv.vf = c.vf(); g.qkv.gate = c.gate();
     g.qkv.cs = c.rope_cs(full ? 1 : 0); g.qkv.sn = c.rope_sn(full ? 1 : 0);
@@ -315,7 +348,8 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     g.qkv.f_rows = c.L.f_rows; g.qkv.row_off = c.p0 - f_origin;
     HIPCHK(launch_gemm(g, EPI_QKV, c.st));
   } else {
-    st = gemm_f32(c, c.h16(), s.d, w.w_qkvg, s.nqkvg(), s.d, c.M, &ns, DORY_K_GEMM_QKVG);
+    st = gemm_f32(c, c.h16(), s.d, wsel(c, i, 0, w.w_qkvg), s.nqkvg(), s.d, c.M, &ns,
+                  DORY_K_GEMM_QKVG);
     if (st != DORY_OK) return st;
   }
   const int64_t split_stride = c.M * s.nqkvg();
@@ -381,7 +415,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                              c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st, c.rl));
     }
   }
-  st = gemm_f32(c, c.z(), s.dq(), w.w_o, s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O);
+  st = gemm_f32(c, c.z(), s.dq(), wsel(c, i, 1, w.w_o), s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O);
   if (st != DORY_OK) return st;
   PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
@@ -393,24 +427,28 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
   const Shape& s = c.s;
   const dory_sublayer_weights& w = c.m->sub[i];
   const int ns_up = gemm_pick_split((int)c.M, 2 * s.F, s.d, max_split_for(c.M));
-  if (ns_up == 1) {
+  const WSel wug = wsel(c, i, 0, w.w_upgate);
+  // the fused SwiGLU epilogue reads bf16 weights; MXFP8 codes go through
+  // the fp32 partials
+  if (ns_up == 1 && !wug.q) {
     PROF(c, DORY_K_GEMM_UPGATE);
     GemmArgs g;
     g.A = c.h16(); g.lda = s.d;
-    g.B = reinterpret_cast<const uint16_t*>(w.w_upgate); g.ldb = s.d;
+    g.B = wug.b; g.ldb = s.d;
     g.M = (int)c.M; g.N = 2 * s.F; g.K = s.d; g.nsplit = 1;
     g.C16 = c.a(); g.ldc16 = s.F; g.s1 = w.s_u; g.s2 = w.s_v; g.F = s.F;
     HIPCHK(launch_gemm(g, EPI_SWIGLU, c.st));
   } else {
     int ns = 1;
-    dory_status st = gemm_f32(c, c.h16(), s.d, w.w_upgate, 2 * s.F, s.d, c.M, &ns, DORY_K_GEMM_UPGATE);
+    dory_status st = gemm_f32(c, c.h16(), s.d, wug, 2 * s.F, s.d, c.M, &ns, DORY_K_GEMM_UPGATE);
     if (st != DORY_OK) return st;
     PROF(c, DORY_K_OTHER);
     HIPCHK(launch_swiglu_partials(c.P(), ns, c.M * 2 * s.F, (int)c.M, s.F, w.s_u, w.s_v, c.a(),
                                   c.st));
   }
   int ns = 1;
-  dory_status st = gemm_f32(c, c.a(), s.F, w.w_down, s.d, s.F, c.M, &ns, DORY_K_GEMM_DOWN);
+  dory_status st = gemm_f32(c, c.a(), s.F, wsel(c, i, 1, w.w_down), s.d, s.F, c.M, &ns,
+                            DORY_K_GEMM_DOWN);
   if (st != DORY_OK) return st;
   PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
@@ -607,6 +645,109 @@ dory_status dory_model_create(const dory_config* cfg, const dory_weights* w, dor
 }
 
 void dory_model_destroy(dory_model* m) { delete m; }
+
+namespace {
+
+// Rows and columns of the two projection matrices of sublayer kind `kind`.
+void mx_dims(const Shape& s, int kind, int which, int64_t* rows, int* cols) {
+  if (kind == DORY_LAYER_MLP) {
+    *rows = which == 0 ? 2 * (int64_t)s.F : s.d;
+    *cols = which == 0 ? s.d : s.F;
+  } else {
+    *rows = which == 0 ? s.nqkvg() : s.d;
+    *cols = which == 0 ? s.d : s.dq();
+  }
+}
+
+// Byte offsets of the codes, scales and dequantized copy of one matrix
+// within its region, and the region size.
+void mx_region(int64_t rows, int cols, size_t* off_sc, size_t* off_deq, size_t* total) {
+  const size_t n = (size_t)rows * cols;
+  *off_sc = align256(n);
+  *off_deq = *off_sc + align256(n / 32);
+  *total = *off_deq + align256(2 * n);
+}
+
+}  // namespace
+
+size_t dory_mxfp8_bytes(const dory_config* cfg) {
+  Shape s;
+  if (read_shape(cfg, &s) != DORY_OK) return 0;
+  std::vector<int> kinds;
+  if (build_schedule(cfg, s, &kinds) != DORY_OK) return 0;
+  size_t total = 0;
+  for (int i = 0; i < s.nsub(); ++i)
+    for (int which = 0; which < 2; ++which) {
+      int64_t rows; int cols; size_t a, b, t;
+      mx_dims(s, kinds[i], which, &rows, &cols);
+      mx_region(rows, cols, &a, &b, &t);
+      total += t;
+    }
+  return total;
+}
+
+dory_status dory_mxfp8_quantize(const void* w, int64_t rows, int32_t cols, void* codes,
+                                void* scales, void* deq, void* stream) {
+  if (!w || !codes || !scales) return fail(DORY_ERR_ARG, "matrix, codes and scales must be non-NULL");
+  if (rows < 1 || cols < 32 || cols % 32 != 0) return fail(DORY_ERR_ARG, "cols must be a positive multiple of 32");
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(codes) |
+       reinterpret_cast<uintptr_t>(deq)) % 16 != 0)
+    return fail(DORY_ERR_ARG, "matrix, codes and dequantized copy must be 16-byte aligned");
+  hipError_t e = launch_mx_quantize(reinterpret_cast<const uint16_t*>(w), rows, cols,
+                                    reinterpret_cast<uint8_t*>(codes), reinterpret_cast<uint8_t*>(scales),
+                                    reinterpret_cast<uint16_t*>(deq), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DORY_ERR_HIP, hipGetErrorString(e));
+  return DORY_OK;
+}
+
+dory_status dory_model_quantize_mxfp8(dory_model* m, void* buf, size_t bytes, void* stream) {
+  if (!m || !buf) return fail(DORY_ERR_ARG, "model and buffer must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(buf) % 256 != 0) return fail(DORY_ERR_ARG, "buffer must be 256-byte aligned");
+  const Shape& s = m->s;
+  // everything is checked before the first launch
+  size_t need = 0;
+  for (int i = 0; i < s.nsub(); ++i)
+    for (int which = 0; which < 2; ++which) {
+      int64_t rows; int cols; size_t o_sc, o_deq, t;
+      mx_dims(s, m->kinds[i], which, &rows, &cols);
+      mx_region(rows, cols, &o_sc, &o_deq, &t);
+      if (cols % 64 != 0) return fail(DORY_ERR_UNSUPPORTED, "MXFP8 needs reduction widths that are multiples of 64");
+      const dory_sublayer_weights& w = m->sub[i];
+      const void* src = m->kinds[i] == DORY_LAYER_MLP ? (which == 0 ? w.w_upgate : w.w_down)
+                                                       : (which == 0 ? w.w_qkvg : w.w_o);
+      if (reinterpret_cast<uintptr_t>(src) % 16 != 0)
+        return fail(DORY_ERR_ARG, "weight matrices must be 16-byte aligned");
+      need += t;
+    }
+  if (need > bytes) return fail(DORY_ERR_CAPACITY, "buffer smaller than dory_mxfp8_bytes()");
+  std::vector<std::array<MxMat, 2>> mx(s.nsub());
+  size_t off = 0;
+  for (int i = 0; i < s.nsub(); ++i)
+    for (int which = 0; which < 2; ++which) {
+      int64_t rows; int cols; size_t o_sc, o_deq, t;
+      mx_dims(s, m->kinds[i], which, &rows, &cols);
+      mx_region(rows, cols, &o_sc, &o_deq, &t);
+      const dory_sublayer_weights& w = m->sub[i];
+      const void* src = m->kinds[i] == DORY_LAYER_MLP ? (which == 0 ? w.w_upgate : w.w_down)
+                                                       : (which == 0 ? w.w_qkvg : w.w_o);
+      uint8_t* base = reinterpret_cast<uint8_t*>(buf) + off;
+      dory_status st = dory_mxfp8_quantize(src, rows, cols, base, base + o_sc, base + o_deq, stream);
+      if (st != DORY_OK) return st;
+      mx[i][which] = MxMat{base, base + o_sc, reinterpret_cast<const uint16_t*>(base + o_deq)};
+      off += t;
+    }
+  m->mx = mx;
+  m->mx_ready = true;
+  m->use_mx = true;
+  return DORY_OK;
+}
+
+dory_status dory_model_use_mxfp8(dory_model* m, int32_t on) {
+  if (!m) return fail(DORY_ERR_ARG, "model is NULL");
+  if (on && !m->mx_ready) return fail(DORY_ERR_ARG, "no MXFP8 copy: call dory_model_quantize_mxfp8 first");
+  m->use_mx = on != 0;
+  return DORY_OK;
+}
 
 size_t dory_kv_bytes(const dory_config* cfg, dory_cache_mode mode, int32_t k_max, int32_t batch,
                      int64_t max_seq) {

@@ -55,6 +55,22 @@ def workspace_bytes(shape, batch, tokens):
     return C.dory_workspace_bytes(make_config(shape), batch, tokens)
 
 
+def mxfp8_bytes(shape):
+    return C.dory_mxfp8_bytes(make_config(shape))
+
+
+def mxfp8_quantize(w):
+    """MXFP8 quantization of a bf16 device matrix [rows, cols]: (codes uint8
+    [rows, cols], scale codes uint8 [rows, cols / 32], dequantized bf16)."""
+    rows, cols = w.shape
+    codes = torch.empty(rows, cols, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=w.device)
+    deq = torch.empty(rows, cols, dtype=torch.bfloat16, device=w.device)
+    C.check(C.dory_mxfp8_quantize(_ptr(w), rows, cols, _ptr(codes), _ptr(scales), _ptr(deq),
+                                  _stream()), "dory_mxfp8_quantize")
+    return codes, scales, deq
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -106,6 +122,17 @@ class Model:
         except Exception:  # interpreter shutdown
             pass
         self.handle = None
+
+    def quantize_mxfp8(self, device="cuda"):
+        """Quantizes the projection matrices to MXFP8 (weight-only) into a
+        buffer owned by this object and switches the model to them."""
+        n = mxfp8_bytes(self.shape)
+        self.mx_buffer = torch.empty(n, dtype=torch.uint8, device=device)
+        C.check(C.dory_model_quantize_mxfp8(self.handle, _ptr(self.mx_buffer), n, _stream()),
+                "dory_model_quantize_mxfp8")
+
+    def use_mxfp8(self, on):
+        C.check(C.dory_model_use_mxfp8(self.handle, 1 if on else 0), "dory_model_use_mxfp8")
 
     def profile_begin(self, max_launches=100000):
         C.check(C.dory_profile_begin(self.handle, max_launches), "dory_profile_begin")

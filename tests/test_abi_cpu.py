@@ -207,3 +207,39 @@ def test_no_lm_head_rejects_logits_request():
 def test_status_strings():
     for s in range(8):
         assert C.dory_status_string(s)
+
+
+def _mx_region(rows, cols):
+    a = lambda x: (x + 255) // 256 * 256
+    n = rows * cols
+    return a(n) + a(n // 32) + a(2 * n)
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, synth.MID128, synth.FULL])
+def test_mxfp8_bytes_closed_form(shape):
+    # per projection matrix: E4M3 codes (1 B per weight), scale codes (1 B per
+    # 32 weights) and the bf16 dequantized copy, each padded to 256 bytes
+    want = 0
+    for kind in ref.layer_kinds(shape):
+        if kind == "mlp":
+            want += _mx_region(2 * shape.d_ff, shape.d_model) + _mx_region(shape.d_model, shape.d_ff)
+        else:
+            nqkvg = 2 * shape.d_q + 2 * shape.d_kv
+            want += _mx_region(nqkvg, shape.d_model) + _mx_region(shape.d_model, shape.d_q)
+    assert M.mxfp8_bytes(shape) == want
+
+
+def test_mxfp8_argument_validation_enqueues_nothing():
+    m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
+    P = ctypes.c_void_p
+    assert C.dory_mxfp8_quantize(P(0x10000), 4, 48, P(0x20000), P(0x30000), None, None) == \
+        C.DORY_ERR_ARG                                    # cols not a multiple of 32
+    assert C.dory_mxfp8_quantize(P(0x10008), 4, 64, P(0x20000), P(0x30000), None, None) == \
+        C.DORY_ERR_ARG                                    # misaligned matrix
+    assert C.dory_mxfp8_quantize(None, 4, 64, P(0x20000), P(0x30000), None, None) == C.DORY_ERR_ARG
+    assert C.dory_model_use_mxfp8(m.handle, 1) == C.DORY_ERR_ARG   # nothing quantized yet
+    assert C.dory_model_use_mxfp8(m.handle, 0) == C.DORY_OK
+    n = M.mxfp8_bytes(synth.TINY)
+    assert C.dory_model_quantize_mxfp8(m.handle, P(0x100000), n - 1, None) == C.DORY_ERR_CAPACITY
+    assert C.dory_model_quantize_mxfp8(m.handle, P(0x100010), n, None) == C.DORY_ERR_ARG
+    assert C.dory_model_use_mxfp8(m.handle, 1) == C.DORY_ERR_ARG
