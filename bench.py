@@ -150,7 +150,29 @@ def time_steps(fn, steps):
     return time.perf_counter() - t0
 
 
-def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4):
+def decode_mxfp8(gm, shape, B=64, steps=4):
+    """Decode tokens/s with MXFP8 weights (W8A16) against bf16: at the same
+    32768-token context (last-loop, k = 1, 2, 4) and at a 2048-token context
+    (k = 4), where the weight stream is a larger share of a step. The model
+    is switched back to bf16 afterwards."""
+    out = {}
+    short = decode_table(gm, shape, (4,), ("last_loop",), B=B, ctx=2048, steps=steps)
+    out["bf16_ctx2048_last_loop_k4"] = short["last_loop_k4"]
+    gm.quantize_mxfp8()
+    try:
+        t = decode_table(gm, shape, (1, 2, 4), ("last_loop",), B=B, steps=steps, mixed=False)
+        for k in (1, 2, 4):
+            out[f"mxfp8_last_loop_k{k}"] = t[f"last_loop_k{k}"]
+        short = decode_table(gm, shape, (4,), ("last_loop",), B=B, ctx=2048, steps=steps)
+        out["mxfp8_ctx2048_last_loop_k4"] = short["last_loop_k4"]
+    finally:
+        gm.use_mxfp8(False)
+        del gm.mx_buffer
+        torch.cuda.empty_cache()
+    return out
+
+
+def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4, mixed=True):
     """Decode tokens/s at a fixed position with `ctx` cached tokens whose K/V
     are synthesized at random (the cost of a step depends on the context
     length, not on the cached values)."""
@@ -177,7 +199,7 @@ def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4):
             out[f"{mode}_k{k}_kv_gb"] = round(kv.buffer.numel() / 1e9, 2)
             del kv, buf
             torch.cuda.empty_cache()
-    if "last_loop" in modes and max(ks) >= 4:
+    if mixed and "last_loop" in modes and max(ks) >= 4:
         # one batch whose sequences run different loop counts, 4:1:1:1 over
         # k = 1, 2, 3, 4 (36 / 9 / 9 / 10 of 64 sequences)
         k_rows = [1] * 36 + [2] * 9 + [3] * 9 + [4] * 10
@@ -284,8 +306,9 @@ def main():
     weights = gpu_weights(shape, kinds)
     gm = M.Model(shape, weights)
     if args.decode_only:
-        print(json.dumps({"decode_tok_s": decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))}),
-              flush=True)
+        d = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
+        d.update(decode_mxfp8(gm, shape))
+        print(json.dumps({"decode_tok_s": d}), flush=True)
         return
     ws = gm.workspace(B, T)
     g = torch.Generator(device="cuda")
@@ -355,8 +378,11 @@ def main():
         del kv, ws
         torch.cuda.empty_cache()
         result["decode_tok_s"] = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
+        result["decode_tok_s"].update(decode_mxfp8(gm, shape))
         result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each; "
-                                   "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences")
+                                   "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences; "
+                                   "mxfp8: projection weights in MXFP8 (W8A16), embedding and LM head "
+                                   "bf16; ctx2048: 2048 cached tokens")
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(k)
     print(json.dumps(result), flush=True)
