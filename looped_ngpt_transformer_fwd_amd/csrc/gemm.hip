@@ -461,6 +461,25 @@ gemm_big_kernel(GemmArgs g) {
     float sq[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) sq[j] = kind <= 1 ? q.s_qk[16 * j + dl] : 0.f;
+    // The RoPE table rows of the tile's 256 token rows (cos in st0/st1, sin
+    // in st2/st3: 256 B per row) go to LDS before any store, and s_qk
+    // becomes plain register values: a global load consumed between the
+    // stores would make each wait for all earlier stores (one counter).
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(sq[j]));
+    __syncthreads();  // every wave is done with the stages
+    if (n0 < dq + dkv) {
+      for (int idx = tid; idx < 256 * 16; idx += 64 * NW) {
+        const int r = idx >> 4, c = idx & 15;
+        const int row = m0 + r;
+        const int t = row < g.M ? row % q.T : 0;
+        const float4 vc = reinterpret_cast<const float4*>(q.cs + (int64_t)t * 64)[c];
+        const float4 vs = reinterpret_cast<const float4*>(q.sn + (int64_t)t * 64)[c];
+        *reinterpret_cast<float4*>((r < 128 ? st0 : st1) + (r & 127) * 256 + c * 16) = vc;
+        *reinterpret_cast<float4*>((r < 128 ? st2 : st3) + (r & 127) * 256 + c * 16) = vs;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -468,16 +487,18 @@ gemm_big_kernel(GemmArgs g) {
         const int row = rbase + i * 16 + e;
         const bool ok = row < g.M;
         const int b = row / q.T, t = row - b * q.T;
+        const int rl = row - m0;  // row within the tile
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = acc[i][j][e];
         if (kind <= 1) {
-          const int tr = ok ? t : 0;
+          const float* lcs = reinterpret_cast<const float*>((rl < 128 ? st0 : st1) + (rl & 127) * 256);
+          const float* lsn = reinterpret_cast<const float*>((rl < 128 ? st2 : st3) + (rl & 127) * 256);
           float r[8];
           float ss = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float c = q.cs[tr * 64 + 16 * j + dl], sn = q.sn[tr * 64 + 16 * j + dl];
+            const float c = lcs[16 * j + dl], sn = lsn[16 * j + dl];
             r[j] = x[j] * c - x[j + 4] * sn;
             r[j + 4] = x[j + 4] * c + x[j] * sn;
             ss += r[j] * r[j] + r[j + 4] * r[j + 4];
@@ -524,28 +545,64 @@ gemm_big_kernel(GemmArgs g) {
     }
   } else {
     // 64-column groups: blocks 0, 1 are up, blocks 2, 3 the gate of the same
-    // 32 features (see the B-row interleave of the DMA sources)
+    // 32 features (see the B-row interleave of the DMA sources). The scales
+    // are loaded and every output computed before the first store: a load
+    // consumed between stores makes the compiler wait for all earlier stores
+    // (one vector-memory counter), which serialized the epilogue.
+    constexpr int NJP = FN / 4;
+    float su[NJP][2], sv[NJP][2];
 #pragma unroll
-    for (int jp = 0; jp < FN / 4; ++jp)
+    for (int jp = 0; jp < NJP; ++jp)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int v = cbase + jp * 64 + h * 16;
-        if (v >= g.N) continue;
-        const int f = ((v >> 6) << 5) | (v & 31);
-        const float su = g.s1[f], sv = g.s2[f];
+        const int f = min(((v >> 6) << 5) | (v & 31), g.F - 1);
+        su[jp][h] = g.s1[f];
+        sv[jp][h] = g.s2[f];
+      }
+    // the loaded scales become plain register values here (one wait for
+    // the loads), so that the guarded stores below depend on no load
+#pragma unroll
+    for (int jp = 0; jp < NJP; ++jp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(su[jp][h]), "+v"(sv[jp][h]));
+    // The wave's outputs (64 rows x 64 features, bf16) are staged through
+    // LDS, free after the main loop, and written as whole 128-byte row
+    // pieces, 16 bytes per lane (in the accumulator layout a lane's values
+    // of one row are 16 features apart: 2-byte stores of 32-byte pieces).
+    static_assert(NJP * 32 == 64 && BIG_WM == 64, "one 64-feature group per wave");
+    constexpr int SROW = 64 * 2 + 16;  // padded LDS row of the staging tile
+    __syncthreads();                   // every wave is done with the stages
+    uint8_t* stg = wave < 3 ? st0 + wave * 64 * SROW
+                 : wave < 6 ? st1 + (wave - 3) * 64 * SROW : st2 + (wave - 6) * 64 * SROW;
+#pragma unroll
+    for (int jp = 0; jp < NJP; ++jp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int row = rbase + i * 16 + e;
-            if (row < g.M) {
-              const float up = acc[i][4 * jp + h][e] * su;
-              const float gt = acc[i][4 * jp + 2 + h][e] * sv;
-              const float act = gt / (1.f + __expf(-gt));
-              g.C16[(int64_t)row * g.ldc16 + f] = f2bf(act * up);
-            }
+            const float up = acc[i][4 * jp + h][e] * su[jp][h];
+            const float gt = acc[i][4 * jp + 2 + h][e] * sv[jp][h];
+            const float act = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt));
+            const int r = (lane >> 4) * 4 + i * 16 + e;
+            const int lf = jp * 32 + h * 16 + (lane & 15);
+            *reinterpret_cast<uint16_t*>(stg + r * SROW + lf * 2) = f2bf(act * up);
           }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int fbase = (n0 + wn * BIG_WN) / 2;  // first feature of the wave's group
+    if (fbase < g.F) {
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int r = pass * 8 + (lane >> 3);
+        const int row = m0 + wm * BIG_WM + r;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * SROW + (lane & 7) * 16);
+        if (row < g.M)
+          *reinterpret_cast<uint4*>(g.C16 + (int64_t)row * g.ldc16 + fbase + (lane & 7) * 8) = v;
       }
+    }
   }
 }
 
