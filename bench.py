@@ -95,8 +95,9 @@ def class_work(shape, M):
         "gemm_o": (2.0 * M * d * dq, "flop", "mfma"),
         "gemm_upgate": (2.0 * M * 2 * F * d, "flop", "mfma"),
         "gemm_down": (2.0 * M * d * F, "flop", "mfma"),
-        # read h (fp32) and y (fp32), write h (fp32) and its bf16 copy
-        "update": (float(M) * d * (4 + 4 + 4 + 2), "byte", "hbm"),
+        # read h (fp32) and y (bf16: the large-M projections write their
+        # output once in bf16), write h (fp32) and its bf16 copy
+        "update": (float(M) * d * (4 + 2 + 4 + 2), "byte", "hbm"),
     }
 
 

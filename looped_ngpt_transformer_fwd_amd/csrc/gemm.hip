@@ -543,6 +543,46 @@ gemm_big_kernel(GemmArgs g) {
           if (row < g.M) C[(int64_t)row * g.ldc + col] = acc[i][j][e] * sc;
         }
     }
+  } else if (EPI == EPI_BF16) {
+    // The wave's 64 x 128 outputs, rounded to bf16, go through LDS (16 KB
+    // per wave, 16-byte chunks XOR-swizzled by row) and leave as 16-byte
+    // pieces of 256-byte rows.
+    __syncthreads();  // every wave is done with the stages
+    uint8_t* stg = (wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3;
+    stg += (wave & 1) * 16384;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = (lane >> 4) * 4 + i * 16 + e;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = j * 16 + (lane & 15);
+          *reinterpret_cast<uint16_t*>(stg + r * 256 + (((col >> 3) ^ (r & 15)) << 4) + (col & 7) * 2) =
+              f2bf(acc[i][j][e]);
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int c0 = n0 + wn * BIG_WN;
+    const bool vec_ok = g.ldc16 % 8 == 0 && (reinterpret_cast<uintptr_t>(g.C16) & 15) == 0;
+#pragma unroll
+    for (int pass = 0; pass < 16; ++pass) {
+      const int r = pass * 4 + (lane >> 4), c = lane & 15;
+      const int row = m0 + wm * BIG_WM + r;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
+      uint16_t* dst = g.C16 + (int64_t)row * g.ldc16 + c0 + c * 8;
+      if (row < g.M) {
+        if (vec_ok && c0 + c * 8 + 8 <= g.N) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint16_t* ve = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (c0 + c * 8 + k < g.N) dst[k] = ve[k];
+        }
+      }
+    }
   } else {
     // 64-column groups: blocks 0, 1 are up, blocks 2, 3 the gate of the same
     // 32 features (see the B-row interleave of the DMA sources). The scales
@@ -633,6 +673,7 @@ hipError_t launch_big(const GemmArgs& a0, int epi, hipStream_t st) {
     case EPI_SWIGLU: hipLaunchKernelGGL((gemm_big_kernel<EPI_SWIGLU, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
     case EPI_LOGITS: hipLaunchKernelGGL((gemm_big_kernel<EPI_LOGITS, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
     case EPI_QKV: hipLaunchKernelGGL((gemm_big_kernel<EPI_QKV, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
+    case EPI_BF16: hipLaunchKernelGGL((gemm_big_kernel<EPI_BF16, BIG_WAVES_M, BIG_WAVES_N>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -940,7 +981,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
     return hipGetLastError();
   }
   if (a.M >= kLargeM) return launch_big(a, epi, st);
-  if (epi == EPI_QKV) return hipErrorInvalidValue;
+  if (epi == EPI_QKV || epi == EPI_BF16) return hipErrorInvalidValue;
   if (a.M <= 64 && (epi == EPI_F32 || epi == EPI_LOGITS)) return launch_skinny(a, epi, st);
   return launch_cfg<64, 128, 32, 64>(a, epi, st);
 }

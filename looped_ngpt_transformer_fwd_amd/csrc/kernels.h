@@ -19,6 +19,7 @@ enum GemmEpi {
   EPI_QKV = 3,     // fused query/key transform (large-M path, head_dim 128):
                    // columns of B = w_qkvg; writes q_hat, fresh K, fresh V^T
                    // and sigma(gate) as qk_prep does (see QkvEpi)
+  EPI_BF16 = 4,    // C16[m, n] = bf16(acc) (ldc16); large-M path only, no split
 };
 
 // Destinations of the fused q/k/v/gate epilogue. Row m = b * T + t is the
@@ -93,7 +94,7 @@ hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M,
 hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
                          int64_t split_stride, int64_t ldy, const float* alpha, int M, int d,
                          const float* x, float* state_out, float* copy_out, hipStream_t st,
-                         RowLoops rl = RowLoops());
+                         RowLoops rl = RowLoops(), bool y_bf16 = false);
 
 // Loop boundary h <- N(h + x) (also writes the bf16 shadow).
 hipError_t launch_boundary(float* h32, uint16_t* h16, const float* x, int M, int d,

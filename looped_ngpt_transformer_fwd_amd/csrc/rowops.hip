@@ -31,7 +31,9 @@ embed_kernel(const int32_t* tok, const uint16_t* E, int vocab, int d, float* h32
 }
 
 // h <- N(h + alpha (N(y) - h)); optional aux copy of the result, optional
-// boundary h <- N(result + x).
+// boundary h <- N(result + x). Y16: y is one bf16 matrix (the large-M
+// projections' output), else nsplit fp32 split-K partials.
+template <bool Y16>
 __global__ void __launch_bounds__(NT_ROW)
 update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss, int64_t ldy,
               const float* alpha, int d, const float* x, float* aux, RowLoops rl) {
@@ -50,6 +52,14 @@ update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss,
     const int c = threadIdx.x + i * NT_ROW;
     if (c < nv) {
       hv[i] = reinterpret_cast<const float4*>(h32 + (int64_t)m * d)[c];
+      if (Y16) {
+        const ushort4 t = reinterpret_cast<const ushort4*>(reinterpret_cast<const uint16_t*>(y) +
+                                                           (int64_t)m * ldy)[c];
+        const float4 acc = make_float4(bf2f(t.x), bf2f(t.y), bf2f(t.z), bf2f(t.w));
+        yv[i] = acc;
+        syy += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+        continue;
+      }
       // split-K partials: four independent accumulators keep loads in flight
       float4 a4[4];
 #pragma unroll
@@ -341,12 +351,18 @@ hipError_t launch_embed(const int32_t* tok, const uint16_t* E, int vocab, int M,
 hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
                          int64_t split_stride, int64_t ldy, const float* alpha, int M, int d,
                          const float* x, float* state_out, float* copy_out, hipStream_t st,
-                         RowLoops rl) {
+                         RowLoops rl, bool y_bf16) {
   if (d % 4 != 0 || d > 4 * MAXV * NT_ROW) return hipErrorInvalidValue;
   float* aux = state_out ? state_out : copy_out;
   if (state_out && copy_out) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(update_kernel, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
-                     split_stride, ldy, alpha, d, x, aux, rl);
+  if (y_bf16) {
+    if (nsplit != 1 || ldy % 4 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(update_kernel<true>, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
+                       split_stride, ldy, alpha, d, x, aux, rl);
+  } else {
+    hipLaunchKernelGGL(update_kernel<false>, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
+                       split_stride, ldy, alpha, d, x, aux, rl);
+  }
   return hipGetLastError();
 }
 

@@ -304,17 +304,27 @@ WSel wsel(const Ctx& c, int sub, int which, const void* w_bf16) {
   return r;
 }
 
-// y = A W^T into P (split partials), returns the split used.
+// y = A W^T into P (split partials), returns the split used. With y16 given
+// (a consumer that reads bf16), large-M calls write y once in bf16 instead
+// (half the bytes of the fp32 output, which is written in one burst at the
+// end of every round of tiles); *y16 tells which form was written.
 dory_status gemm_f32(Ctx& c, const uint16_t* A, int64_t lda, const WSel& W, int N, int K,
-                     int64_t M, int* nsplit_out, int cls) {
+                     int64_t M, int* nsplit_out, int cls, bool* y16 = nullptr) {
   PROF(c, cls);
   GemmArgs g;
   g.A = A; g.lda = lda;
   g.B = W.b; g.ldb = K; g.Bq = W.q; g.Bs = W.sc;
   g.M = (int)M; g.N = N; g.K = K;
   g.nsplit = gemm_pick_split((int)M, N, K, max_split_for(M));
-  g.C = c.P(); g.ldc = N; g.split_stride = M * N;
-  HIPCHK(launch_gemm(g, EPI_F32, c.st));
+  const bool half = y16 && M >= kLargeM && !W.q && g.nsplit == 1;
+  if (y16) *y16 = half;
+  if (half) {
+    g.C16 = reinterpret_cast<uint16_t*>(c.P()); g.ldc16 = N;
+    HIPCHK(launch_gemm(g, EPI_BF16, c.st));
+  } else {
+    g.C = c.P(); g.ldc = N; g.split_stride = M * N;
+    HIPCHK(launch_gemm(g, EPI_F32, c.st));
+  }
   *nsplit_out = g.nsplit;
   return DORY_OK;
 }
@@ -415,11 +425,12 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                              c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st, c.rl));
     }
   }
-  st = gemm_f32(c, c.z(), s.dq(), wsel(c, i, 1, w.w_o), s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O);
+  bool y16 = false;
+  st = gemm_f32(c, c.z(), s.dq(), wsel(c, i, 1, w.w_o), s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O, &y16);
   if (st != DORY_OK) return st;
   PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
-                       uo.aux, nullptr, c.st, c.rl));
+                       uo.aux, nullptr, c.st, c.rl, y16));
   return DORY_OK;
 }
 
@@ -447,12 +458,13 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
                                   c.st));
   }
   int ns = 1;
+  bool y16 = false;
   dory_status st = gemm_f32(c, c.a(), s.F, wsel(c, i, 1, w.w_down), s.d, s.F, c.M, &ns,
-                            DORY_K_GEMM_DOWN);
+                            DORY_K_GEMM_DOWN, &y16);
   if (st != DORY_OK) return st;
   PROF(c, DORY_K_UPDATE);
   HIPCHK(launch_update(c.h32(), c.h16(), c.P(), ns, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
-                       uo.aux, nullptr, c.st, c.rl));
+                       uo.aux, nullptr, c.st, c.rl, y16));
   return DORY_OK;
 }
 
