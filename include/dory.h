@@ -170,7 +170,11 @@ dory_status dory_kv_slot(const dory_kv* kv, int32_t sublayer, int32_t loop, dory
  * Chunked prefill is a sequence of such calls.
  *   tokens: device int32 [B, T]; ids outside [0, V) produce NaN outputs.
  *   k >= 1: loop count (section Training with Loops). Under per-loop
- *     caching k <= k_max and every step on one cache uses the same k.
+ *     caching k <= k_max, and every earlier position must hold loop-k
+ *     entries (written by a step with at least k loops, or declared by
+ *     dory_kv_set_length): a step may use fewer loops than earlier ones,
+ *     and its positions then hold only loops 1 .. k (DORY_ERR_MODE
+ *     otherwise).
  *   mode: must equal the mode the cache was bound with.
  *   ws / ws_bytes: device workspace of at least dory_workspace_bytes(cfg, B, T).
  *   logits: device fp32 [B, V], logits of the last position, or NULL.
@@ -217,12 +221,41 @@ dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tok
                                   size_t ws_bytes, float* logits, int32_t* next, float* hidden,
                                   float* states, void* stream);
 
-/* Declares that the first `length` positions of every sequence in the bound
- * buffer already hold valid K/V (for example a cache restored by the caller),
- * so that the next step starts at that position. 0 <= length <= max_seq;
- * under per-loop caching the loop count of later steps is not constrained
- * by earlier ones after this call. */
+/* Sets the number of cached positions of every sequence; the next step
+ * starts at that position. 0 <= length <= max_seq. Shortening forgets the
+ * positions past `length` (for example rejected speculative tokens);
+ * lengthening declares that the new positions already hold valid K/V of
+ * every loop (for example a cache restored by the caller). */
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length);
+
+/* One round of self-speculative greedy decoding (section Self-Speculative
+ * Decoding: the same checkpoint drafts at a shallow loop count and verifies
+ * at a deeper one in one batched pass over the drafted tokens). From the
+ * tokens `last` (device int32 [B], not yet in the cache) at position
+ * L = dory_kv_length(kv): gamma draft decode steps at k_draft, greedy; the
+ * cache is rolled back to L; one verification step over the gamma + 1
+ * tokens (last and the drafts) at k_verify, with the greedy token after
+ * every position written to out (device int32 [gamma + 1][B]). Draft j is
+ * accepted while it equals the verifier's token after position L + j - 1;
+ * the batch keeps the n drafts accepted by every sequence (n_accepted, host
+ * int32), the cache keeps positions up to L + n, and out rows 0 .. n are the
+ * next n + 1 tokens of every sequence (row n, the verifier's own token after
+ * the last accepted position, feeds the next round). With greedy selection
+ * the emitted tokens are those of plain decoding at k_verify. Rejection
+ * sampling for sampled decoding, and reuse of the drafts' input-block and
+ * loop-1 activations in the verification pass, are not implemented: the
+ * verification recomputes them (with per-loop caching it rewrites the same
+ * input-block and loop-1 entries). Per-loop caches only (as on the pages;
+ * DORY_ERR_MODE otherwise): under last-loop caching the verification chunk
+ * reads its own tokens' current-loop entries where token-by-token decoding
+ * reads final-loop ones. scratch: device int32 of 2 B (gamma + 1)
+ * elements. ws: at least dory_workspace_bytes(cfg, B, gamma + 1).
+ * 1 <= k_draft <= k_verify <= k_max; needs an LM head. Synchronous: returns
+ * after the round (n_accepted is read back). */
+dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, int32_t B,
+                               int32_t gamma, int32_t k_draft, int32_t k_verify, dory_cache_mode mode,
+                               void* ws, size_t ws_bytes, int32_t* scratch, int32_t* out,
+                               int32_t* n_accepted, void* stream);
 
 /* ---- MXFP8 weights (W8A16) ------------------------------------------------
  * Section Quantization (Post-Training Quantization): an MXFP8 checkpoint made

@@ -86,6 +86,8 @@ SIGNATURES = {
     "dory_kv_set_length": (_I32, [_P, _I64]),
     "dory_profile_begin": (_I32, [_P, _I32]),
     "dory_profile_end": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
+    "dory_selfspec_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P,
+                                  ctypes.POINTER(_I32), _P]),
     "dory_mxfp8_quantize": (_I32, [_P, _I64, _I32, _P, _P, _P, _P]),
     "dory_mxfp8_bytes": (_SZ, [ctypes.POINTER(dory_config)]),
     "dory_model_quantize_mxfp8": (_I32, [_P, _P, _SZ, _P]),
@@ -198,6 +200,12 @@ def dory_debug_mask(window, L, T, out, stream):
 
 def dory_kv_set_length(kv, length):
     return lib().dory_kv_set_length(kv, length)
+
+
+def dory_selfspec_step(m, kv, last, B, gamma, k_draft, k_verify, mode, ws, ws_bytes, scratch, out,
+                       n_accepted, stream):
+    return lib().dory_selfspec_step(m, kv, last, B, gamma, k_draft, k_verify, mode, ws, ws_bytes,
+                                    scratch, out, ctypes.byref(n_accepted), stream)
 
 
 def dory_mxfp8_quantize(w, rows, cols, codes, scales, deq, stream):

@@ -96,6 +96,9 @@ hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
                          const float* x, float* state_out, float* copy_out, hipStream_t st,
                          RowLoops rl = RowLoops(), bool y_bf16 = false);
 
+// dst [cols][rows] = transpose of src [rows][cols] (int32).
+hipError_t launch_transpose_i32(const int32_t* src, int rows, int cols, int32_t* dst, hipStream_t st);
+
 // Loop boundary h <- N(h + x) (also writes the bf16 shadow).
 hipError_t launch_boundary(float* h32, uint16_t* h16, const float* x, int M, int d,
                            hipStream_t st);

@@ -366,6 +366,22 @@ hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
   return hipGetLastError();
 }
 
+namespace {
+__global__ void transpose_i32_kernel(const int32_t* src, int rows, int cols, int32_t* dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * cols) return;
+  const int r = i / cols, c = i - r * cols;
+  dst[(int64_t)c * rows + r] = src[i];
+}
+}  // namespace
+
+hipError_t launch_transpose_i32(const int32_t* src, int rows, int cols, int32_t* dst, hipStream_t st) {
+  if (rows < 1 || cols < 1) return hipErrorInvalidValue;
+  const int n = rows * cols;
+  hipLaunchKernelGGL(transpose_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, src, rows, cols, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_boundary(float* h32, uint16_t* h16, const float* x, int M, int d,
                            hipStream_t st) {
   if (d % 4 != 0 || d > 4 * MAXV * NT_ROW) return hipErrorInvalidValue;

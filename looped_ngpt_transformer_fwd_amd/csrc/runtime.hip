@@ -215,7 +215,9 @@ struct dory_kv {
   int k_max, batch;
   int64_t max_seq;
   int64_t len;
-  int k_used;
+  // per-loop caching: filled[j] (j = 1 .. k_max) = number of leading
+  // positions whose loop-j entries are written (non-increasing in j)
+  std::vector<int64_t> filled;
   bool invalid;
   // per sublayer: offset of slot 0 (or SIZE_MAX for MLP), rows and ring
   std::vector<size_t> off;
@@ -473,8 +475,10 @@ dory_status run_sublayer(Ctx& c, int i, int slot, bool write, const UpdateOpts& 
   return attention_sublayer(c, i, slot, write, uo);
 }
 
+// next_all (device int32 [T][B], or null): greedy token after every position
+// of the step, one LM-head call of B rows per position.
 dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_t* next,
-                     float* hidden, float* states) {
+                     float* hidden, float* states, int32_t* next_all = nullptr) {
   const Shape& s = c.s;
   const int64_t Md = c.M * s.d;
   const bool per_loop = c.kv->mode == DORY_CACHE_PER_LOOP;
@@ -548,13 +552,28 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
       HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
     }
   }
+  if (next_all) {
+    for (int t = 0; t < c.T; ++t) {
+      GemmArgs g;
+      g.A = c.h16() + (int64_t)t * s.d; g.lda = (int64_t)c.T * s.d;
+      g.B = c.m->lm_head; g.ldb = s.d;
+      g.M = c.B; g.N = s.V; g.K = s.d; g.nsplit = 1;
+      g.C = c.logits_scratch(); g.ldc = s.V; g.s1 = c.m->s_z;
+      {
+        PROF(c, DORY_K_GEMM_LM);
+        HIPCHK(launch_gemm(g, EPI_LOGITS, c.st));
+      }
+      PROF(c, DORY_K_OTHER);
+      HIPCHK(launch_argmax(c.logits_scratch(), c.B, s.V, next_all + (int64_t)t * c.B, c.st));
+    }
+  }
   return DORY_OK;
 }
 
 dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
                         int32_t k, const int32_t* k_rows, dory_cache_mode mode, void* ws,
                         size_t ws_bytes, float* logits, int32_t* next, float* hidden,
-                        float* states, void* stream) {
+                        float* states, void* stream, int32_t* next_all = nullptr) {
   if (!m || !kv || !tokens) return fail(DORY_ERR_ARG, "model, cache and tokens must be non-NULL");
   if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
   if (B <= 0 || T <= 0) return fail(DORY_ERR_ARG, "B and T must be >= 1");
@@ -574,8 +593,9 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
   if (mode != kv->mode) return fail(DORY_ERR_MODE, "cache mode differs from the bound mode");
   if (mode == DORY_CACHE_PER_LOOP) {
     if (k > kv->k_max) return fail(DORY_ERR_MODE, "per-loop cache: k exceeds k_max");
-    if (kv->k_used != 0 && kv->k_used != k)
-      return fail(DORY_ERR_MODE, "per-loop cache: k differs from earlier steps");
+    // a loop-j query reads the loop-j entries of every earlier position
+    if (kv->filled[k] < kv->len)
+      return fail(DORY_ERR_MODE, "per-loop cache: earlier positions lack loop-k entries");
   }
   if (B > kv->batch) return fail(DORY_ERR_CAPACITY, "B exceeds the bound batch");
   if (B < kv->batch) return fail(DORY_ERR_ARG, "B must equal the bound batch");
@@ -598,13 +618,14 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
     if (hipMemcpyAsync(c.krows(), k_rows, (size_t)B * 4, hipMemcpyHostToDevice, c.st) != hipSuccess)
       return fail(DORY_ERR_HIP, "copy of the per-sequence loop counts failed");
   }
-  dory_status st = run_step(c, tokens, k, logits, next, hidden, states);
+  dory_status st = run_step(c, tokens, k, logits, next, hidden, states, next_all);
   if (st != DORY_OK) {
     if (st == DORY_ERR_HIP) kv->invalid = true;
     return st;
   }
   kv->len += T;
-  if (mode == DORY_CACHE_PER_LOOP) kv->k_used = k;
+  if (mode == DORY_CACHE_PER_LOOP)
+    for (int j = 1; j <= k; ++j) kv->filled[j] = kv->len;
   return DORY_OK;
 }
 
@@ -798,7 +819,8 @@ dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dor
   dory_kv* kv = new dory_kv();
   kv->m = m; kv->base = reinterpret_cast<uint8_t*>(kv_dev); kv->bytes = kv_bytes;
   kv->mode = mode; kv->k_max = k_max; kv->batch = batch; kv->max_seq = max_seq;
-  kv->len = 0; kv->k_used = 0; kv->invalid = false;
+  kv->len = 0; kv->invalid = false;
+  kv->filled.assign(k_max + 1, 0);
   kv->off.assign(s.nsub(), (size_t)-1);
   kv->nslots.assign(s.nsub(), 0);
   kv->rows.assign(s.nsub(), 0);
@@ -827,7 +849,7 @@ void dory_kv_destroy(dory_kv* kv) { delete kv; }
 dory_status dory_kv_reset(dory_kv* kv) {
   if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");
   kv->len = 0;
-  kv->k_used = 0;
+  std::fill(kv->filled.begin(), kv->filled.end(), 0);
   kv->invalid = false;
   return DORY_OK;
 }
@@ -883,11 +905,88 @@ dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tok
                      states, stream);
 }
 
+dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, int32_t B,
+                               int32_t gamma, int32_t k_draft, int32_t k_verify, dory_cache_mode mode,
+                               void* ws, size_t ws_bytes, int32_t* scratch, int32_t* out,
+                               int32_t* n_accepted, void* stream) {
+  if (!m || !kv || !last || !scratch || !out || !n_accepted)
+    return fail(DORY_ERR_ARG, "model, cache, tokens, scratch, out and n_accepted must be non-NULL");
+  if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
+  if (gamma < 1) return fail(DORY_ERR_ARG, "gamma must be >= 1");
+  if (k_draft < 1 || k_verify < k_draft) return fail(DORY_ERR_ARG, "need 1 <= k_draft <= k_verify");
+  if (!m->s.lm) return fail(DORY_ERR_ARG, "model has no LM head");
+  if (B != kv->batch) return fail(DORY_ERR_ARG, "B must equal the bound batch");
+  if (mode != kv->mode) return fail(DORY_ERR_MODE, "cache mode differs from the bound mode");
+  // under last-loop caching a verification chunk reads its own tokens'
+  // current-loop entries where step-by-step decoding reads final-loop ones,
+  // so the verifier would not reproduce plain decoding
+  if (mode != DORY_CACHE_PER_LOOP) return fail(DORY_ERR_MODE, "self-speculative decoding needs the per-loop cache");
+  if (kv->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure; call dory_kv_reset");
+  const int64_t L0 = kv->len;
+  if (L0 + gamma + 1 > kv->max_seq) return fail(DORY_ERR_CAPACITY, "cache capacity exceeded");
+  if (mode == DORY_CACHE_PER_LOOP) {
+    if (k_verify > kv->k_max) return fail(DORY_ERR_MODE, "per-loop cache: k_verify exceeds k_max");
+    if (kv->filled[k_verify] < L0)
+      return fail(DORY_ERR_MODE, "per-loop cache: earlier positions lack loop-k_verify entries");
+  }
+  const size_t need = std::max(plan_ws(m->s, B, 1).total, plan_ws(m->s, B, gamma + 1).total);
+  if (!ws || ws_bytes < need) return fail(DORY_ERR_WORKSPACE, "workspace smaller than dory_workspace_bytes(B, gamma + 1)");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int G = gamma + 1;
+  // scratch rows 0 .. gamma: the token fed to draft step j (row 0: `last`)
+  // and, in row j, the draft of step j; then the same as [B][gamma + 1]
+  if (hipMemcpyAsync(scratch, last, (size_t)B * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return fail(DORY_ERR_HIP, "copy of the last tokens failed");
+  for (int j = 1; j <= gamma; ++j) {
+    dory_status s1 = step_common(m, kv, scratch + (int64_t)(j - 1) * B, B, 1, k_draft, nullptr, mode,
+                                 ws, ws_bytes, nullptr, scratch + (int64_t)j * B, nullptr, nullptr,
+                                 stream);
+    if (s1 != DORY_OK) {
+      dory_kv_set_length(kv, L0);
+      return s1;
+    }
+  }
+  dory_kv_set_length(kv, L0);  // roll back the drafts' positions
+  int32_t* bt = scratch + (int64_t)G * B;
+  if (launch_transpose_i32(scratch, G, B, bt, st) != hipSuccess)
+    return fail(DORY_ERR_HIP, "token transpose failed");
+  dory_status s2 = step_common(m, kv, bt, B, G, k_verify, nullptr, mode, ws, ws_bytes, nullptr,
+                               nullptr, nullptr, nullptr, stream, out);
+  if (s2 != DORY_OK) {
+    dory_kv_set_length(kv, L0);
+    return s2;
+  }
+  std::vector<int32_t> drafts((size_t)G * B), greedy((size_t)G * B);
+  if (hipMemcpyAsync(drafts.data(), scratch, drafts.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(greedy.data(), out, greedy.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    kv->invalid = true;
+    return fail(DORY_ERR_HIP, "copy of the drafted and verified tokens failed");
+  }
+  // draft j is accepted while it equals the verifier's greedy token after
+  // position L0 + j - 1; the batch keeps the prefix accepted by every row
+  int n = gamma;
+  for (int b = 0; b < B; ++b) {
+    int nb = 0;
+    while (nb < gamma && drafts[(size_t)(nb + 1) * B + b] == greedy[(size_t)nb * B + b]) ++nb;
+    n = std::min(n, nb);
+  }
+  dory_kv_set_length(kv, L0 + n + 1);
+  *n_accepted = n;
+  return DORY_OK;
+}
+
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length) {
   if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");
   if (length < 0 || length > kv->max_seq) return fail(DORY_ERR_CAPACITY, "length outside [0, max_seq]");
+  if (length <= kv->len) {
+    // roll back: positions at or past `length` are forgotten
+    for (auto& f : kv->filled) f = std::min(f, length);
+  } else {
+    // extend: the caller declares every loop's entries of the new positions
+    for (auto& f : kv->filled) f = length;
+  }
   kv->len = length;
-  kv->k_used = 0;
   return DORY_OK;
 }
 

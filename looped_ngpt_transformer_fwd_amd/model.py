@@ -123,6 +123,20 @@ class Model:
             pass
         self.handle = None
 
+    def selfspec_step(self, kv, last, gamma, k_draft, k_verify, ws=None):
+        """One self-speculative round (greedy): returns (n accepted, tokens
+        [B, n + 1]) -- the next n + 1 tokens of every sequence."""
+        B = kv.batch
+        if ws is None:
+            ws = self.workspace(B, gamma + 1)
+        scratch = torch.empty(2 * B * (gamma + 1), dtype=torch.int32, device=last.device)
+        out = torch.empty(gamma + 1, B, dtype=torch.int32, device=last.device)
+        n = ctypes.c_int32()
+        C.check(C.dory_selfspec_step(self.handle, kv.handle, _ptr(last), B, gamma, k_draft, k_verify,
+                                     kv.mode_code, _ptr(ws), ws.numel(), _ptr(scratch), _ptr(out), n,
+                                     _stream()), "dory_selfspec_step")
+        return n.value, out[:n.value + 1].t().contiguous()
+
     def quantize_mxfp8(self, device="cuda"):
         """Quantizes the projection matrices to MXFP8 (weight-only) into a
         buffer owned by this object and switches the model to them."""
@@ -221,6 +235,7 @@ class KVCache:
         self.model = model
         self.mode = mode
         self.mode_code = MODE_CODE[mode]
+        self.batch = batch
         n = kv_bytes(model.shape, mode, k_max, batch, max_seq)
         if n == 0:
             raise ValueError("invalid cache parameters")
