@@ -222,6 +222,74 @@ def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4, mixed=True):
     return out
 
 
+def decode_selfspec(gm, shape, B=64, ctx=32768, gamma=4, k_draft=1, k_verify=4, steps=4):
+    """Self-speculative rounds (per-loop caches): gamma greedy drafts at
+    k_draft, then one verification pass over gamma + 1 positions at k_verify.
+    With random weights the acceptance rate carries no information, so the
+    round time is reported against the k_verify decode step: a round pays
+    off when the batch accepts more than (round / step - 1) drafts."""
+    ws = gm.workspace(B, gamma + 1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2)
+    toks = torch.randint(0, shape.vocab, (B,), dtype=torch.int32, device="cuda", generator=g)
+    kv = gm.kv_cache("per_loop", k_verify, B, ctx + gamma + 1)
+    buf = kv.buffer.view(torch.bfloat16)
+    chunk = 1 << 28
+    for o in range(0, buf.numel(), chunk):
+        n = min(chunk, buf.numel() - o)
+        buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
+    acc = []
+
+    def rnd():
+        kv.set_length(ctx)
+        acc.append(gm.selfspec_step(kv, toks, gamma, k_draft, k_verify, ws=ws)[0])
+
+    def plain():
+        kv.set_length(ctx)
+        gm.decode_step(kv, toks, k_verify, ws=ws, logits=True, next_token=True)
+    rnd()
+    plain()
+    t_round = time_steps(rnd, steps) / steps
+    t_step = time_steps(plain, steps) / steps
+    del kv, buf
+    torch.cuda.empty_cache()
+    return {"round_ms": round(t_round * 1e3, 3), "decode_step_ms": round(t_step * 1e3, 3),
+            "break_even_accepted": round(t_round / t_step - 1, 2),
+            "tok_s_all_accepted": round(B * (gamma + 1) / t_round, 1),
+            "tok_s_none_accepted": round(B / t_round, 1),
+            "decode_tok_s": round(B / t_step, 1),
+            "accepted_random_weights": acc[1:],
+            "config": f"B={B}, {ctx} cached tokens, per_loop, gamma={gamma}, "
+                      f"draft k={k_draft}, verify k={k_verify}"}
+
+
+def prefix_copy(gm, shape, n=32768, B=8, steps=4):
+    """Prefix caching: the cached K/V of one sequence's n-token prefix
+    (synthesized at random) copied into B sequences of another cache.
+    Algorithmic bytes: what the source holds for the prefix (every full
+    attention sublayer's n positions, every sliding-window ring), read once
+    and written once per destination sequence."""
+    src = gm.kv_cache("last_loop", 1, 1, n)
+    buf = src.buffer.view(torch.bfloat16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    buf.copy_((0.02 * torch.randn(buf.numel(), device="cuda", generator=g)).to(torch.bfloat16))
+    src.set_length(n)
+    dst = gm.kv_cache("last_loop", 1, B, n)
+
+    def one():
+        dst.reset()
+        for b in range(B):
+            dst.copy_prefix_from(src, 0, b, n)
+    one()
+    dt = time_steps(one, steps) / steps
+    moved = 2 * src.buffer.numel() * B
+    del src, dst, buf
+    torch.cuda.empty_cache()
+    return {"prefix_tokens": n, "sequences": B, "ms": round(dt * 1e3, 3),
+            "GB_s": round(moved / dt / 1e9, 1), "frac_hbm": round(moved / dt / 1e9 / HBM_PEAK_GBS, 3)}
+
+
 class _RowGather:
     """Embedding rows widened to float64 on demand."""
 
@@ -309,7 +377,8 @@ def main():
     if args.decode_only:
         d = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
         d.update(decode_mxfp8(gm, shape))
-        print(json.dumps({"decode_tok_s": d}), flush=True)
+        print(json.dumps({"decode_tok_s": d, "selfspec": decode_selfspec(gm, shape),
+                          "prefix_copy": prefix_copy(gm, shape)}), flush=True)
         return
     ws = gm.workspace(B, T)
     g = torch.Generator(device="cuda")
@@ -380,6 +449,8 @@ def main():
         torch.cuda.empty_cache()
         result["decode_tok_s"] = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
         result["decode_tok_s"].update(decode_mxfp8(gm, shape))
+        result["selfspec"] = decode_selfspec(gm, shape)
+        result["prefix_copy"] = prefix_copy(gm, shape)
         result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each; "
                                    "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences; "
                                    "mxfp8: projection weights in MXFP8 (W8A16), embedding and LM head "

@@ -228,6 +228,27 @@ dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tok
  * every loop (for example a cache restored by the caller). */
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length);
 
+/* Prefix caching (section Last-Loop KV Caching: serving reuses cached
+ * prefixes). Copies the cached K/V of positions 0 .. n - 1 of sequence
+ * src_seq of `src` into sequence dst_seq of `dst`, so that a prompt prefix
+ * shared by several requests is computed once: the step after the copy
+ * continues at position n exactly as if dst_seq had run the prefix itself
+ * with the loop counts src_seq used. Both caches must be bound to the same
+ * model and policy (DORY_ERR_ARG / DORY_ERR_MODE); 1 <= n <= length of src
+ * (DORY_ERR_ARG); n <= max_seq of dst (DORY_ERR_CAPACITY). The length of dst
+ * must be 0 or n (DORY_ERR_STATE) and becomes n: the call sets it for every
+ * sequence of dst, so every sequence must receive a prefix of length n (or
+ * the caller's own entries) before dst's next step. Sliding-window
+ * sublayers copy the positions both rings hold (the last ring-size
+ * positions). Per-loop caching: the loops copied are those whose entries
+ * src holds for all n positions, up to dst's k_max; dst then holds only
+ * the loops every copied sequence received, and a later step needs loop-k
+ * entries as usual. src and dst may be the same cache (sequence to
+ * sequence). Enqueued on `stream` (a hipStream_t, NULL for the default
+ * stream); all checks happen before anything is enqueued. */
+dory_status dory_kv_copy_prefix(const dory_kv* src, int32_t src_seq, dory_kv* dst, int32_t dst_seq,
+                                int64_t n, void* stream);
+
 /* One round of self-speculative greedy decoding (section Self-Speculative
  * Decoding: the same checkpoint drafts at a shallow loop count and verifies
  * at a deeper one in one batched pass over the drafted tokens). From the

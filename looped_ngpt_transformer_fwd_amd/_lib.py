@@ -84,6 +84,7 @@ SIGNATURES = {
     "dory_decode_step_rows": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_debug_mask": (_I32, [_I32, _I64, _I32, _P, _P]),
     "dory_kv_set_length": (_I32, [_P, _I64]),
+    "dory_kv_copy_prefix": (_I32, [_P, _I32, _P, _I32, _I64, _P]),
     "dory_profile_begin": (_I32, [_P, _I32]),
     "dory_profile_end": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "dory_selfspec_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P,
@@ -200,6 +201,10 @@ def dory_debug_mask(window, L, T, out, stream):
 
 def dory_kv_set_length(kv, length):
     return lib().dory_kv_set_length(kv, length)
+
+
+def dory_kv_copy_prefix(src, src_seq, dst, dst_seq, n, stream):
+    return lib().dory_kv_copy_prefix(src, src_seq, dst, dst_seq, n, stream)
 
 
 def dory_selfspec_step(m, kv, last, B, gamma, k_draft, k_verify, mode, ws, ws_bytes, scratch, out,

@@ -680,13 +680,14 @@ hipError_t launch_big(const GemmArgs& a0, int epi, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel for M <= 64 (decode, the LM head of a prefill): the weight
-// stream dominates, so the goal is bytes in flight. A ring of four LDS
-// stages (one K step of 64 each, the same XOR-swizzled 128-byte rows as the
-// large kernel) filled by DMA three steps ahead; every step issues exactly
-// four DMA per wave (the last steps reload the final step into a stage no
-// one reads again), so the wait before each step is vmcnt(8).
-// 64 x 64 output tiles, 4 waves of 32 x 32, split-K over blockIdx.z.
+// Skinny kernel for small M (decode, the LM head of a prefill, short
+// verification chunks of a batch): the weight stream dominates, so the goal
+// is bytes in flight. A ring of four LDS stages (one K step of 64 each, the
+// same XOR-swizzled 128-byte rows as the large kernel) filled by DMA three
+// steps ahead; every step issues exactly four DMA per wave (the last steps
+// reload the final step into a stage no one reads again), so the wait
+// before each step is vmcnt(8). 64 x 64 output tiles, 4 waves of 32 x 32,
+// split-K; above 64 rows one workgroup per 64-row block, grouped by XCD.
 constexpr int SK_MAX = 4;
 
 template <int EPI>
@@ -705,10 +706,29 @@ gemm_skinny_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * 64;
+  // work item: (64-column tile, split) pair and 64-row block. Up to 64 rows:
+  // blockIdx.x = tile, blockIdx.z = split. More rows (1-D grid): workgroups
+  // are dispatched round-robin over the 8 XCDs, so XCD x takes pairs x,
+  // x + 8, ... and runs the row blocks of one pair back to back; the pair's
+  // weight tile then comes from that XCD's L2 after the first row block.
+  int tile, split, m0 = 0;
+  if (g.M > 64) {
+    const int nmb = (g.M + 63) / 64;
+    const int lin = blockIdx.x, j = lin >> 3;
+    const int pair = (lin & 7) + 8 * (j / nmb);
+    const int ntile = (g.N + 63) / 64;
+    if (pair >= ntile * g.nsplit) return;  // padding of the last round of pairs
+    tile = pair % ntile;
+    split = pair / ntile;
+    m0 = (j % nmb) * 64;
+  } else {
+    tile = blockIdx.x;
+    split = blockIdx.z;
+  }
+  const int n0 = tile * 64;
   const int ksteps = g.K / BK;
   const int per = (ksteps + g.nsplit - 1) / g.nsplit;
-  const int ks0 = blockIdx.z * per;
+  const int ks0 = split * per;
   const int n = max(0, min(ksteps, ks0 + per) - ks0);
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
@@ -719,7 +739,7 @@ gemm_skinny_kernel(GemmArgs g) {
   for (int i = 0; i < 2; ++i) {
     const int r = (wave + 4 * i) * 8 + lr;
     const int lc = (lane & 7) ^ ((r >> 1) & 7);
-    aoff[i] = (uint32_t)((int64_t)min(r, g.M - 1) * g.lda * 2 + lc * 16);
+    aoff[i] = (uint32_t)((int64_t)min(m0 + r, g.M - 1) * g.lda * 2 + lc * 16);
     boff[i] = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldb * 2 + lc * 16);
   }
   const int fr = lane & 31, fh = lane >> 5;
@@ -774,8 +794,8 @@ gemm_skinny_kernel(GemmArgs g) {
   const int col = n0 + wn * 32 + (lane & 31);
   if (col < g.N) {
     const float sc = (EPI == EPI_LOGITS) ? g.s1[col] : 1.f;
-    float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
-    const int rbase = wm * 32 + (lane >> 5) * 4;
+    float* C = g.C + (int64_t)split * g.split_stride;
+    const int rbase = m0 + wm * 32 + (lane >> 5) * 4;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = rbase + (e >> 2) * 8 + (e & 3);
@@ -924,6 +944,11 @@ gemm_skinny_fp8_kernel(GemmArgs g) {
 
 hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t st) {
   dim3 grid((a.N + 63) / 64, 1, a.nsplit), block(256);
+  if (a.M > 64) {
+    // 1-D grid: 8 pairs per round, every row block of each
+    const int pairs = ((a.N + 63) / 64) * a.nsplit;
+    grid = dim3((unsigned)(8 * ((a.M + 63) / 64) * ((pairs + 7) / 8)), 1, 1);
+  }
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL((gemm_skinny_kernel<EPI_F32>), grid, block, 0, st, a); break;
     case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny_kernel<EPI_LOGITS>), grid, block, 0, st, a); break;
@@ -947,16 +972,17 @@ hipError_t launch_cfg(const GemmArgs& a, int epi, hipStream_t st) {
 }
 
 constexpr int kLargeM = 1024;
+static_assert(kGemmSkinnyMaxM < kLargeM, "the skinny range ends below the large-M kernel");
 
 }  // namespace
 
 int gemm_pick_split(int M, int N, int K, int max_split) {
   if (M >= kLargeM) return 1;
   const int ksteps = K / BK;
-  if (M <= 64) {
+  if (M <= kGemmSkinnyMaxM) {
     // skinny path: the most workgroups that fit one round (2 per CU, 512),
     // at least SK_MAX K steps each, within max_split
-    const int tiles = (N + 63) / 64;
+    const int tiles = ((N + 63) / 64) * ((M + 63) / 64);
     int s = 1;
     while (s < max_split && tiles * (s + 1) <= 512 && ksteps / (s + 1) >= SK_MAX) ++s;
     return s;
@@ -982,7 +1008,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   }
   if (a.M >= kLargeM) return launch_big(a, epi, st);
   if (epi == EPI_QKV || epi == EPI_BF16) return hipErrorInvalidValue;
-  if (a.M <= 64 && (epi == EPI_F32 || epi == EPI_LOGITS)) return launch_skinny(a, epi, st);
+  if (a.M <= kGemmSkinnyMaxM && (epi == EPI_F32 || epi == EPI_LOGITS)) return launch_skinny(a, epi, st);
   return launch_cfg<64, 128, 32, 64>(a, epi, st);
 }
 

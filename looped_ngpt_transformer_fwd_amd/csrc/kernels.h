@@ -60,6 +60,11 @@ struct GemmArgs {
   const uint8_t* Bs = nullptr;
 };
 
+// GEMMs with at most this many rows (every M below the large-M kernel's
+// 1024) and an fp32 or logits output stream the weights through the skinny
+// kernel (no fused SwiGLU epilogue there).
+constexpr int kGemmSkinnyMaxM = 1023;
+
 // Picks a tile configuration and split factor; `max_split` bounds the split
 // (the workspace holds that many partial outputs).
 int gemm_pick_split(int M, int N, int K, int max_split);
@@ -153,6 +158,15 @@ hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_row
                            int64_t f_origin, int B, int n_kv, int dh, int64_t pos_a,
                            int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
                            int64_t ring, hipStream_t st, RowLoops rl = RowLoops());
+
+// Copy the entries of positions [pos_a, pos_b) of sequence s_seq of one
+// cache slot into sequence d_seq of another (layouts as QkDest: K rows
+// [batch][n_kv][rows][dh], V^T [batch][n_kv][dh][rows]; row = pos mod ring
+// when ring > 0). The two ranges must not overlap in memory unless identical.
+hipError_t launch_kv_copy(const uint16_t* sk, const uint16_t* sv, int64_t s_rows, int64_t s_ring,
+                          int s_seq, uint16_t* dk, uint16_t* dv, int64_t d_rows, int64_t d_ring,
+                          int d_seq, int n_kv, int dh, int64_t pos_a, int64_t pos_b,
+                          hipStream_t st);
 
 // Zero columns [c0, c1) of every row of a fresh V^T buffer
 // ([B][n_kv][dh][f_rows]); the prefill attention reads whole 8-key chunks.

@@ -284,6 +284,48 @@ __global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t 
   vc[(bg * dh + d) * c_rows + crow] = vf[(bg * dh + d) * f_rows + frow];
 }
 
+// Cache-to-cache copy of positions [pos_a, pos_b) of one sequence's K rows
+// and V^T columns. blockIdx.x = 64-position tile counted from pos_a rounded
+// down to a multiple of 8, blockIdx.y = group. Rows and rings are multiples
+// of 8, so an aligned group of 8 positions occupies 8 consecutive, 16-byte
+// aligned V^T columns on both sides and moves as one 16-byte vector; K rows
+// move in 16-byte pieces (dh a multiple of 8). Positions outside the range
+// are never written: in a ring they share rows with positions inside it.
+__global__ void kv_copy_kernel(const uint16_t* sk, const uint16_t* sv, int64_t s_rows,
+                               int64_t s_ring, int64_t s_bg, uint16_t* dk, uint16_t* dv,
+                               int64_t d_rows, int64_t d_ring, int64_t d_bg, int dh,
+                               int64_t pos_a, int64_t pos_b) {
+  const int64_t base = (pos_a & ~(int64_t)7) + (int64_t)blockIdx.x * 64;
+  const int64_t sbg = s_bg + blockIdx.y, dbg = d_bg + blockIdx.y;
+  const int cpr = dh / 8;  // 16-byte pieces per K row
+  for (int i = threadIdx.x; i < 64 * cpr; i += blockDim.x) {
+    const int64_t pos = base + i / cpr;
+    if (pos < pos_a || pos >= pos_b) continue;
+    const int c = i % cpr;
+    const int64_t sr = s_ring > 0 ? pos % s_ring : pos;
+    const int64_t dr = d_ring > 0 ? pos % d_ring : pos;
+    *reinterpret_cast<uint4*>(dk + (dbg * d_rows + dr) * dh + c * 8) =
+        *reinterpret_cast<const uint4*>(sk + (sbg * s_rows + sr) * dh + c * 8);
+  }
+  for (int i = threadIdx.x; i < 8 * dh; i += blockDim.x) {
+    const int d = i >> 3;
+    const int64_t p0 = base + (i & 7) * 8;
+    const uint16_t* srow = sv + (sbg * dh + d) * s_rows;
+    uint16_t* drow = dv + (dbg * dh + d) * d_rows;
+    if (p0 >= pos_a && p0 + 8 <= pos_b) {
+      const int64_t sr = s_ring > 0 ? p0 % s_ring : p0;
+      const int64_t dr = d_ring > 0 ? p0 % d_ring : p0;
+      *reinterpret_cast<uint4*>(drow + dr) = *reinterpret_cast<const uint4*>(srow + sr);
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        const int64_t pos = p0 + e;
+        if (pos < pos_a || pos >= pos_b) continue;
+        drow[d_ring > 0 ? pos % d_ring : pos] = srow[s_ring > 0 ? pos % s_ring : pos];
+      }
+    }
+  }
+}
+
 __global__ void rope_table_kernel(int64_t p0, int T, int half, int dh, double base, float* cs,
                                   float* sn) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -433,6 +475,20 @@ hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_row
   if (pos_b <= pos_a) return hipSuccess;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
                      kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring, rl);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_copy(const uint16_t* sk, const uint16_t* sv, int64_t s_rows, int64_t s_ring,
+                          int s_seq, uint16_t* dk, uint16_t* dv, int64_t d_rows, int64_t d_ring,
+                          int d_seq, int n_kv, int dh, int64_t pos_a, int64_t pos_b,
+                          hipStream_t st) {
+  if (pos_b <= pos_a) return hipSuccess;
+  if (dh % 8 != 0 || s_rows % 8 != 0 || d_rows % 8 != 0 || s_ring % 8 != 0 || d_ring % 8 != 0)
+    return hipErrorInvalidValue;
+  const int64_t span = pos_b - (pos_a & ~(int64_t)7);
+  hipLaunchKernelGGL(kv_copy_kernel, dim3((unsigned)((span + 63) / 64), n_kv), dim3(256), 0, st,
+                     sk, sv, s_rows, s_ring, (int64_t)s_seq * n_kv, dk, dv, d_rows, d_ring,
+                     (int64_t)d_seq * n_kv, dh, pos_a, pos_b);
   return hipGetLastError();
 }
 

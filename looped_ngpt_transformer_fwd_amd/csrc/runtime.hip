@@ -441,9 +441,9 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
   const dory_sublayer_weights& w = c.m->sub[i];
   const int ns_up = gemm_pick_split((int)c.M, 2 * s.F, s.d, max_split_for(c.M));
   const WSel wug = wsel(c, i, 0, w.w_upgate);
-  // the fused SwiGLU epilogue reads bf16 weights; MXFP8 codes go through
-  // the fp32 partials
-  if (ns_up == 1 && !wug.q) {
+  // the fused SwiGLU epilogue reads bf16 weights and runs on the tiled
+  // kernels; MXFP8 codes and the skinny kernel go through fp32 outputs
+  if (ns_up == 1 && !wug.q && c.M > kGemmSkinnyMaxM) {
     PROF(c, DORY_K_GEMM_UPGATE);
     GemmArgs g;
     g.A = c.h16(); g.lda = s.d;
@@ -973,6 +973,53 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
   }
   dory_kv_set_length(kv, L0 + n + 1);
   *n_accepted = n;
+  return DORY_OK;
+}
+
+dory_status dory_kv_copy_prefix(const dory_kv* src, int32_t src_seq, dory_kv* dst, int32_t dst_seq,
+                                int64_t n, void* stream) {
+  if (!src || !dst) return fail(DORY_ERR_ARG, "caches must be non-NULL");
+  if (src->m != dst->m) return fail(DORY_ERR_ARG, "caches bound to different models");
+  if (src->mode != dst->mode) return fail(DORY_ERR_MODE, "caches use different policies");
+  if (src_seq < 0 || src_seq >= src->batch || dst_seq < 0 || dst_seq >= dst->batch)
+    return fail(DORY_ERR_ARG, "sequence index outside the bound batch");
+  if (n < 1 || n > src->len) return fail(DORY_ERR_ARG, "n must be in [1, source length]");
+  if (n > dst->max_seq) return fail(DORY_ERR_CAPACITY, "n exceeds the destination's max_seq");
+  if (dst->len != 0 && dst->len != n)
+    return fail(DORY_ERR_STATE, "destination length must be 0 or n");
+  if (src->invalid || dst->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure");
+  if (src == dst && src_seq == dst_seq) return DORY_OK;
+  const Shape& s = src->m->s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // loops whose first n positions the source holds (per-loop); slot j is loop j + 1
+  int loops = 1;
+  if (src->mode == DORY_CACHE_PER_LOOP) {
+    loops = 0;
+    while (loops < std::min(src->k_max, dst->k_max) && src->filled[loops + 1] >= n) ++loops;
+  }
+  for (int i = 0; i < s.nsub(); ++i) {
+    if (src->m->kinds[i] == DORY_LAYER_MLP) continue;
+    const int slots = src->nslots[i] > 1 ? loops : 1;
+    // a ring keeps its last `ring` positions: copy what both rings hold
+    int64_t keep = n;
+    if (src->ring[i] > 0) keep = std::min(keep, src->ring[i]);
+    if (dst->ring[i] > 0) keep = std::min(keep, dst->ring[i]);
+    for (int j = 0; j < slots; ++j) {
+      SlotPtr a = slot_ptr(src, i, j), b = slot_ptr(dst, i, j);
+      if (launch_kv_copy(a.k, a.v, a.rows, a.ring, src_seq, b.k, b.v, b.rows, b.ring, dst_seq, s.nkv,
+                         s.dh, n - keep, n, st) != hipSuccess) {
+        dst->invalid = true;
+        return fail(DORY_ERR_HIP, "KV copy launch failed");
+      }
+    }
+  }
+  if (dst->len == 0) {
+    dst->len = n;
+    for (int j = 0; j <= dst->k_max; ++j) dst->filled[j] = (j == 0 || j <= loops) ? n : 0;
+  } else {
+    // the other sequences' loops stay as they are; loops this one lacks are not held
+    for (int j = loops + 1; j <= dst->k_max; ++j) dst->filled[j] = 0;
+  }
   return DORY_OK;
 }
 

@@ -254,6 +254,13 @@ class KVCache:
     def set_length(self, length):
         C.check(C.dory_kv_set_length(self.handle, length), "dory_kv_set_length")
 
+    def copy_prefix_from(self, src, src_seq, dst_seq, n):
+        """Reuses the first n cached positions of sequence src_seq of cache
+        `src` as those of sequence dst_seq of this cache (prefix caching);
+        this cache's length becomes n."""
+        C.check(C.dory_kv_copy_prefix(src.handle, src_seq, self.handle, dst_seq, n, _stream()),
+                "dory_kv_copy_prefix")
+
     def slot(self, sublayer, loop=0):
         info = C.dory_kv_slot_info()
         C.check(C.dory_kv_slot(self.handle, sublayer, loop, info), "dory_kv_slot")

@@ -243,3 +243,34 @@ def test_mxfp8_argument_validation_enqueues_nothing():
     assert C.dory_model_quantize_mxfp8(m.handle, P(0x100000), n - 1, None) == C.DORY_ERR_CAPACITY
     assert C.dory_model_quantize_mxfp8(m.handle, P(0x100010), n, None) == C.DORY_ERR_ARG
     assert C.dory_model_use_mxfp8(m.handle, 1) == C.DORY_ERR_ARG
+
+
+def test_copy_prefix_validated_before_enqueue():
+    """Prefix copy: every rejection happens on the host, before anything is
+    enqueued, and leaves both caches' lengths as they were."""
+    m, src = _model_and_kv(batch=1, max_seq=64)
+    kvb = M.kv_bytes(synth.TINY, "last_loop", 4, 3, 32)
+    dst = ctypes.c_void_p()
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0xA00000), kvb, C.DORY_CACHE_LAST_LOOP, 4, 3,
+                           32, dst), "bind")
+    C.check(C.dory_kv_set_length(src, 40), "set_length")
+    assert C.dory_kv_copy_prefix(None, 0, dst, 0, 8, None) == C.DORY_ERR_ARG
+    assert C.dory_kv_copy_prefix(src, 1, dst, 0, 8, None) == C.DORY_ERR_ARG     # src batch is 1
+    assert C.dory_kv_copy_prefix(src, 0, dst, 3, 8, None) == C.DORY_ERR_ARG     # dst batch is 3
+    assert C.dory_kv_copy_prefix(src, 0, dst, -1, 8, None) == C.DORY_ERR_ARG
+    assert C.dory_kv_copy_prefix(src, 0, dst, 0, 0, None) == C.DORY_ERR_ARG
+    assert C.dory_kv_copy_prefix(src, 0, dst, 0, 41, None) == C.DORY_ERR_ARG    # beyond src length
+    assert C.dory_kv_copy_prefix(src, 0, dst, 0, 33, None) == C.DORY_ERR_CAPACITY
+    C.check(C.dory_kv_set_length(dst, 5), "set_length")
+    assert C.dory_kv_copy_prefix(src, 0, dst, 0, 8, None) == C.DORY_ERR_STATE   # dst length not 0 / n
+    assert C.dory_kv_length(src) == 40 and C.dory_kv_length(dst) == 5
+    m2, other = _model_and_kv(mode="per_loop", batch=1, max_seq=64)
+    C.check(C.dory_kv_set_length(other, 40), "set_length")
+    assert C.dory_kv_copy_prefix(other, 0, dst, 0, 8, None) == C.DORY_ERR_ARG   # another model
+    kvp = M.kv_bytes(synth.TINY, "per_loop", 4, 3, 32)
+    dst2 = ctypes.c_void_p()
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0xA00000), kvp, C.DORY_CACHE_PER_LOOP, 4, 3, 32,
+                           dst2), "bind")
+    assert C.dory_kv_copy_prefix(src, 0, dst2, 0, 8, None) == C.DORY_ERR_MODE   # policies differ
+    for h in (src, dst, other, dst2):
+        C.dory_kv_destroy(h)
