@@ -14,7 +14,8 @@ namespace dory {
 enum GemmEpi {
   EPI_F32 = 0,     // C (+ split * split_stride) = partial sum of split z
   EPI_SWIGLU = 1,  // B = [W_up; W_gate] (2F rows); C16[m, f] =
-                   //   bf16(SiLU(s2[f] * gate) * s1[f] * up); N = 2F; no split
+                   //   bf16(SiLU(s2[f] * gate) * s1[f] * up); N = 2F; no split;
+                   //   large-M path only
   EPI_LOGITS = 2,  // C[m, n] = s1[n] * acc; no split
   EPI_QKV = 3,     // fused query/key transform (large-M path, head_dim 128):
                    // columns of B = w_qkvg; writes q_hat, fresh K, fresh V^T
