@@ -175,11 +175,17 @@ class Weights:
     only the right tensors exist for each sublayer.
     """
 
+    # float64 copies kept per object, up to this many bytes (first come);
+    # larger models convert the rest on every access
+    F64_CACHE_BYTES = 4 << 30
+
     def __init__(self, shape: Shape, kinds, seed: int = 0):
         self.shape = shape
         self.kinds = list(kinds)
         self.seed = seed
         self._cache = {}
+        self._f64 = {}
+        self._f64_bytes = 0
 
     def names(self):
         s = self.shape
@@ -229,15 +235,28 @@ class Weights:
         return self._cache[name]
 
     def f64(self, name: str) -> np.ndarray:
+        """float64 values of a tensor (read-only when kept in the cache)."""
+        if name in self._f64:
+            return self._f64[name]
         r = self.raw(name)
-        if r.dtype == np.uint16:
-            return f64_from_bf16_bits(r)
-        return r.astype(np.float64)
+        out = f64_from_bf16_bits(r) if r.dtype == np.uint16 else r.astype(np.float64)
+        if self._f64_bytes + out.nbytes <= self.F64_CACHE_BYTES:
+            out.flags.writeable = False
+            self._f64[name] = out
+            self._f64_bytes += out.nbytes
+        return out
+
+    def _forget_f64(self, name: str) -> None:
+        old = self._f64.pop(name, None)
+        if old is not None:
+            self._f64_bytes -= old.nbytes
 
     def set_raw(self, name: str, value: np.ndarray) -> None:
         """Override one tensor (bf16 bits for matrices, float32 for vectors),
         used to build special cases such as zero gates."""
+        self._forget_f64(name)
         self._cache[name] = value
 
     def drop(self, name: str) -> None:
+        self._forget_f64(name)
         self._cache.pop(name, None)

@@ -97,3 +97,40 @@ def test_recurrent_pair_decode_full_width(pair, mode):
         for i in range(k):
             per_token_check(st[i].reshape(B, 1, -1), o["states"][i], f"decode {t} s_{i + 1}")
         per_token_check(out["hidden"].cpu().numpy().reshape(B, 1, -1), o["hidden"], f"decode {t} hidden")
+
+
+def test_recurrent_pair_rows_between_64_and_1024(pair):
+    """Projections with 64 < M < 1024 rows at full width: the skinny GEMM's
+    XCD-grouped 64-row blocks with K = 2304 and 6144 and N up to 12288, last
+    block ragged. Chunked prefill of 3 sequences (600 and 990 rows) under the
+    per-loop cache, then decode of 100 sequences (100 rows) after a 12-token
+    prefill (1200 rows, large-M path)."""
+    shape, W, gm, om = pair
+    k = 2
+    log("pair 3 x (200 + 330) per_loop")
+    B = 3
+    toks = synth.tokens(5, B, 530, shape.vocab)
+    kv = gm.kv_cache("per_loop", k, B, 530)
+    oc = ref.Cache(shape, "per_loop", B)
+    for a, b in [(0, 200), (200, 530)]:
+        out = gm.prefill(kv, torch.from_numpy(toks[:, a:b].copy()).cuda(), k, logits=False,
+                         hidden=True, states=True)
+        torch.cuda.synchronize()
+        o = om.step(oc, toks[:, a:b], k, logits=None)
+        st = out["states"].cpu().numpy()
+        for i in range(k):
+            per_token_check(st[i], o["states"][i], f"[{a},{b}) s_{i + 1}")
+        per_token_check(out["hidden"].cpu().numpy(), o["hidden"], f"[{a},{b}) hidden")
+    log("pair decode B=100")
+    B, T0 = 100, 12
+    toks = synth.tokens(6, B, T0 + 2, shape.vocab)
+    kv = gm.kv_cache("last_loop", k, B, T0 + 2)
+    oc = ref.Cache(shape, "last_loop", B)
+    gm.prefill(kv, torch.from_numpy(toks[:, :T0].copy()).cuda(), k, logits=False)
+    om.step(oc, toks[:, :T0], k, logits=None)
+    for t in range(T0, T0 + 2):
+        out = gm.decode_step(kv, torch.from_numpy(toks[:, t].copy()).cuda(), k, logits=False,
+                             next_token=False, hidden=True)
+        torch.cuda.synchronize()
+        o = om.step(oc, toks[:, t:t + 1], k, logits=None)
+        per_token_check(out["hidden"].cpu().numpy().reshape(B, 1, -1), o["hidden"], f"decode {t} hidden")
