@@ -378,6 +378,7 @@ def main():
         d = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
         d.update(decode_mxfp8(gm, shape))
         print(json.dumps({"decode_tok_s": d, "selfspec": decode_selfspec(gm, shape),
+                          "selfspec_b8_ctx4096": decode_selfspec(gm, shape, B=8, ctx=4096),
                           "prefix_copy": prefix_copy(gm, shape)}), flush=True)
         return
     ws = gm.workspace(B, T)
@@ -450,6 +451,7 @@ def main():
         result["decode_tok_s"] = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
         result["decode_tok_s"].update(decode_mxfp8(gm, shape))
         result["selfspec"] = decode_selfspec(gm, shape)
+        result["selfspec_b8_ctx4096"] = decode_selfspec(gm, shape, B=8, ctx=4096)
         result["prefix_copy"] = prefix_copy(gm, shape)
         result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each; "
                                    "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences; "
