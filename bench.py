@@ -290,6 +290,41 @@ def prefix_copy(gm, shape, n=32768, B=8, steps=4):
             "GB_s": round(moved / dt / 1e9, 1), "frac_hbm": round(moved / dt / 1e9 / HBM_PEAK_GBS, 3)}
 
 
+def long_context(gm, shape, k=4, total=262144, chunk=8192, n_dec=128):
+    """One 262,144-token sequence: chunked prefill in chunks of 8,192 at k
+    (last-loop cache; the later chunks attend over up to 262,143 earlier
+    positions), then greedy decode steps at the full context."""
+    kv = gm.kv_cache("last_loop", k, 1, total + n_dec)
+    ws = gm.workspace(1, chunk)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    toks = torch.randint(0, shape.vocab, (1, total), dtype=torch.int32, device="cuda", generator=g)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = None
+    for a in range(0, total, chunk):
+        last = a + chunk == total
+        out = gm.prefill(kv, toks[:, a:a + chunk], k, ws=ws, logits=last, next_token=last)
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t0
+    t = out["next"]
+    t0 = time.perf_counter()
+    for _ in range(n_dec):
+        t = gm.decode_step(kv, t, k, ws=ws, logits=True, next_token=True)["next"]
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t0
+    del kv, ws
+    torch.cuda.empty_cache()
+    return {"prefill_tok_s": round(total / t_pre, 1), "prefill_s": round(t_pre, 3),
+            "decode_tok_s": round(n_dec / t_dec, 1), "decode_ms_per_step": round(t_dec / n_dec * 1e3, 3),
+            "config": f"B=1, {total} tokens in chunks of {chunk}, k={k}, last_loop, "
+                      f"then {n_dec} greedy decode steps"}
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 class _RowGather:
     """Embedding rows widened to float64 on demand."""
 
@@ -435,6 +470,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    progress(f"prefill k={k}: {value:.0f} tokens/s")
     if not args.no_extra:
         pre = {f"k{k}": round(value, 1)}
         for kk in (1, 2, 4):
@@ -448,16 +484,23 @@ def main():
         result["prefill_tok_s"] = dict(sorted(pre.items()))
         del kv, ws
         torch.cuda.empty_cache()
+        progress("prefill k-sweep done")
         result["decode_tok_s"] = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
+        progress("decode table done")
         result["decode_tok_s"].update(decode_mxfp8(gm, shape))
+        progress("mxfp8 decode done")
         result["selfspec"] = decode_selfspec(gm, shape)
         result["selfspec_b8_ctx4096"] = decode_selfspec(gm, shape, B=8, ctx=4096)
+        progress("self-speculative rounds done")
         result["prefix_copy"] = prefix_copy(gm, shape)
+        result["long_context"] = long_context(gm, shape)
+        progress("long context done")
         result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each; "
                                    "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences; "
                                    "mxfp8: projection weights in MXFP8 (W8A16), embedding and LM head "
                                    "bf16; ctx2048: 2048 cached tokens")
     if not args.no_cpu:
+        progress("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(k)
     print(json.dumps(result), flush=True)
 
