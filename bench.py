@@ -367,10 +367,17 @@ def cpu_baseline(k, n_tokens=512):
     t0 = time.perf_counter()
     om.step(ref.Cache(sh, ref.MODE_LAST, 1), toks, k)
     dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"float64 oracle, full 72-sublayer shape, k={k}, sequence 0 tokens "
-                      f"0..{n_tokens - 1} (of 4 x 8192), one prefill step, {dt:.1f} s"}
+                      f"0..{n_tokens - 1} (of 4 x 8192), one prefill step, {dt:.1f} s",
+            "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 
 def main():
