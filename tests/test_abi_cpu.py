@@ -274,3 +274,40 @@ def test_copy_prefix_validated_before_enqueue():
     assert C.dory_kv_copy_prefix(src, 0, dst2, 0, 8, None) == C.DORY_ERR_MODE   # policies differ
     for h in (src, dst, other, dst2):
         C.dory_kv_destroy(h)
+
+
+def test_selfspec_validated_before_enqueue():
+    """Self-speculative round: argument, mode, workspace and capacity errors
+    are found on the host before anything is enqueued; the cache length and
+    the accepted count are left as they were."""
+    m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
+    h = ctypes.c_void_p()
+    kvb = M.kv_bytes(synth.TINY, "per_loop", 2, 2, 16)
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, C.DORY_CACHE_PER_LOOP, 2, 2, 16, h),
+            "bind")
+    ws_bytes = M.workspace_bytes(synth.TINY, 2, 5)
+    n = ctypes.c_int32(-1)
+
+    def call(B=2, gamma=4, kd=1, kv_=2, mode=C.DORY_CACHE_PER_LOOP, wsb=ws_bytes, last=0x500000,
+             handle=h):
+        return C.dory_selfspec_step(m.handle, handle, ctypes.c_void_p(last) if last else None, B, gamma,
+                                    kd, kv_, mode, ctypes.c_void_p(0x700000), wsb,
+                                    ctypes.c_void_p(0x600000), ctypes.c_void_p(0x680000), n, None)
+    assert call(gamma=0) == C.DORY_ERR_ARG
+    assert call(kd=0) == C.DORY_ERR_ARG
+    assert call(kd=3, kv_=2) == C.DORY_ERR_ARG                 # k_draft above k_verify
+    assert call(last=0) == C.DORY_ERR_ARG
+    assert call(B=1) == C.DORY_ERR_ARG                         # B must equal the bound batch
+    assert call(kv_=3) == C.DORY_ERR_MODE                      # above k_max
+    assert call(mode=C.DORY_CACHE_LAST_LOOP) == C.DORY_ERR_MODE
+    assert call(wsb=16) == C.DORY_ERR_WORKSPACE
+    C.check(C.dory_kv_set_length(h, 12), "set_length")
+    assert call() == C.DORY_ERR_CAPACITY                       # 12 + 4 + 1 > 16
+    assert C.dory_kv_length(h) == 12 and n.value == -1
+    hl = ctypes.c_void_p()
+    kvl = M.kv_bytes(synth.TINY, "last_loop", 2, 2, 16)
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvl, C.DORY_CACHE_LAST_LOOP, 2, 2, 16,
+                           hl), "bind")
+    assert call(mode=C.DORY_CACHE_LAST_LOOP, handle=hl) == C.DORY_ERR_MODE   # per-loop caches only
+    for x in (h, hl):
+        C.dory_kv_destroy(x)
