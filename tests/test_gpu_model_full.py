@@ -275,3 +275,91 @@ def test_long_context_per_loop_decode_matches_prefill(full):
     assert kv.length == L
     del kv
     torch.cuda.empty_cache()
+
+
+def _top2_gap(logits):
+    srt = np.sort(logits, axis=1)
+    return srt[:, -1] - srt[:, -2]
+
+
+def test_selfspec_full_shape_matches_plain_decode(full):
+    """Self-speculative rounds at full shape (per-loop cache, 4 sequences,
+    40-token prompts, gamma 4, verify at k = 4, drafts at k = 1 and 4) emit
+    the tokens of plain greedy decoding at k = 4, up to the first position
+    whose top-2 logit gap in the plain run is below 0.05 (rounding of the
+    different launch shapes may pick the other token there)."""
+    _, gm, _ = full
+    B, T0, k, gamma, n = 4, 40, 4, 4, 8
+    toks = torch.from_numpy(synth.tokens(71, B, T0, SHAPE.vocab)).cuda()
+    kv = gm.kv_cache("per_loop", k, B, T0 + 16)
+    out = gm.prefill(kv, toks, k, logits=True, next_token=True)
+    t = out["next"]
+    plain, gaps = [t.cpu().numpy()], [_top2_gap(out["logits"].cpu().numpy())]
+    for _ in range(n - 1):
+        out = gm.decode_step(kv, t, k, logits=True, next_token=True)
+        t = out["next"]
+        plain.append(t.cpu().numpy())
+        gaps.append(_top2_gap(out["logits"].cpu().numpy()))
+    torch.cuda.synchronize()
+    plain, gaps = np.stack(plain, axis=1), np.stack(gaps, axis=1)
+    del kv
+    for kd in (1, k):
+        log(f"full-shape selfspec k_draft={kd}")
+        kv = gm.kv_cache("per_loop", k, B, T0 + 16)
+        last = gm.prefill(kv, toks, k, logits=False, next_token=True)["next"]
+        got, accepted = [last.cpu().numpy()[:, None]], 0
+        while sum(x.shape[1] for x in got) < n:
+            na, tk = gm.selfspec_step(kv, last, gamma, kd, k)
+            got.append(tk.cpu().numpy())
+            last = tk[:, -1].contiguous()
+            accepted += na
+        torch.cuda.synchronize()
+        spec = np.concatenate(got, axis=1)[:, :n]
+        compared = 0
+        for r in range(B):
+            for i in range(n):
+                if spec[r, i] != plain[r, i]:
+                    assert gaps[r, i] < 0.05, f"row {r} token {i}: {spec[r, i]} vs {plain[r, i]}"
+                    break
+                compared += 1
+                if gaps[r, i] < 0.05:
+                    break
+        log(f"  accepted drafts {accepted}, tokens compared {compared}")
+        assert compared >= B
+        if kd == k:
+            assert accepted > 0
+        del kv
+
+
+def test_prefix_copy_full_shape_continuation(full):
+    """Prefix caching at full shape: an 1100-token prefix (the 1024-row
+    sliding-window rings have wrapped) prefilled once for one sequence and
+    copied into two, then a 40-token suffix and one decode step, matches
+    prefilling the whole prompt for both sequences, bit for bit: the prefix
+    runs the large-M kernels either way (1,100 or 2,200 rows), which compute
+    every row the same way whatever the row count (no split-K), so the
+    copied entries equal the ones computed in place."""
+    _, gm, _ = full
+    B, n, T, k = 2, 1100, 40, 2
+    prefix = synth.tokens(72, 1, n, SHAPE.vocab)
+    rest = torch.from_numpy(synth.tokens(73, B, T + 1, SHAPE.vocab)).cuda()
+    ref_kv = gm.kv_cache("last_loop", k, B, n + T + 1)
+    gm.prefill(ref_kv, torch.from_numpy(np.repeat(prefix, B, axis=0)).cuda(), k, logits=False)
+    want = gm.prefill(ref_kv, rest[:, :T].contiguous(), k, logits=True, hidden=True)
+    want_d = gm.decode_step(ref_kv, rest[:, T].contiguous(), k, logits=True, next_token=False,
+                            hidden=True)
+    src = gm.kv_cache("last_loop", k, 1, n)
+    gm.prefill(src, torch.from_numpy(prefix).cuda(), k, logits=False)
+    dst = gm.kv_cache("last_loop", k, B, n + T + 1)
+    for b in range(B):
+        dst.copy_prefix_from(src, 0, b, n)
+    got = gm.prefill(dst, rest[:, :T].contiguous(), k, logits=True, hidden=True)
+    got_d = gm.decode_step(dst, rest[:, T].contiguous(), k, logits=True, next_token=False, hidden=True)
+    torch.cuda.synchronize()
+    for what, a, b in [("suffix hidden", got["hidden"], want["hidden"]),
+                       ("suffix logits", got["logits"], want["logits"]),
+                       ("decode hidden", got_d["hidden"], want_d["hidden"]),
+                       ("decode logits", got_d["logits"], want_d["logits"])]:
+        a, b = a.cpu().numpy(), b.cpu().numpy()
+        per_token_check(a, b.astype(np.float64), what)
+        np.testing.assert_array_equal(a, b, err_msg=what)
