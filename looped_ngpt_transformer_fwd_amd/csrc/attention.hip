@@ -417,8 +417,8 @@ attn_prefill_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ decode
 constexpr int DEC_NT = 256;
-constexpr int DEC_MAXK = 512;   // keys per split of full-attention layers, a multiple of 64
-constexpr int DEC_SWAK = 256;   // keys per split of sliding-window layers (more workgroups)
+constexpr int DEC_MAXK = 256;   // keys per split of full-attention layers, a multiple of 64
+constexpr int DEC_SWAK = 256;   // keys per split of sliding-window layers
 
 __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
   bf16x8 v;
@@ -637,7 +637,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 __global__ void __launch_bounds__(128)
 attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const uint16_t* gate,
                            uint16_t* z, RowLoops rl) {
-  __shared__ float wsc[1024];  // 2^(m_s - M) per split (nsplit <= 1024)
+  __shared__ float wsc[2048];  // 2^(m_s - M) per split (nsplit <= 2048)
   __shared__ float pm[128];    // per-thread partial maxima (blockDim = dh <= 128)
   const int bh = blockIdx.x, d = threadIdx.x;
   const int b = bh / n_q, h = bh % n_q;

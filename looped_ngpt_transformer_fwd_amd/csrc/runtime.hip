@@ -34,7 +34,7 @@ dory_status fail(dory_status s, const std::string& msg) {
 int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-constexpr int kMaxDecodeSplits = 1024;
+constexpr int kMaxDecodeSplits = 2048;
 constexpr int kMaxGemmSplit = 16;   // split-K partials for 64 < M < kLargeM
 constexpr int kMaxSkinnySplit = 32; // and for M <= 64 (weight-streaming path)
 
