@@ -311,3 +311,20 @@ def test_selfspec_validated_before_enqueue():
     assert call(mode=C.DORY_CACHE_LAST_LOOP, handle=hl) == C.DORY_ERR_MODE   # per-loop caches only
     for x in (h, hl):
         C.dory_kv_destroy(x)
+
+
+def test_decode_context_limit_rejected_before_enqueue():
+    """Decode attention covers at most 524,288 keys (2,048 splits of 256): a
+    decode step at position 524,288 is refused on the host."""
+    m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
+    h = ctypes.c_void_p()
+    kvb = M.kv_bytes(synth.TINY, "last_loop", 1, 1, 600000)
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, C.DORY_CACHE_LAST_LOOP, 1, 1,
+                           600000, h), "bind")
+    C.check(C.dory_kv_set_length(h, 524288), "set_length")
+    ws_bytes = M.workspace_bytes(synth.TINY, 1, 1)
+    assert C.dory_decode_step(m.handle, h, ctypes.c_void_p(0x500000), 1, 1, C.DORY_CACHE_LAST_LOOP,
+                              ctypes.c_void_p(0x700000), ws_bytes, None, None, None, None,
+                              None) == C.DORY_ERR_UNSUPPORTED
+    assert C.dory_kv_length(h) == 524288
+    C.dory_kv_destroy(h)
