@@ -192,7 +192,7 @@ dory_status dory_prefill(dory_model* m, dory_kv* kv, const int32_t* tokens, int3
 /* One decode step: one new token per sequence (tokens: device int32 [B]) at
  * position dory_kv_length(kv). Arguments as for dory_prefill with T = 1;
  * hidden is [B, d] and states [k, B, d]. The split-K decode attention
- * covers at most 524,288 keys: a step at a longer context returns
+ * covers at most 1,048,576 keys: a step at a longer context returns
  * DORY_ERR_UNSUPPORTED before anything is enqueued (prefill chunks have no
  * such limit). */
 dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,

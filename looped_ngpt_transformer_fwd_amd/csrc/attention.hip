@@ -417,8 +417,14 @@ attn_prefill_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ decode
 constexpr int DEC_NT = 256;
-constexpr int DEC_MAXK = 256;   // keys per split of full-attention layers, a multiple of 64
-constexpr int DEC_SWAK = 256;   // keys per split of sliding-window layers
+// Keys per split (multiples of 64): sliding-window layers and contexts up to
+// DEC_LONG keys use DEC_SWAK / DEC_MAXK (more workgroups in flight); longer
+// full-attention contexts use DEC_LONGK, which halves the partials that the
+// combine kernel merges per (sequence, head).
+constexpr int DEC_MAXK = 256;
+constexpr int DEC_SWAK = 256;
+constexpr int DEC_LONGK = 512;
+constexpr int64_t DEC_LONG = 65536;
 
 __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
   bf16x8 v;
@@ -691,10 +697,19 @@ hipError_t prefill_cfg(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+int decode_split_keys(int64_t lo, int64_t p, bool window) {
+  if (window) return DEC_SWAK;
+  return p + 1 - lo / 64 * 64 > DEC_LONG ? DEC_LONGK : DEC_MAXK;
+}
+
 template <int DH, int GRP>
 hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st) {
   dim3 grid(nsplit, a.n_kv, a.B);
-  if (a.window > 0)
+  const int64_t lo = a.window > 0 ? std::max<int64_t>(0, a.p0 - a.window + 1) : 0;
+  const int sk = decode_split_keys(lo, a.p0, a.window > 0);
+  if (sk == DEC_LONGK)
+    hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_LONGK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
+  else if (a.window > 0)
     hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_SWAK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
   else
     hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_MAXK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
@@ -723,7 +738,7 @@ int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit) {
 
 int decode_attn_pick_split(int64_t lo, int64_t p, bool window) {
   const int64_t base = lo / 64 * 64;
-  const int64_t sk = window ? DEC_SWAK : DEC_MAXK;
+  const int64_t sk = decode_split_keys(lo, p, window);
   const int64_t s = (p + 1 - base + sk - 1) / sk;
   return (int)(s < 1 ? 1 : s);
 }

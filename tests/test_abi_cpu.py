@@ -314,17 +314,18 @@ def test_selfspec_validated_before_enqueue():
 
 
 def test_decode_context_limit_rejected_before_enqueue():
-    """Decode attention covers at most 524,288 keys (2,048 splits of 256): a
-    decode step at position 524,288 is refused on the host."""
+    """Decode attention covers at most 1,048,576 keys (2,048 splits of 512 at
+    long contexts): a decode step at position 1,048,576 is refused on the
+    host."""
     m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
     h = ctypes.c_void_p()
-    kvb = M.kv_bytes(synth.TINY, "last_loop", 1, 1, 600000)
+    kvb = M.kv_bytes(synth.TINY, "last_loop", 1, 1, 1100000)
     C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, C.DORY_CACHE_LAST_LOOP, 1, 1,
-                           600000, h), "bind")
-    C.check(C.dory_kv_set_length(h, 524288), "set_length")
+                           1100000, h), "bind")
+    C.check(C.dory_kv_set_length(h, 1048576), "set_length")
     ws_bytes = M.workspace_bytes(synth.TINY, 1, 1)
     assert C.dory_decode_step(m.handle, h, ctypes.c_void_p(0x500000), 1, 1, C.DORY_CACHE_LAST_LOOP,
                               ctypes.c_void_p(0x700000), ws_bytes, None, None, None, None,
                               None) == C.DORY_ERR_UNSUPPORTED
-    assert C.dory_kv_length(h) == 524288
+    assert C.dory_kv_length(h) == 1048576
     C.dory_kv_destroy(h)
