@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import synth
 from looped_ngpt_transformer_fwd_amd import _lib as C
@@ -15,6 +16,14 @@ from looped_ngpt_transformer_fwd_amd import model as M
 from oracle import ref
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dory.h")
+
+# These checks hand fake device addresses to the compute calls and rely on the
+# host refusing them; with a visible device a regressed check would enqueue
+# kernels on those addresses, so the module runs on hosts without a GPU only.
+# (Counting devices does not initialise the runtime.)
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="host-validation checks with fake device pointers run "
+                                       "on GPU-less hosts only")
 
 
 def declared_functions():
@@ -159,12 +168,33 @@ def test_bind_rejects_small_buffer_and_bad_mode():
     assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n - 1, 0, 1, 2, 64, h) == \
         C.DORY_ERR_CAPACITY
     assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n, 7, 1, 2, 64, h) == C.DORY_ERR_MODE
-    # the attention kernels index a slab of head_dim x rows in 32 bits
+    # the attention kernels take positions in 31 bits (at most 2^24) and
+    # address a slab of rows x head_dim x 2 bytes with 32-bit offsets
     big = 1 << 24
     assert M.kv_bytes(synth.TINY, "last_loop", 1, 1, big) > 0
     assert M.kv_bytes(synth.TINY, "last_loop", 1, 1, big + 1) == 0
     assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), 1 << 40, 0, 1, 1, big + 1, h) == \
         C.DORY_ERR_ARG
+
+
+def test_bind_refuses_a_slab_of_2_pow_32_bytes():
+    """At head_dim 128 a full-attention slab of 2^24 rows is exactly 2^32
+    bytes, which 32-bit offsets cannot span: binding it is refused before
+    anything is enqueued, and 2^24 - 8 rows (the last multiple of 8 below)
+    are accepted."""
+    m = M.Model(synth.PAIR, _fake_tensor_map(synth.PAIR))
+    h = ctypes.c_void_p()
+    big = 1 << 24
+    assert M.kv_bytes(synth.PAIR, "last_loop", 1, 1, big) == 0
+    assert M.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 7) == 0   # rounds up to 2^24 rows
+    n = M.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 8)
+    assert n == ref.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 8)
+    assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), 1 << 40, 0, 1, 1, big, h) == \
+        C.DORY_ERR_ARG
+    assert "2^32" in C.dory_last_error()
+    assert not h.value
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), n, 0, 1, 1, big - 8, h), "bind")
+    C.dory_kv_destroy(h)
 
 
 def test_model_create_rejects_bad_configs():

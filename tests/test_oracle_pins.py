@@ -307,6 +307,108 @@ def test_attention_sublayer_invariant_to_position_shift():
     assert np.max(np.abs(q0 - q1)) > 1e-3
 
 
+# ---------------------------------------------------------------- R5 query-key transform
+
+def _head_norms(x):
+    return np.linalg.norm(x, axis=-1)
+
+
+def test_qkvg_uniform_scale_gives_per_head_norm_c():
+    """Reading R5 (section Architecture, query-key scale): with s_qk = c on
+    every channel, each head of q_hat and of k_hat has length c at every
+    token. A normalization over all heads jointly (or none) fails this."""
+    sh = synth.TINY
+    c = float(np.float32(1.3))         # the vector is stored in float32
+    m, _ = tiny_model(sh, overrides={"sub0.s_qk": np.full(sh.head_dim, c, np.float32)})
+    h = m.weight("embed")[synth.tokens(41, 2, 9, sh.vocab)]
+    pos = np.arange(9) + 5
+    q, k, v, g = m.qkvg(0, h, pos)
+    assert q.shape == (2, sh.n_q_heads, 9, sh.head_dim)
+    assert k.shape == (2, sh.n_kv_heads, 9, sh.head_dim)
+    np.testing.assert_allclose(_head_norms(q), c, rtol=1e-13)
+    np.testing.assert_allclose(_head_norms(k), c, rtol=1e-13)
+    # the pin is sensitive: a joint normalization of all heads (head norms
+    # c * |q_j| / |q|) departs from c by far more than rounding
+    raw = h @ m.weight("sub0.w_qkvg").T
+    qr = raw[..., :sh.d_q]
+    joint = c * qr / np.linalg.norm(qr, axis=-1, keepdims=True)
+    jn = np.linalg.norm(joint.reshape(2, 9, sh.n_q_heads, sh.head_dim), axis=-1)
+    assert np.max(np.abs(jn - c)) > 0.1
+
+
+def test_qkvg_scale_applied_after_rotation_and_norm():
+    """With a per-channel s_qk, q_hat / s_qk and k_hat / s_qk are unit vectors
+    per head: the scale multiplies the rotated, normalized head. Applying it
+    before the norm, or before the rotation (which mixes channel i with
+    channel i + dh/2), would leave these lengths away from 1."""
+    sh = synth.TINY
+    m, w = tiny_model(sh)
+    s_qk = m.weight("sub0.s_qk")
+    assert np.ptp(s_qk) > 0.3                     # a genuinely non-uniform scale
+    h = m.weight("embed")[synth.tokens(42, 1, 7, sh.vocab)]
+    pos = np.array([0, 1, 2, 50, 300, 1023, 4000])
+    q, k, _, _ = m.qkvg(0, h, pos)
+    np.testing.assert_allclose(_head_norms(q / s_qk), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(_head_norms(k / s_qk), 1.0, rtol=1e-13)
+    # scale before the norm: N(s * rope(q)) / s is not unit length
+    raw = (h @ m.weight("sub0.w_qkvg").T)[..., :sh.d_q]
+    qr = raw.reshape(1, 7, sh.n_q_heads, sh.head_dim).transpose(0, 2, 1, 3)
+    alt = ref.l2_normalize(s_qk * ref.rope(qr, pos, sh.rope_base_swa))
+    assert np.max(np.abs(_head_norms(alt / s_qk) - 1.0)) > 1e-2
+    # scale before the rotation: rope(s * N(q)) / s is not unit length
+    alt2 = ref.rope(s_qk * ref.l2_normalize(qr), pos, sh.rope_base_swa)
+    assert np.max(np.abs(_head_norms(alt2 / s_qk) - 1.0)) > 1e-2
+
+
+def test_qkvg_hand_built_weights_closed_form():
+    """Hand-built projection rows: with h = e_0 the projections are column 0
+    of w_qkvg. Each q and k head gets one nonzero channel pair (i, i + dh/2)
+    holding (a, b), so after the rotate-half RoPE (reading R4) the head is the
+    2-D rotation of (a, b) by p * base^(-2i/dh) in that pair, and after the
+    per-head norm and s_qk (reading R5) q_hat = s_qk * rotated / |(a, b)|.
+    v and g are column 0 of their row blocks unchanged. Distinct pairs and
+    values per head pin the row order q | k | v | gate, the head order, the
+    pair layout and the RoPE base of the sublayer's kind."""
+    sh = synth.TINY_REC_FULL        # sublayer 0 sliding-window, sublayer 4 full attention
+    d, dh, nq, nkv = sh.d_model, sh.head_dim, sh.n_q_heads, sh.n_kv_heads
+    half = dh // 2
+    nrows = 2 * sh.d_q + 2 * sh.d_kv
+    g_ = np.random.default_rng(43)
+    col = np.zeros(nrows)
+    pairs = {}
+    for j in range(nq + nkv):
+        i = (3 * j + 1) % half
+        a, b = g_.uniform(0.5, 2.0), g_.uniform(-2.0, 2.0)
+        r0 = j * dh                      # q heads first, then k heads (rows d_q ..)
+        col[r0 + i], col[r0 + i + half] = a, b
+        pairs[j] = (i, a, b)
+    vg = g_.standard_normal(sh.d_kv + sh.d_q)
+    col[sh.d_q + sh.d_kv:] = vg
+    wmat = np.zeros((nrows, d))
+    wmat[:, 0] = col
+    s_qk = g_.uniform(0.5, 1.5, dh)
+    for sub, base in ((0, sh.rope_base_swa), (4, sh.rope_base_full)):
+        m = ref.OracleModel(sh, lambda n, sub=sub: {f"sub{sub}.w_qkvg": wmat,
+                                                     f"sub{sub}.s_qk": s_qk}[n])
+        h = np.zeros((1, 3, d))
+        h[..., 0] = 1.0
+        pos = np.array([0, 3, 777])
+        q, k, v, gt = m.qkvg(sub, h, pos)
+        for j in range(nq + nkv):
+            i, a, b = pairs[j]
+            out = q[0, j] if j < nq else k[0, j - nq]
+            for t, p in enumerate(pos):
+                ang = p * base ** (-2.0 * i / dh)
+                want = np.zeros(dh)
+                want[i] = a * math.cos(ang) - b * math.sin(ang)
+                want[i + half] = b * math.cos(ang) + a * math.sin(ang)
+                want *= s_qk / math.hypot(a, b)
+                np.testing.assert_allclose(out[t], want, atol=1e-14)
+        for t in range(3):
+            np.testing.assert_array_equal(v[0, :, t].reshape(-1), vg[:sh.d_kv])
+            np.testing.assert_array_equal(gt[0, t], vg[sh.d_kv:])
+
+
 # ---------------------------------------------------------------- P7 scale cancellation
 
 def test_output_projection_scale_cancels():
