@@ -351,10 +351,59 @@ typedef enum dory_kernel_class {
 dory_status dory_profile_begin(dory_model* m, int32_t max_launches);
 dory_status dory_profile_end(dory_model* m, int64_t* counts, double* ms);
 
-/* Mask dump for bit-exact tests: out (device uint8 [T, L + T]) receives 1
- * where the attention kernels treat key position u as visible to the query
- * at position L + t (u <= L + t, and L + t - u < window unless window is 0). */
-dory_status dory_debug_mask(int32_t window, int64_t L, int32_t T, uint8_t* out, void* stream);
+/* Greedy selection (greedy decoding of the workload descriptions; reading:
+ * the lowest index wins ties): out[r] = argmax over i < n of logits[r * n + i]
+ * for each of `rows` rows. logits: device fp32 [rows, n]; out: device int32
+ * [rows]. NaN entries never win; a row without a value above -inf yields 0.
+ * The same kernel as the `next` output of the compute calls. Asynchronous on
+ * `stream`. */
+dory_status dory_greedy(const float* logits, int32_t rows, int32_t n, int32_t* out, void* stream);
+
+/* ---- Debug probes of the production kernels (bit-exact tests) ------------
+ * These run the attention kernels and index computations of the compute
+ * calls on probe inputs; they exist so that tests can read the mask and the
+ * cache rows those kernels actually use.
+ *
+ * Cache rows (section Last-Loop KV Caching; the ring of a sliding-window
+ * slot): rows_out[i] (device int64 [n]) receives the row of position
+ * pos_a + i in the slots of `sublayer`, evaluated on the device by the
+ * function every cache-writing kernel uses (position mod ring for a
+ * sliding-window slot, the position for a full-attention slot).
+ * 0 <= pos_a, pos_a + n <= max_seq. */
+dory_status dory_debug_kv_slots(const dory_kv* kv, int32_t sublayer, int64_t pos_a, int64_t n,
+                                int64_t* rows_out, void* stream);
+
+/* Runs the attention of attention sublayer `sublayer` (its kind: sliding
+ * window or full, section Architecture; window of section Long-Context
+ * Extension) exactly as a step over positions p0 .. p0 + T - 1 does, on the
+ * caller's inputs: q_hat bf16 [B][n_q][T][head_dim] (already transformed),
+ * the step's own keys k_new and values v_new bf16 [B][n_kv][T][head_dim], the
+ * gate sigma(g) bf16 [B * T][n_q * head_dim]; z (bf16, same shape as the
+ * gate) receives the gated attention output. B is the cache's bound batch.
+ * Keys below p0 are read from the slot (`loop` selects it under per-loop
+ * caching) as the step would read them: the caller writes them through
+ * dory_kv_slot() in its layout. T = 1 runs the decode kernels (the token's
+ * K/V are first stored in the slot, as a decode step stores them); T > 1 the
+ * prefill kernels (the slot is not written). The cache length is not used or
+ * changed; p0 + T <= max_seq. ws: at least dory_workspace_bytes(cfg, B, T). */
+dory_status dory_debug_attention(dory_model* m, dory_kv* kv, int32_t sublayer, int32_t loop,
+                                 int64_t p0, int32_t T, const void* q_hat, const void* k_new,
+                                 const void* v_new, const void* gate, void* z, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* Mask dump (bit-exact tests): out (device uint16 [B][n_q][T][p0 + T])
+ * receives the weight, as a bf16 bit pattern, that the attention kernels of
+ * `sublayer` give key position u for the query at position p0 + t of query
+ * head h when all scores are equal (zero queries and keys): 1 / (number of
+ * visible keys) at the visible keys and 0 at the others, so its nonzero
+ * pattern is the mask the kernels apply. It is read off the kernels'
+ * outputs, with one-hot values probing head_dim keys at a time
+ * (ceil((p0 + T) / head_dim) runs of the kernels of dory_debug_attention,
+ * decode kernels for T = 1). Overwrites the contents of the slot (`loop`
+ * under per-loop caching) and the workspace; the cache length is unchanged.
+ * Arguments and errors as for dory_debug_attention. */
+dory_status dory_debug_mask(dory_model* m, dory_kv* kv, int32_t sublayer, int32_t loop, int64_t p0,
+                            int32_t T, void* ws, size_t ws_bytes, uint16_t* out, void* stream);
 
 const char* dory_status_string(dory_status s);
 const char* dory_last_error(void);

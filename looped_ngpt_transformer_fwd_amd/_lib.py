@@ -82,7 +82,10 @@ SIGNATURES = {
     "dory_decode_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_prefill_rows": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_decode_step_rows": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
-    "dory_debug_mask": (_I32, [_I32, _I64, _I32, _P, _P]),
+    "dory_greedy": (_I32, [_P, _I32, _I32, _P, _P]),
+    "dory_debug_kv_slots": (_I32, [_P, _I32, _I64, _I64, _P, _P]),
+    "dory_debug_attention": (_I32, [_P, _P, _I32, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dory_debug_mask": (_I32, [_P, _P, _I32, _I32, _I64, _I32, _P, _SZ, _P, _P]),
     "dory_kv_set_length": (_I32, [_P, _I64]),
     "dory_kv_copy_prefix": (_I32, [_P, _I32, _P, _I32, _I64, _P]),
     "dory_profile_begin": (_I32, [_P, _I32]),
@@ -195,8 +198,22 @@ def dory_decode_step_rows(m, kv, tokens, B, k_rows, mode, ws, ws_bytes, logits, 
                                        hidden, states, stream)
 
 
-def dory_debug_mask(window, L, T, out, stream):
-    return lib().dory_debug_mask(window, L, T, out, stream)
+def dory_greedy(logits, rows, n, out, stream):
+    return lib().dory_greedy(logits, rows, n, out, stream)
+
+
+def dory_debug_kv_slots(kv, sublayer, pos_a, n, rows_out, stream):
+    return lib().dory_debug_kv_slots(kv, sublayer, pos_a, n, rows_out, stream)
+
+
+def dory_debug_attention(m, kv, sublayer, loop, p0, T, q_hat, k_new, v_new, gate, z, ws, ws_bytes,
+                         stream):
+    return lib().dory_debug_attention(m, kv, sublayer, loop, p0, T, q_hat, k_new, v_new, gate, z, ws,
+                                      ws_bytes, stream)
+
+
+def dory_debug_mask(m, kv, sublayer, loop, p0, T, ws, ws_bytes, out, stream):
+    return lib().dory_debug_mask(m, kv, sublayer, loop, p0, T, ws, ws_bytes, out, stream)
 
 
 def dory_kv_set_length(kv, length):

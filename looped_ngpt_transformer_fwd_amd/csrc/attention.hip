@@ -505,7 +505,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int64_t u = u0 + 8 * (r >> 2) + 4 * t + (r & 3);
-      const int64_t row = a.ring > 0 ? u % a.ring : u;
+      const int64_t row = cache_row(u, a.ring);
       const uint32_t off = (u >= ua && u < ub) ? (uint32_t)(row * DH + 8 * G) * 2u : OOB;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -517,7 +517,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
     // their first key is a cached position
     const int64_t uv = u0 + 8 * G;
     const bool vany = uv + 7 >= ua && uv < ub;
-    const uint32_t voff = vany ? (uint32_t)((a.ring > 0 ? uv % a.ring : uv) * 2 + r * a.c_rows * 2) : OOB;
+    const uint32_t voff = vany ? (uint32_t)(cache_row(uv, a.ring) * 2 + r * a.c_rows * 2) : OOB;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       auto v = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, (int)(16 * nb * a.c_rows * 2), 0);

@@ -68,10 +68,11 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Attention visibility: a query at position p sees key u iff u <= p and, for
-// a sliding-window layer (window > 0), p - u < window.
-__device__ __forceinline__ bool key_visible(int64_t p, int64_t u, int window) {
-  return u <= p && (window == 0 || p - u < window);
+// Row of position u in a cache slot: u mod ring for a sliding-window slot
+// stored as a ring (ring > 0), u itself for a linear slot. Every kernel that
+// stores or copies cache entries by position computes the row here.
+__device__ __forceinline__ int64_t cache_row(int64_t u, int64_t ring) {
+  return ring > 0 ? u % ring : u;
 }
 
 }  // namespace dory

@@ -177,9 +177,24 @@ hipError_t launch_vt_zero_cols(uint16_t* vf, int64_t f_rows, int B, int n_kv, in
 // Greedy argmax over rows of [rows, n] fp32, lowest index on ties.
 hipError_t launch_argmax(const float* x, int rows, int n, int32_t* out, hipStream_t st);
 
-// Visibility predicate dump: out[t * L + u] = 1 iff key u is visible to the
-// query at position p0 + t (u < p0 + C), for window (0 = full attention).
-hipError_t launch_debug_mask(int window, int64_t p0, int C, uint8_t* out, hipStream_t st);
+// ------------------------------------------------------------ debug dumps
+// n 16-bit values set to v.
+hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t st);
+// K and V of positions p0 .. p0 + T - 1 ([B][n_kv][T][dh] bf16) stored where
+// the query/key transform stores them (see QkDest).
+hipError_t launch_kv_place(const uint16_t* k, const uint16_t* v, int B, int n_kv, int T, int dh,
+                           int64_t p0, QkDest dst, hipStream_t st);
+// One-hot V probe values for positions [ua, ub): 1.0 at head dimension
+// u - first, 0 elsewhere; cached positions (below p0, and held by the ring)
+// into the cache slot's V^T, the step's positions into vnew [B][n_kv][T][dh].
+hipError_t launch_mask_probe_v(uint16_t* vc, int64_t c_rows, int64_t ring, uint16_t* vnew, int B,
+                               int T, int n_kv, int dh, int64_t p0, int64_t ua, int64_t ub,
+                               int64_t first, hipStream_t st);
+// out [B][n_q][T][L] at key columns first .. first + dh - 1: the bf16 z values.
+hipError_t launch_mask_extract(const uint16_t* z, int B, int T, int n_q, int dh, int64_t L,
+                               int64_t first, uint16_t* out, hipStream_t st);
+// out[i] = cache row of position pos_a + i in a slot with this ring.
+hipError_t launch_slot_rows(int64_t pos_a, int64_t n, int64_t ring, int64_t* out, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

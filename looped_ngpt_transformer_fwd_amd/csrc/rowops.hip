@@ -2,7 +2,10 @@
 // fused nGPT normalize-and-update (optionally with the loop-boundary
 // re-injection fused in), the query/key transform (RoPE, per-head L2 norm,
 // s_qk) with the K/V placement, KV-cache copies, SwiGLU over split partials,
-// greedy argmax and the mask dump used by the bit-exact tests.
+// greedy argmax, and the probe kernels of the debug dumps (fills, K/V
+// placement, one-hot mask probes, slot rows).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -207,8 +210,7 @@ qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq
   const int dq = nq * dh, dkv = nkv * dh;
   const int N = 2 * dq + 2 * dkv;
   const float* row = P + (int64_t)m * N;
-  int64_t krow = pos - kv.pos_origin;
-  if (kv.ring > 0) krow %= kv.ring;
+  const int64_t krow = cache_row(pos - kv.pos_origin, kv.ring);
   const int per_block = NT_ROW / half;
   const int ngroups = (nq + nkv + per_block - 1) / per_block;
   if ((int)blockIdx.y < ngroups) {
@@ -265,7 +267,7 @@ __global__ void prefix_copy_kernel(const uint16_t* kc, const uint16_t* vc, int64
   const int64_t pos = pos_a + blockIdx.x;
   const int g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int64_t bg = (int64_t)b * nkv + g;
-  const int64_t crow = ring > 0 ? pos % ring : pos;
+  const int64_t crow = cache_row(pos, ring);
   const int64_t frow = blockIdx.x;
   kf[(bg * f_rows + frow) * dh + d] = kc[(bg * c_rows + crow) * dh + d];
   vf[(bg * dh + d) * f_rows + frow] = vc[(bg * dh + d) * c_rows + crow];
@@ -278,7 +280,7 @@ __global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t 
   const int g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   if (rl.k_rows && rl.k_rows[b] != rl.loop + 1) return;  // not this sequence's last loop
   const int64_t bg = (int64_t)b * nkv + g;
-  const int64_t crow = ring > 0 ? pos % ring : pos;
+  const int64_t crow = cache_row(pos, ring);
   const int64_t frow = pos - f_origin;
   kc[(bg * c_rows + crow) * dh + d] = kf[(bg * f_rows + frow) * dh + d];
   vc[(bg * dh + d) * c_rows + crow] = vf[(bg * dh + d) * f_rows + frow];
@@ -302,8 +304,8 @@ __global__ void kv_copy_kernel(const uint16_t* sk, const uint16_t* sv, int64_t s
     const int64_t pos = base + i / cpr;
     if (pos < pos_a || pos >= pos_b) continue;
     const int c = i % cpr;
-    const int64_t sr = s_ring > 0 ? pos % s_ring : pos;
-    const int64_t dr = d_ring > 0 ? pos % d_ring : pos;
+    const int64_t sr = cache_row(pos, s_ring);
+    const int64_t dr = cache_row(pos, d_ring);
     *reinterpret_cast<uint4*>(dk + (dbg * d_rows + dr) * dh + c * 8) =
         *reinterpret_cast<const uint4*>(sk + (sbg * s_rows + sr) * dh + c * 8);
   }
@@ -313,14 +315,14 @@ __global__ void kv_copy_kernel(const uint16_t* sk, const uint16_t* sv, int64_t s
     const uint16_t* srow = sv + (sbg * dh + d) * s_rows;
     uint16_t* drow = dv + (dbg * dh + d) * d_rows;
     if (p0 >= pos_a && p0 + 8 <= pos_b) {
-      const int64_t sr = s_ring > 0 ? p0 % s_ring : p0;
-      const int64_t dr = d_ring > 0 ? p0 % d_ring : p0;
+      const int64_t sr = cache_row(p0, s_ring);
+      const int64_t dr = cache_row(p0, d_ring);
       *reinterpret_cast<uint4*>(drow + dr) = *reinterpret_cast<const uint4*>(srow + sr);
     } else {
       for (int e = 0; e < 8; ++e) {
         const int64_t pos = p0 + e;
         if (pos < pos_a || pos >= pos_b) continue;
-        drow[d_ring > 0 ? pos % d_ring : pos] = srow[s_ring > 0 ? pos % s_ring : pos];
+        drow[cache_row(pos, d_ring)] = srow[cache_row(pos, s_ring)];
       }
     }
   }
@@ -375,11 +377,58 @@ __global__ void __launch_bounds__(NT_ARG) argmax_kernel(const float* x, int n, i
   }
 }
 
-__global__ void debug_mask_kernel(int window, int64_t p0, int C, uint8_t* out) {
-  const int64_t L = p0 + C;
-  const int t = blockIdx.x;
-  for (int64_t u = threadIdx.x; u < L; u += blockDim.x)
-    out[(int64_t)t * L + u] = key_visible(p0 + t, u, window) ? 1 : 0;
+__global__ void fill_u16_kernel(uint16_t* p, int64_t n, uint16_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// K and V of positions p0 .. p0 + T - 1 given as [B][n_kv][T][dh] go to the
+// places the query/key transform stores them (K rows and V^T columns of
+// QkDest, row cache_row(p0 + t - pos_origin, ring)). grid (T, n_kv, B),
+// block dh.
+__global__ void kv_place_kernel(const uint16_t* k, const uint16_t* v, int T, int nkv, int dh,
+                                int64_t p0, QkDest dst) {
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int64_t bg = (int64_t)b * nkv + g;
+  const int64_t row = cache_row(p0 + t - dst.pos_origin, dst.ring);
+  const int64_t src = (bg * T + t) * dh + d;
+  dst.kbase[(bg * dst.k_rows + row) * dh + d] = k[src];
+  dst.vbase[(bg * dh + d) * dst.v_cols + row] = v[src];
+}
+
+// Mask probe values: for positions u in [ua, ub), V entries become one-hot,
+// 1.0 at head dimension u - first (when that lies in [0, dh)) and 0
+// elsewhere. Cached positions (u < p0, and u >= p0 - ring for a ring) are
+// written to the V^T column of their cache row; positions p0 .. p0 + T - 1 to
+// vnew [B][n_kv][T][dh]. grid (ub - ua, n_kv, B), block dh.
+__global__ void mask_probe_v_kernel(uint16_t* vc, int64_t c_rows, int64_t ring, uint16_t* vnew,
+                                    int T, int nkv, int dh, int64_t p0, int64_t ua, int64_t first) {
+  const int64_t u = ua + blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int64_t bg = (int64_t)b * nkv + g;
+  const uint16_t val = (u - first == d) ? (uint16_t)0x3F80 : (uint16_t)0;
+  if (u < p0) {
+    if (ring > 0 && u < p0 - ring) return;  // no longer held by the ring
+    vc[(bg * dh + d) * c_rows + cache_row(u, ring)] = val;
+  } else if (u < p0 + T) {
+    vnew[(bg * T + (u - p0)) * dh + d] = val;
+  }
+}
+
+// out[((b * nq + h) * T + t) * L + first + d] = z[b * T + t][h * dh + d] (the
+// bf16 weight of key first + d) for first + d < L. grid (B * T, nq), block dh.
+__global__ void mask_extract_kernel(const uint16_t* z, int T, int nq, int dh, int64_t L,
+                                    int64_t first, uint16_t* out) {
+  const int bt = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int b = bt / T, t = bt - b * T;
+  if (first + d >= L) return;
+  out[(((int64_t)b * nq + h) * T + t) * L + first + d] = z[(int64_t)bt * nq * dh + h * dh + d];
+}
+
+__global__ void slot_rows_kernel(int64_t pos_a, int64_t n, int64_t ring, int64_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = cache_row(pos_a + i, ring);
 }
 
 }  // namespace
@@ -513,8 +562,39 @@ hipError_t launch_argmax(const float* x, int rows, int n, int32_t* out, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_debug_mask(int window, int64_t p0, int C, uint8_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(debug_mask_kernel, dim3(C), dim3(256), 0, st, window, p0, C, out);
+hipError_t launch_fill_u16(uint16_t* p, int64_t n, uint16_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(fill_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_place(const uint16_t* k, const uint16_t* v, int B, int n_kv, int T, int dh,
+                           int64_t p0, QkDest dst, hipStream_t st) {
+  hipLaunchKernelGGL(kv_place_kernel, dim3(T, n_kv, B), dim3(dh), 0, st, k, v, T, n_kv, dh, p0, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_probe_v(uint16_t* vc, int64_t c_rows, int64_t ring, uint16_t* vnew, int B,
+                               int T, int n_kv, int dh, int64_t p0, int64_t ua, int64_t ub,
+                               int64_t first, hipStream_t st) {
+  if (ub <= ua) return hipSuccess;
+  hipLaunchKernelGGL(mask_probe_v_kernel, dim3((unsigned)(ub - ua), n_kv, B), dim3(dh), 0, st, vc,
+                     c_rows, ring, vnew, T, n_kv, dh, p0, ua, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_extract(const uint16_t* z, int B, int T, int n_q, int dh, int64_t L,
+                               int64_t first, uint16_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(mask_extract_kernel, dim3(B * T, n_q), dim3(dh), 0, st, z, T, n_q, dh, L, first,
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_rows(int64_t pos_a, int64_t n, int64_t ring, int64_t* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pos_a, n,
+                     ring, out);
   return hipGetLastError();
 }
 

@@ -344,6 +344,48 @@ struct UpdateOpts {
   float* aux = nullptr;      // copy of the post-update value
 };
 
+// The attention of one sublayer over the step's q_hat (grouped-query,
+// sliding-window or causal by `full`), gated into z. Prefill reads the step's
+// own K/V from the fresh buffers, rows counted from f_origin (the step's first
+// position rounded down to 8), after copying the cached positions
+// [f_origin, p0) in front of them and zeroing the V^T columns past the step's
+// last key up to the next multiple of 8 (the kernel reads whole 8-key
+// chunks); keys below f_origin come from the cache slot. Decode reads the
+// cache slot only: the token's K/V are stored there first.
+dory_status attend(Ctx& c, const SlotPtr& sp, bool full, const uint16_t* q, const uint16_t* gate,
+                   uint16_t* z) {
+  const Shape& s = c.s;
+  AttnArgs aa{};
+  aa.q = q;
+  aa.kc = sp.k; aa.vc = sp.v; aa.c_rows = sp.rows; aa.ring = sp.ring;
+  aa.gate = gate; aa.z = z;
+  aa.B = c.B; aa.C = c.T; aa.n_q = s.nq; aa.n_kv = s.nkv; aa.dh = s.dh;
+  aa.p0 = c.p0; aa.window = full ? 0 : s.W; aa.scale = (float)s.scale;
+  aa.rl = c.rl;
+  if (c.T == 1) {
+    const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
+    const int nsd = decode_attn_pick_split(lo, c.p0, !full);  // <= kMaxDecodeSplits (checked up front)
+    PROF(c, DORY_K_ATTN);
+    HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
+    return DORY_OK;
+  }
+  const int64_t f_origin = c.p0 / 8 * 8;
+  {
+    const int64_t vend = c.p0 + c.T - f_origin;
+    PROF(c, DORY_K_KV_WRITE);
+    HIPCHK(launch_vt_zero_cols(c.vf(), c.L.f_rows, c.B, s.nkv, s.dh, vend, (vend + 7) / 8 * 8, c.st));
+  }
+  if (c.p0 > f_origin) {
+    PROF(c, DORY_K_KV_WRITE);
+    HIPCHK(launch_prefix_copy(sp.k, sp.v, sp.rows, sp.ring, c.B, s.nkv, s.dh, f_origin, c.p0,
+                              c.kf(), c.vf(), c.L.f_rows, c.st));
+  }
+  aa.kf = c.kf(); aa.vf = c.vf(); aa.f_rows = c.L.f_rows; aa.f_origin = f_origin;
+  PROF(c, DORY_K_ATTN);
+  HIPCHK(launch_attn_prefill(aa, c.st));
+  return DORY_OK;
+}
+
 dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const UpdateOpts& uo) {
   const Shape& s = c.s;
   const dory_sublayer_weights& w = c.m->sub[i];
@@ -370,69 +412,28 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     st = gemm_f32(c, c.h16(), s.d, wsel(c, i, 0, w.w_qkvg), s.nqkvg(), s.d, c.M, &ns,
                   DORY_K_GEMM_QKVG);
     if (st != DORY_OK) return st;
-  }
-  const int64_t split_stride = c.M * s.nqkvg();
-
-  AttnArgs aa{};
-  aa.q = c.qh();
-  aa.kc = sp.k; aa.vc = sp.v; aa.c_rows = sp.rows; aa.ring = sp.ring;
-  aa.gate = c.gate(); aa.z = c.z();
-  aa.B = c.B; aa.C = c.T; aa.n_q = s.nq; aa.n_kv = s.nkv; aa.dh = s.dh;
-  aa.p0 = c.p0; aa.window = full ? 0 : s.W; aa.scale = (float)s.scale;
-  aa.rl = c.rl;
-
-  if (c.T == 1) {
+    const int64_t split_stride = c.M * s.nqkvg();
     // decode: the current token's K/V go straight into the cache slot (the
     // last-loop rule read literally: overwrite at every loop), then the
-    // attention reads the cache only
-    QkDest kd{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring};
-    {
-      PROF(c, DORY_K_QK);
-      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, 1, c.p0, s.nq, s.nkv, s.dh,
+    // attention reads the cache only; prefill: the step's K/V go to the
+    // fresh buffers
+    const QkDest kd = c.T == 1 ? QkDest{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring}
+                               : QkDest{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
+    PROF(c, DORY_K_QK);
+    HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh,
                           c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
-                          c.gate(), c.st, c.rl));
-    }
-    const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
-    const int nsd = decode_attn_pick_split(lo, c.p0, !full);  // <= kMaxDecodeSplits (checked up front)
-    PROF(c, DORY_K_ATTN);
-    HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
-  } else {
-    // prefill: fresh K/V of the step live in the workspace, rows counted from
-    // f_origin (the step's first position rounded down to a multiple of 8);
-    // cached positions [f_origin, p0) are copied in front of them
-    if (!c.fused_qkv()) {
-      QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
-      PROF(c, DORY_K_QK);
-      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh,
-                            c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
-                            c.gate(), c.st));
-    }
-    {
-      // the attention reads whole 8-key V chunks: zero the columns past the
-      // step's last key up to the chunk boundary
-      const int64_t vend = c.p0 + c.T - f_origin;
-      PROF(c, DORY_K_KV_WRITE);
-      HIPCHK(launch_vt_zero_cols(c.vf(), c.L.f_rows, c.B, s.nkv, s.dh, vend, (vend + 7) / 8 * 8, c.st));
-    }
-    if (c.p0 > f_origin) {
-      PROF(c, DORY_K_KV_WRITE);
-      HIPCHK(launch_prefix_copy(sp.k, sp.v, sp.rows, sp.ring, c.B, s.nkv, s.dh, f_origin, c.p0,
-                                c.kf(), c.vf(), c.L.f_rows, c.st));
-    }
-    aa.kf = c.kf(); aa.vf = c.vf(); aa.f_rows = c.L.f_rows; aa.f_origin = f_origin;
-    {
-      PROF(c, DORY_K_ATTN);
-      HIPCHK(launch_attn_prefill(aa, c.st));
-    }
-    if (write) {
-      PROF(c, DORY_K_KV_WRITE);
-      // persistent store after the step's attention; a ring keeps only the
-      // newest `ring` positions
-      int64_t pa = c.p0;
-      if (sp.ring > 0) pa = std::max<int64_t>(pa, c.p0 + c.T - sp.ring);
-      HIPCHK(launch_kv_write(c.kf(), c.vf(), c.L.f_rows, f_origin, c.B, s.nkv, s.dh, pa,
-                             c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st, c.rl));
-    }
+                          c.gate(), c.st, c.T == 1 ? c.rl : RowLoops()));
+  }
+  st = attend(c, sp, full, c.qh(), c.gate(), c.z());
+  if (st != DORY_OK) return st;
+  if (c.T > 1 && write) {
+    PROF(c, DORY_K_KV_WRITE);
+    // persistent store after the step's attention; a ring keeps only the
+    // newest `ring` positions
+    int64_t pa = c.p0;
+    if (sp.ring > 0) pa = std::max<int64_t>(pa, c.p0 + c.T - sp.ring);
+    HIPCHK(launch_kv_write(c.kf(), c.vf(), c.L.f_rows, f_origin, c.B, s.nkv, s.dh, pa,
+                           c.p0 + c.T, sp.k, sp.v, sp.rows, sp.ring, c.st, c.rl));
   }
   bool y16 = false;
   st = gemm_f32(c, c.z(), s.dq(), wsel(c, i, 1, w.w_o), s.d, s.dq(), c.M, &ns, DORY_K_GEMM_O, &y16);
@@ -1079,11 +1080,141 @@ dory_status dory_profile_end(dory_model* m, int64_t* counts, double* ms) {
   return st;
 }
 
-dory_status dory_debug_mask(int32_t window, int64_t L, int32_t T, uint8_t* out, void* stream) {
-  if (!out || T < 1 || L < 0 || window < 0) return fail(DORY_ERR_ARG, "bad mask arguments");
-  hipError_t e = launch_debug_mask(window, L, T, out, reinterpret_cast<hipStream_t>(stream));
+dory_status dory_greedy(const float* logits, int32_t rows, int32_t n, int32_t* out, void* stream) {
+  if (!logits || !out) return fail(DORY_ERR_ARG, "logits and out must be non-NULL");
+  if (rows < 1 || n < 1) return fail(DORY_ERR_ARG, "rows and n must be >= 1");
+  hipError_t e = launch_argmax(logits, rows, n, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DORY_ERR_HIP, hipGetErrorString(e));
   return DORY_OK;
+}
+
+dory_status dory_debug_kv_slots(const dory_kv* kv, int32_t sublayer, int64_t pos_a, int64_t n,
+                                int64_t* rows_out, void* stream) {
+  if (!kv || !rows_out) return fail(DORY_ERR_ARG, "cache and rows_out must be non-NULL");
+  const Shape& s = kv->m->s;
+  if (sublayer < 0 || sublayer >= s.nsub() || kv->m->kinds[sublayer] == DORY_LAYER_MLP)
+    return fail(DORY_ERR_ARG, "not an attention sublayer");
+  if (pos_a < 0 || n < 1 || pos_a + n > kv->max_seq)
+    return fail(DORY_ERR_ARG, "positions outside [0, max_seq)");
+  hipError_t e = launch_slot_rows(pos_a, n, kv->ring[sublayer], rows_out,
+                                  reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DORY_ERR_HIP, hipGetErrorString(e));
+  return DORY_OK;
+}
+
+namespace {
+
+// Shared checks of the attention probes: an attention sublayer's slot of a
+// valid cache, the step's positions within max_seq, a large enough
+// workspace, and a decode context within the split limit.
+dory_status probe_check(const dory_model* m, const dory_kv* kv, int32_t sublayer, int32_t loop,
+                        int64_t p0, int32_t T, void* ws, size_t ws_bytes, SlotPtr* sp, bool* full) {
+  if (!m || !kv || !ws) return fail(DORY_ERR_ARG, "model, cache and workspace must be non-NULL");
+  if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
+  if (kv->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure; call dory_kv_reset");
+  const Shape& s = m->s;
+  if (sublayer < 0 || sublayer >= s.nsub() || m->kinds[sublayer] == DORY_LAYER_MLP)
+    return fail(DORY_ERR_ARG, "not an attention sublayer");
+  int slot = 0;
+  if (kv->nslots[sublayer] > 1) {
+    if (loop < 0 || loop >= kv->nslots[sublayer]) return fail(DORY_ERR_ARG, "loop out of range");
+    slot = loop;
+  }
+  if (T < 1 || p0 < 0) return fail(DORY_ERR_ARG, "need T >= 1 and p0 >= 0");
+  if (p0 + T > kv->max_seq) return fail(DORY_ERR_CAPACITY, "p0 + T exceeds max_seq");
+  if (ws_bytes < plan_ws(s, kv->batch, T).total)
+    return fail(DORY_ERR_WORKSPACE, "workspace smaller than dory_workspace_bytes(batch, T)");
+  *full = m->kinds[sublayer] == DORY_LAYER_ATTN_FULL;
+  if (T == 1) {
+    const int64_t lo = *full ? 0 : std::max<int64_t>(0, p0 - s.W + 1);
+    if (decode_attn_pick_split(lo, p0, !*full) > kMaxDecodeSplits)
+      return fail(DORY_ERR_UNSUPPORTED, "context too long for decode attention splits");
+  }
+  *sp = slot_ptr(kv, sublayer, slot);
+  return DORY_OK;
+}
+
+// Where the step's own K/V go before the attention: the cache row of p0 for
+// decode (as the decode step stores them), the fresh buffers for prefill.
+QkDest probe_dest(const Ctx& c, const SlotPtr& sp) {
+  if (c.T == 1) return QkDest{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring};
+  return QkDest{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, c.p0 / 8 * 8, 0};
+}
+
+}  // namespace
+
+dory_status dory_debug_attention(dory_model* m, dory_kv* kv, int32_t sublayer, int32_t loop,
+                                 int64_t p0, int32_t T, const void* q_hat, const void* k_new,
+                                 const void* v_new, const void* gate, void* z, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  SlotPtr sp;
+  bool full = false;
+  dory_status st = probe_check(m, kv, sublayer, loop, p0, T, ws, ws_bytes, &sp, &full);
+  if (st != DORY_OK) return st;
+  if (!q_hat || !k_new || !v_new || !gate || !z)
+    return fail(DORY_ERR_ARG, "q_hat, k_new, v_new, gate and z must be non-NULL");
+  const int B = kv->batch;
+  Ctx c{m, kv, m->s, B, T, (int64_t)B * T, p0, reinterpret_cast<uint8_t*>(ws),
+        plan_ws(m->s, B, T), reinterpret_cast<hipStream_t>(stream)};
+  const Shape& s = m->s;
+  hipError_t e = launch_kv_place(reinterpret_cast<const uint16_t*>(k_new),
+                                 reinterpret_cast<const uint16_t*>(v_new), B, s.nkv, T, s.dh, p0,
+                                 probe_dest(c, sp), c.st);
+  if (e != hipSuccess) {
+    kv->invalid = true;
+    return fail(DORY_ERR_HIP, hipGetErrorString(e));
+  }
+  st = attend(c, sp, full, reinterpret_cast<const uint16_t*>(q_hat),
+              reinterpret_cast<const uint16_t*>(gate), reinterpret_cast<uint16_t*>(z));
+  if (st == DORY_ERR_HIP) kv->invalid = true;
+  return st;
+}
+
+dory_status dory_debug_mask(dory_model* m, dory_kv* kv, int32_t sublayer, int32_t loop, int64_t p0,
+                            int32_t T, void* ws, size_t ws_bytes, uint16_t* out, void* stream) {
+  SlotPtr sp;
+  bool full = false;
+  dory_status st = probe_check(m, kv, sublayer, loop, p0, T, ws, ws_bytes, &sp, &full);
+  if (st != DORY_OK) return st;
+  if (!out) return fail(DORY_ERR_ARG, "out must be non-NULL");
+  const int B = kv->batch;
+  const Shape& s = m->s;
+  Ctx c{m, kv, s, B, T, (int64_t)B * T, p0, reinterpret_cast<uint8_t*>(ws), plan_ws(s, B, T),
+        reinterpret_cast<hipStream_t>(stream)};
+  // probe inputs in the workspace: q_hat = 0 and K = 0 give every key the
+  // score 0, so a visible key has probability 1 / (number of visible keys)
+  // and a masked one exactly 0; gate = 1, and with one-hot values the output
+  // column of a key is its weight. The step's own K/V sit in the
+  // projection-output region until they are placed.
+  const int64_t nkv_el = (int64_t)B * s.nkv * T * s.dh;
+  uint16_t* knew = reinterpret_cast<uint16_t*>(c.P());
+  uint16_t* vnew = knew + nkv_el;
+  const int64_t slot_el = (int64_t)B * s.nkv * sp.rows * s.dh;
+  const int64_t L = p0 + T;
+  const QkDest dst = probe_dest(c, sp);
+  auto run = [&]() -> dory_status {
+    HIPCHK(launch_fill_u16(c.qh(), c.M * s.dq(), 0, c.st));
+    HIPCHK(launch_fill_u16(c.gate(), c.M * s.dq(), 0x3F80, c.st));
+    HIPCHK(launch_fill_u16(knew, 2 * nkv_el, 0, c.st));
+    HIPCHK(launch_fill_u16(sp.k, slot_el, 0, c.st));
+    HIPCHK(launch_fill_u16(sp.v, slot_el, 0, c.st));
+    // Pass r puts one-hot values on the keys [r dh, (r + 1) dh): output
+    // column d of every query head is the weight of key r dh + d. Each pass
+    // rewrites the keys of the previous pass (back to 0) and of its own.
+    for (int64_t first = 0; first < L; first += s.dh) {
+      const int64_t ua = std::max<int64_t>(0, first - s.dh), ub = std::min<int64_t>(L, first + s.dh);
+      HIPCHK(launch_mask_probe_v(sp.v, sp.rows, sp.ring, vnew, B, T, s.nkv, s.dh, p0, ua, ub, first,
+                                 c.st));
+      HIPCHK(launch_kv_place(knew, vnew, B, s.nkv, T, s.dh, p0, dst, c.st));
+      dory_status r = attend(c, sp, full, c.qh(), c.gate(), c.z());
+      if (r != DORY_OK) return r;
+      HIPCHK(launch_mask_extract(c.z(), B, T, s.nq, s.dh, L, first, out, c.st));
+    }
+    return DORY_OK;
+  };
+  st = run();
+  if (st == DORY_ERR_HIP) kv->invalid = true;
+  return st;
 }
 
 const char* dory_status_string(dory_status s) {

@@ -276,7 +276,47 @@ class KVCache:
         self.handle = None
 
 
-def debug_mask(window, L, T, device="cuda"):
-    out = torch.empty(T, L + T, dtype=torch.uint8, device=device)
-    C.check(C.dory_debug_mask(window, L, T, _ptr(out), _stream()), "dory_debug_mask")
+def greedy(logits):
+    """Argmax of each row of a device fp32 [rows, n] tensor (lowest index on
+    ties): device int32 [rows]."""
+    rows, n = logits.shape
+    out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    C.check(C.dory_greedy(_ptr(logits), rows, n, _ptr(out), _stream()), "dory_greedy")
+    return out
+
+
+def debug_kv_slots(kv, sublayer, pos_a, n):
+    """Device-evaluated cache rows of positions pos_a .. pos_a + n - 1."""
+    out = torch.empty(n, dtype=torch.int64, device=kv.buffer.device)
+    C.check(C.dory_debug_kv_slots(kv.handle, sublayer, pos_a, n, _ptr(out), _stream()),
+            "dory_debug_kv_slots")
+    return out
+
+
+def debug_attention(kv, sublayer, p0, q_hat, k_new, v_new, gate, loop=0, ws=None):
+    """Attention kernels of `sublayer` on caller inputs (see
+    dory_debug_attention): q_hat [B, n_q, T, dh], k_new / v_new
+    [B, n_kv, T, dh], gate [B * T, n_q * dh] (bf16 device tensors); returns z."""
+    m = kv.model
+    T = q_hat.shape[2]
+    if ws is None:
+        ws = m.workspace(kv.batch, T, q_hat.device)
+    z = torch.empty_like(gate)
+    C.check(C.dory_debug_attention(m.handle, kv.handle, sublayer, loop, p0, T, _ptr(q_hat),
+                                   _ptr(k_new), _ptr(v_new), _ptr(gate), _ptr(z), _ptr(ws),
+                                   ws.numel(), _stream()), "dory_debug_attention")
+    return z
+
+
+def debug_mask(kv, sublayer, p0, T, loop=0, ws=None):
+    """Key weights under equal scores, read off the attention kernels of
+    `sublayer` (see dory_debug_mask): bf16 bit patterns as int16
+    [B, n_q, T, p0 + T]; nonzero exactly at the visible keys."""
+    m = kv.model
+    dev = kv.buffer.device
+    if ws is None:
+        ws = m.workspace(kv.batch, T, dev)
+    out = torch.empty(kv.batch, m.shape.n_q_heads, T, p0 + T, dtype=torch.int16, device=dev)
+    C.check(C.dory_debug_mask(m.handle, kv.handle, sublayer, loop, p0, T, _ptr(ws), ws.numel(),
+                              _ptr(out), _stream()), "dory_debug_mask")
     return out

@@ -359,3 +359,39 @@ def test_decode_context_limit_rejected_before_enqueue():
                               None) == C.DORY_ERR_UNSUPPORTED
     assert C.dory_kv_length(h) == 1048576
     C.dory_kv_destroy(h)
+
+
+def test_debug_probes_validated_before_enqueue():
+    """The attention probes, the slot dump and greedy selection refuse bad
+    arguments on the host (fake device pointers are never touched)."""
+    m, kv = _model_and_kv(synth.TINY_REC_FULL, batch=1, max_seq=64)
+    P = ctypes.c_void_p
+    wsb = M.workspace_bytes(synth.TINY_REC_FULL, 1, 8)
+
+    def mask(sub=0, loop=0, p0=0, T=8, ws=0x700000, wsn=wsb, out=0x800000):
+        return C.dory_debug_mask(m.handle, kv, sub, loop, p0, T, P(ws) if ws else None, wsn,
+                                 P(out) if out else None, None)
+
+    def attn(sub=0, p0=0, T=8, q=0x510000):
+        return C.dory_debug_attention(m.handle, kv, sub, 0, p0, T, P(q) if q else None, P(0x520000),
+                                      P(0x530000), P(0x540000), P(0x550000), P(0x700000), wsb, None)
+    assert mask(sub=1) == C.DORY_ERR_ARG          # an MLP sublayer
+    assert mask(sub=99) == C.DORY_ERR_ARG
+    assert mask(T=0) == C.DORY_ERR_ARG
+    assert mask(p0=-1) == C.DORY_ERR_ARG
+    assert mask(p0=60, T=8) == C.DORY_ERR_CAPACITY
+    assert mask(wsn=16) == C.DORY_ERR_WORKSPACE
+    assert mask(ws=0) == C.DORY_ERR_ARG
+    assert mask(out=0) == C.DORY_ERR_ARG
+    assert attn(q=0) == C.DORY_ERR_ARG
+    assert attn(sub=3) == C.DORY_ERR_ARG
+    rows = P(0x600000)
+    assert C.dory_debug_kv_slots(kv, 1, 0, 4, rows, None) == C.DORY_ERR_ARG
+    assert C.dory_debug_kv_slots(kv, 0, 60, 8, rows, None) == C.DORY_ERR_ARG
+    assert C.dory_debug_kv_slots(kv, 0, 0, 0, rows, None) == C.DORY_ERR_ARG
+    assert C.dory_debug_kv_slots(kv, 0, 0, 4, None, None) == C.DORY_ERR_ARG
+    assert C.dory_greedy(P(0x600000), 0, 10, P(0x610000), None) == C.DORY_ERR_ARG
+    assert C.dory_greedy(P(0x600000), 2, 0, P(0x610000), None) == C.DORY_ERR_ARG
+    assert C.dory_greedy(None, 2, 10, P(0x610000), None) == C.DORY_ERR_ARG
+    assert C.dory_kv_length(kv) == 0
+    C.dory_kv_destroy(kv)

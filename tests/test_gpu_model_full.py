@@ -2,10 +2,12 @@
 SwiGLU 6144, window 1024, vocab 131072, 16 input + 40 recurrent x k + 16
 output sublayers) at the sizes and launch configurations of the benchmark.
 
-* Prefill B=4 x T=8192, k = 1, 2, 4: attention is causal, so the first 48
-  positions of a sequence depend on its first 48 tokens only; those of
-  sequences 0 and 3 are compared with the float64 oracle run on 48 tokens
-  (hidden state and every loop state). At every position: hidden rows have
+* Prefill B=4 x T=8192, k = 1, 2, 4: attention is causal, so the first S
+  positions of a sequence depend on its first S tokens only; at k = 1 and 4
+  the first 1,100 positions of sequence 0 (beyond the 1,024-key window, over
+  several key and query tiles), at k = 2 the first 48 of sequences 0 and 3,
+  are compared with the float64 oracle run on those tokens (hidden state and
+  every loop state). At every position: hidden rows have
   unit length, the logits are s_z times the inner products of the last hidden
   row with the LM-head rows, and the greedy token is their argmax (lowest
   index on ties, bit-exact). Prefill from an empty cache does not depend on
@@ -85,9 +87,14 @@ def _check_lm_head(weight, hidden_last, logits, nxt, what):
 
 @pytest.mark.parametrize("k", [1, 2, 4])
 def test_prefill_benchmark_config(full, k):
+    """At k = 1 and 4 the first 1,100 positions of sequence 0 (past the
+    1,024-key window of the sliding-window layers, over 17 causal key tiles
+    and 5 query tiles of the attention kernel), at k = 2 the first 48 of
+    sequences 0 and 3, against the oracle run on those tokens (causality
+    makes the prefix exact)."""
     weight, gm, om = full
-    B, T, S = 4, 8192, 48
-    rows = [0, 3]
+    B, T = 4, 8192
+    S, rows = (48, [0, 3]) if k == 2 else (1100, [0])
     log(f"full prefill B={B} T={T} k={k}")
     toks = synth.tokens(0, B, T, SHAPE.vocab)
     kv = gm.kv_cache("last_loop", k, B, T)
