@@ -204,6 +204,24 @@ dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, 
                              float* logits, int32_t* next, float* hidden, float* states,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): a decode
+ * step like dory_decode_step, without a workspace argument. Its workspace is
+ * a static device array of DORY_NOALLOC_SCRATCH_BYTES per GPU, created when
+ * the library's code is loaded on that GPU and held until the process ends;
+ * the call allocates nothing (no hipMalloc, no allocating library routine).
+ * The scratch is laid out for exactly this step (split-K and split-attention
+ * partials for its position), so that a batch of 64 sequences at 32,768
+ * cached tokens fits; a step needing more returns DORY_ERR_WORKSPACE before
+ * anything is enqueued. Nothing in the scratch needs to start at zero. Every
+ * call on one GPU uses that GPU's single array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialized by the
+ * caller. Other arguments, outputs and errors as for dory_decode_step. */
+#define DORY_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+dory_status dory_decode_step_noalloc(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                                     int32_t k, dory_cache_mode mode, float* logits, int32_t* next,
+                                     float* hidden, float* states, void* stream);
+
 /* Steps whose sequences run different loop counts (one checkpoint served at
  * any loop count per request, section Introduction; rollouts of one batch
  * routed to different loop counts, section Post-Training, RLVR with a

@@ -80,6 +80,7 @@ SIGNATURES = {
     "dory_kv_slot": (_I32, [_P, _I32, _I32, ctypes.POINTER(dory_kv_slot_info)]),
     "dory_prefill": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_decode_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
+    "dory_decode_step_noalloc": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "dory_prefill_rows": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_decode_step_rows": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P]),
     "dory_greedy": (_I32, [_P, _I32, _I32, _P, _P]),
@@ -184,6 +185,14 @@ def dory_prefill(m, kv, tokens, B, T, k, mode, ws, ws_bytes, logits, nxt, hidden
 def dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidden, states, stream):
     return lib().dory_decode_step(m, kv, tokens, B, k, mode, ws, ws_bytes, logits, nxt, hidden,
                                   states, stream)
+
+
+def dory_decode_step_noalloc(m, kv, tokens, B, k, mode, logits, nxt, hidden, states, stream):
+    return lib().dory_decode_step_noalloc(m, kv, tokens, B, k, mode, logits, nxt, hidden, states,
+                                          stream)
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def dory_prefill_rows(m, kv, tokens, B, T, k_rows, mode, ws, ws_bytes, logits, nxt, hidden, states,

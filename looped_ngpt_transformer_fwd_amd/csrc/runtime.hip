@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <array>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -129,7 +130,10 @@ struct WsLayout {
   int64_t f_rows;
 };
 
-WsLayout plan_ws(const Shape& s, int B, int T) {
+// exact_p0 >= 0 (a decode step at that position): the split-K partials and
+// the decode-attention partials are sized for that step (the splits its
+// GEMMs and attention launches pick) instead of for the most any step needs.
+WsLayout plan_ws(const Shape& s, int B, int T, int64_t exact_p0 = -1) {
   WsLayout L{};
   const int64_t M = (int64_t)B * T;
   size_t off = 0;
@@ -144,11 +148,26 @@ WsLayout plan_ws(const Shape& s, int B, int T) {
   L.gate = take(M * s.dq() * 2);
   L.z = take(M * s.dq() * 2);
   L.a = take(M * s.F * 2);
-  int64_t ncols = std::max<int64_t>(s.nqkvg(), s.d);
-  const int64_t nsplit = max_split_for(M);
-  if (M < kLargeM) ncols = std::max<int64_t>(ncols, 2 * (int64_t)s.F);
-  L.P = take((size_t)nsplit * M * ncols * 4);
-  L.part = take((size_t)decode_attn_part_floats(B, s.nq, s.dh, kMaxDecodeSplits) * 4);
+  if (exact_p0 >= 0 && T == 1) {
+    // the projections of a decode step: (N, K) of q/k/v/gate, attention
+    // output, up/gate and down
+    const int shapes[4][2] = {{s.nqkvg(), s.d}, {s.d, s.dq()}, {2 * s.F, s.d}, {s.d, s.F}};
+    size_t pbytes = 0;
+    for (const auto& nk : shapes)
+      pbytes = std::max(pbytes, (size_t)gemm_pick_split((int)M, nk[0], nk[1], max_split_for(M)) *
+                                    M * nk[0] * 4);
+    L.P = take(pbytes);
+    const int64_t lo_w = std::max<int64_t>(0, exact_p0 - s.W + 1);
+    const int ns = std::max(decode_attn_pick_split(0, exact_p0, false),
+                            decode_attn_pick_split(lo_w, exact_p0, true));
+    L.part = take((size_t)decode_attn_part_floats(B, s.nq, s.dh, ns) * 4);
+  } else {
+    int64_t ncols = std::max<int64_t>(s.nqkvg(), s.d);
+    const int64_t nsplit = max_split_for(M);
+    if (M < kLargeM) ncols = std::max<int64_t>(ncols, 2 * (int64_t)s.F);
+    L.P = take((size_t)nsplit * M * ncols * 4);
+    L.part = take((size_t)decode_attn_part_floats(B, s.nq, s.dh, kMaxDecodeSplits) * 4);
+  }
   L.logits = s.lm ? take((size_t)B * s.V * 4) : 0;
   // cos / sin tables of the step's positions for the two RoPE bases
   L.rope = take((size_t)4 * T * (s.dh / 2) * 4);
@@ -578,10 +597,13 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   return DORY_OK;
 }
 
+// exact_ws: the workspace is laid out for exactly this step (plan_ws with the
+// step's position); otherwise for any step of B x T tokens.
 dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
                         int32_t k, const int32_t* k_rows, dory_cache_mode mode, void* ws,
                         size_t ws_bytes, float* logits, int32_t* next, float* hidden,
-                        float* states, void* stream, int32_t* next_all = nullptr) {
+                        float* states, void* stream, int32_t* next_all = nullptr,
+                        bool exact_ws = false) {
   if (!m || !kv || !tokens) return fail(DORY_ERR_ARG, "model, cache and tokens must be non-NULL");
   if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
   if (B <= 0 || T <= 0) return fail(DORY_ERR_ARG, "B and T must be >= 1");
@@ -616,8 +638,11 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
   }
   if (!ws) return fail(DORY_ERR_ARG, "workspace is NULL");
   const Shape& s = m->s;
-  WsLayout L = plan_ws(s, B, T);
-  if (ws_bytes < L.total) return fail(DORY_ERR_WORKSPACE, "workspace smaller than dory_workspace_bytes()");
+  WsLayout L = exact_ws ? plan_ws(s, B, T, kv->len) : plan_ws(s, B, T);
+  if (ws_bytes < L.total)
+    return fail(DORY_ERR_WORKSPACE, exact_ws ? "the step needs more scratch than the static "
+                                               "array holds (DORY_NOALLOC_SCRATCH_BYTES)"
+                                             : "workspace smaller than dory_workspace_bytes()");
   if ((logits || next) && !s.lm) return fail(DORY_ERR_ARG, "model has no LM head");
   Ctx c{m, kv, s, B, T, (int64_t)B * T, kv->len, reinterpret_cast<uint8_t*>(ws), L,
         reinterpret_cast<hipStream_t>(stream)};
@@ -895,6 +920,62 @@ dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, 
                              void* stream) {
   return step_common(m, kv, tokens, B, 1, k, nullptr, mode, ws, ws_bytes, logits, next, hidden, states,
                      stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of dory_decode_step_noalloc: one static array per GPU, held
+// until the process ends. In host code `scratch` only names the symbol; its
+// device address (one per GPU) comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratch = DORY_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array (looked up once per GPU).
+dory_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DORY_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DORY_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DORY_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DORY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dory_status dory_decode_step_noalloc(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
+                                     int32_t k, dory_cache_mode mode, float* logits, int32_t* next,
+                                     float* hidden, float* states, void* stream) {
+  if (!m || !kv) return fail(DORY_ERR_ARG, "model and cache must be non-NULL");
+  if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
+  if (B <= 0) return fail(DORY_ERR_ARG, "B must be >= 1");
+  // the size check comes first: a step that does not fit is refused before
+  // any HIP call
+  const size_t need = plan_ws(m->s, B, 1, kv->len).total;
+  if (need > kNoAllocScratch)
+    return fail(DORY_ERR_WORKSPACE, "the step needs " + std::to_string(need) +
+                                        " bytes of scratch, more than the static array holds (" +
+                                        std::to_string(kNoAllocScratch) + ")");
+  void* ws = nullptr;
+  dory_status st = scratch_for_current_device(&ws);
+  if (st != DORY_OK) return st;
+  return step_common(m, kv, tokens, B, 1, k, nullptr, mode, ws, kNoAllocScratch, logits, next,
+                     hidden, states, stream, nullptr, true);
 }
 
 dory_status dory_prefill_rows(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,

@@ -395,3 +395,24 @@ def test_debug_probes_validated_before_enqueue():
     assert C.dory_greedy(None, 2, 10, P(0x610000), None) == C.DORY_ERR_ARG
     assert C.dory_kv_length(kv) == 0
     C.dory_kv_destroy(kv)
+
+
+def test_noalloc_decode_size_checked_before_any_hip_call():
+    """The allocation-free decode step refuses a step whose exact scratch
+    exceeds the static array (here 1,024 sequences at full width) before any
+    HIP call, and validates its arguments like dory_decode_step."""
+    m = M.Model(synth.FULL, _fake_tensor_map(synth.FULL))
+    h = ctypes.c_void_p()
+    kvb = M.kv_bytes(synth.FULL, "last_loop", 1, 1024, 64)
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, C.DORY_CACHE_LAST_LOOP, 1, 1024,
+                           64, h), "bind")
+    st = C.dory_decode_step_noalloc(m.handle, h, ctypes.c_void_p(0x500000), 1024, 1,
+                                    C.DORY_CACHE_LAST_LOOP, None, None, None, None, None)
+    assert st == C.DORY_ERR_WORKSPACE
+    assert "static array" in C.dory_last_error()
+    assert C.dory_decode_step_noalloc(None, h, ctypes.c_void_p(0x500000), 1024, 1, 0, None, None,
+                                      None, None, None) == C.DORY_ERR_ARG
+    assert C.dory_decode_step_noalloc(m.handle, h, ctypes.c_void_p(0x500000), 0, 1, 0, None, None,
+                                      None, None, None) == C.DORY_ERR_ARG
+    assert C.dory_kv_length(h) == 0
+    C.dory_kv_destroy(h)
