@@ -74,12 +74,17 @@ attn_prefill_kernel(AttnArgs a) {
   constexpr int KCH = DH / 8;
   constexpr int K_BLOCKS = KT_BYTES / 1024, V_BLOCKS = VT_BYTES / 1024;
   constexpr int KRPB = 1024 / (DH * 2);  // key rows per DMA block
-  constexpr int NT = PF_WAVES * 64;
 
-  // Three LDS stages (two tiles in flight), as separate arrays: every LDS
-  // read below names its stage statically, so the compiler can tell it
-  // apart from the DMA still landing in the other stages and does not drain
-  // that DMA before the read.
+  // Software pipeline over key tiles: iteration j computes the scores of
+  // tile j + 1 on the matrix pipe while the softmax of tile j runs on the
+  // VALU (the two are independent, so the compiler interleaves them), then
+  // the P V product of tile j; the other wave of the SIMD fills the matrix
+  // pipe meanwhile. K tiles are needed one iteration before their V tiles,
+  // so each has its own ring of three LDS stages, filled by DMA: iteration j
+  // loads K of tile j + 3 and V of tile j + 2, and waits for the loads of
+  // iteration j - 2. Every stage is a separate array so that each LDS read
+  // names its stage statically and the compiler does not drain DMA still
+  // landing elsewhere.
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t ks1[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t ks2[KT_BYTES];
@@ -200,7 +205,8 @@ attn_prefill_kernel(AttnArgs a) {
     const int d = (wave + j * PF_WAVES) * 8 + (lane >> 3);
     v_cm[j] = (uint32_t)(((lane & 7) ^ ((d >> 1) & 7)) * 8) % ring_div;
   }
-  auto issue = [&](int64_t kt, uint8_t* kst, uint8_t* vst) __attribute__((always_inline)) {
+  auto issue_k = [&](int it, uint8_t* kst) __attribute__((always_inline)) {
+    const int64_t kt = kt_first + (int64_t)min(it, ntiles - 1) * BN;
     const uint32_t km = (uint32_t)kt % ring_div;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
@@ -217,6 +223,10 @@ attn_prefill_kernel(AttnArgs a) {
       const uint32_t off = (in_cache ? ci : fr) * DH + c * 8;
       dma16_flat((in_cache ? kcb : kfb) + off, kst + blk * 1024);
     }
+  };
+  auto issue_v = [&](int it, uint8_t* vst) __attribute__((always_inline)) {
+    const int64_t kt = kt_first + (int64_t)min(it, ntiles - 1) * BN;
+    const uint32_t km = (uint32_t)kt % ring_div;
 #pragma unroll
     for (int j = 0; j < VJ; ++j) {
       const int blk = wave + j * PF_WAVES;
@@ -238,43 +248,30 @@ attn_prefill_kernel(AttnArgs a) {
       dma16_flat((use_c ? vcb : vfb) + off, vst + blk * 1024);
     }
   };
-  // DMA instructions issued per tile by this wave
-  const int per_tile = (K_BLOCKS > wave ? (K_BLOCKS - wave + PF_WAVES - 1) / PF_WAVES : 0) +
-                       (V_BLOCKS > wave ? (V_BLOCKS - wave + PF_WAVES - 1) / PF_WAVES : 0);
-
-  // the query fragments must have landed before the DMA stream starts: the
-  // vmcnt waits in the loop count DMA only
-  wait_vm0_attn();
-  issue(kt_first, ks0, vs0);
-  issue(kt_first + (int64_t)min(1, ntiles - 1) * BN, ks1, vs1);
-
-  // Every tile issues the loads of the tile two ahead, clamped to the last
-  // tile (a reload into a stage no one reads again), so the wait count is
-  // the same in every tile and no branch surrounds the DMA.
-  auto tile = [&](int it, const uint8_t* kst, const uint8_t* vst, uint8_t* kn, uint8_t* vn) {
-    const int64_t kt = kt_first + (int64_t)it * BN;
-    // this wave's loads of tile `it` are done once at most the next tile's
-    // loads are outstanding
-    if constexpr (K_BLOCKS % PF_WAVES == 0 && V_BLOCKS % PF_WAVES == 0) {
-      constexpr int pt = K_BLOCKS / PF_WAVES + V_BLOCKS / PF_WAVES;
-      static_assert(pt == 1 || pt == 2 || pt == 4, "wait counts");
-      __builtin_amdgcn_s_waitcnt(pt == 4 ? 0x0F74 : pt == 2 ? 0x0F72 : 0x0F71);
-    } else {
-      if (per_tile == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-      else if (per_tile == 2) __builtin_amdgcn_s_waitcnt(0x0F72);
-      else if (per_tile == 1) __builtin_amdgcn_s_waitcnt(0x0F71);
-      else wait_vm0_attn();
+  // DMA instructions this wave issues per K tile and per V tile
+  const int kpw = K_BLOCKS > wave ? (K_BLOCKS - wave + PF_WAVES - 1) / PF_WAVES : 0;
+  const int vpw = V_BLOCKS > wave ? (V_BLOCKS - wave + PF_WAVES - 1) / PF_WAVES : 0;
+  // s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited). The count must be a
+  // compile-time constant wherever it can be (every wave issues the same
+  // number of DMA when the blocks divide evenly): with a count chosen at run
+  // time the compiler cannot tell which DMA an LDS read depends on and
+  // drains them all before it.
+  constexpr bool kEven = K_BLOCKS % PF_WAVES == 0 && V_BLOCKS % PF_WAVES == 0;
+  constexpr int kPW = K_BLOCKS / PF_WAVES, vPW = V_BLOCKS / PF_WAVES;
+  auto wait_vm = [](int n) __attribute__((always_inline)) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F76); break;
     }
-    barrier_lds();
-    issue(kt_first + (int64_t)min(it + 2, ntiles - 1) * BN, kn, vn);
+  };
 
-    // tile class for this wave
-    const bool dead = !wave_live || kt > wq_hi ||
-                      (a.window > 0 && wq_lo - (kt + BN - 1) >= a.window);
-    if (dead) return;
-    const bool interior = kt + BN - 1 <= wq_lo && (a.window == 0 || wq_hi - kt < a.window);
-
-    floatx16 sacc[BN / 32];
+  // S^T of one tile: 32 keys x 32 queries per accumulator, two per tile
+  auto scores = [&](const uint8_t* kst, floatx16 (&sacc)[BN / 32]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -285,51 +282,9 @@ attn_prefill_kernel(AttnArgs a) {
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[s], sacc[kb], 0, 0, 0);
       }
     }
-    if (!interior) {
-      // relative positions fit 32 bits: |pq - u| < C + 64
-      const int rel0 = (int)(pq - kt) - hl * 8;  // pq - (key index within tile)
-      const bool qok = tq < C;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int dist = rel0 - (kb * 32 + (e >> 3) * 16 + (e & 7));  // pq - u
-          const bool vis = qok && dist >= 0 && (a.window == 0 || dist < a.window);
-          if (!vis) sacc[kb][e] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: the reference maximum m_run (that of the exponentials
-    // accumulated so far) moves only when a score exceeds it by more than 8
-    // in base-2 units, so probabilities stay below 2^8 and o and l are
-    // rescaled rarely; the final o / l is the same softmax either way. (From
-    // m_run = -inf the first visible score always moves it; all-masked
-    // queries keep -inf and contribute probabilities of 0.)
-    if (__ballot((mx - m_run) * sl2 > 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * sl2);
-      m_run = m_new;
-      l_run *= corr;
-#pragma unroll
-      for (int i = 0; i < DH / 32; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= corr;
-    }
-    const float nm = -(m_run == -INFINITY ? 0.f : m_run) * sl2;
-    bf16x8 pf[BN / 32][2];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, nm));
-        l_run += p;
-        pf[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
-      }
+  };
+  // O^T += V^T P^T of one tile
+  auto pv = [&](const uint8_t* vst, const bf16x8 (&pf)[BN / 32][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) {
       const uint8_t* vrow = vst + db * 32 * (BN * 2);
@@ -342,21 +297,146 @@ attn_prefill_kernel(AttnArgs a) {
         }
     }
   };
+  // masks of an edge (or dead) tile, applied to its scores
+  auto mask = [&](int it, floatx16 (&sacc)[BN / 32]) __attribute__((always_inline)) {
+    const int64_t kt = kt_first + (int64_t)it * BN;
+    const bool interior = wave_live && kt + BN - 1 <= wq_lo &&
+                          (a.window == 0 || wq_hi - kt < a.window);
+    if (interior) return;
+    // relative positions fit 32 bits: |pq - u| < C + 64 + window
+    const int rel0 = (int)(pq - kt) - hl * 8;  // pq - (key index within tile)
+    const bool qok = tq < C;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dist = rel0 - (kb * 32 + (e >> 3) * 16 + (e & 7));  // pq - u
+        const bool vis = qok && dist >= 0 && (a.window == 0 || dist < a.window);
+        if (!vis) sacc[kb][e] = -INFINITY;
+      }
+  };
+  // Online softmax of one tile's scores into bf16 probabilities. Lazy
+  // rescaling: the reference maximum m_run moves only when a score exceeds
+  // it by more than 8 in base-2 units, so probabilities stay below 2^8 and o
+  // and l are rescaled rarely; the final o / l is the same softmax either
+  // way. Returns the factor by which o must be rescaled (1 if the reference
+  // did not move; from m_run = -inf the first visible score always moves it,
+  // and all-masked queries keep -inf and get probabilities of 0). l sums the
+  // same bf16-rounded probabilities that enter the P V product.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto softmax = [&](const floatx16 (&sacc)[BN / 32], bf16x8 (&pf)[BN / 32][2]) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool grow = (mx - m_run) * sl2 > 8.f;
+    const float m_new = grow ? mx : m_run;
+    // branch-free: exp2(0) = 1 when the reference stays, exp2(-inf) = 0 when
+    // it leaves -inf
+    const float corr = __builtin_amdgcn_exp2f(grow ? (m_run - m_new) * sl2 : 0.f);
+    m_run = m_new;
+    const float nm = -(m_run == -INFINITY ? 0.f : m_run) * sl2;
+    float la = 0.f, lb = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 pp;
+          pp[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * h + e], sl2, nm)));
+          pp[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * h + e + 1], sl2, nm)));
+          pf[kb][h][e] = pp[0];
+          pf[kb][h][e + 1] = pp[1];
+          if (e & 2) lb = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lb, false);
+          else la = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, la, false);
+        }
+      }
+    l_run = l_run * corr + (la + lb);
+    return corr;
+  };
+  auto rescale = [&](float corr) __attribute__((always_inline)) {
+    if (__ballot(corr != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= corr;
+    }
+  };
 
-  // stage of tile t is t % 3; the tile two ahead goes into stage (t + 2) % 3
-  for (int it = 0;; it += 6) {
-    tile(it, ks0, vs0, ks2, vs2);
-    if (it + 1 >= ntiles) break;
-    tile(it + 1, ks1, vs1, ks0, vs0);
-    if (it + 2 >= ntiles) break;
-    tile(it + 2, ks2, vs2, ks1, vs1);
-    if (it + 3 >= ntiles) break;
-    tile(it + 3, ks0, vs0, ks2, vs2);
-    if (it + 4 >= ntiles) break;
-    tile(it + 4, ks1, vs1, ks0, vs0);
-    if (it + 5 >= ntiles) break;
-    tile(it + 5, ks2, vs2, ks1, vs1);
-    if (it + 6 >= ntiles) break;
+  // the query fragments must have landed before the DMA stream starts: the
+  // vmcnt waits below count DMA only
+  wait_vm0_attn();
+  issue_k(0, ks0);
+  issue_k(1, ks1);
+  issue_v(0, vs0);
+  issue_k(2, ks2);
+  issue_v(1, vs1);
+  if constexpr (kEven) {
+    static_assert(2 * kPW + 2 * vPW <= 15, "wait count");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kPW + 2 * vPW));  // tile 0's K has landed
+  } else {
+    wait_vm(2 * kpw + 2 * vpw);
+  }
+  barrier_lds();
+  floatx16 sc[BN / 32], sn[BN / 32];
+  bf16x8 pf[BN / 32][2];
+  scores(ks0, sc);
+
+  // Iteration j: K read from stage (j + 1) % 3 and K of tile j + 3 loaded
+  // into stage j % 3; V read from stage j % 3 and V of tile j + 2 loaded
+  // into stage (j + 2) % 3. Loads past the last tile reload it (uniform
+  // counts, no branch around the DMA); the scores computed from such a
+  // reload after the last tile are discarded. s_cur holds the scores of tile
+  // j on entry, s_next receives those of tile j + 1.
+  auto iter = [&](int j, const uint8_t* kr, uint8_t* kw, const uint8_t* vr, uint8_t* vw,
+                  floatx16 (&s_cur)[BN / 32], floatx16 (&s_next)[BN / 32])
+      __attribute__((always_inline)) {
+    // the loads of iteration j - 2 (K of j + 1, V of j) have landed
+    if constexpr (kEven) __builtin_amdgcn_s_waitcnt(0x0F70 | (kPW + vPW));
+    else wait_vm(kpw + vpw);
+    barrier_lds();
+    issue_k(j + 3, kw);
+    issue_v(j + 2, vw);
+    mask(j, s_cur);
+    scores(kr, s_next);
+    const float corr = softmax(s_cur, pf);
+    // interleave: per score MFMA of the next tile, one LDS fragment read and
+    // a share of the current tile's softmax
+    constexpr int NMF = (BN / 32) * (DH / 16);
+    constexpr int AHEAD = 4;  // fragment reads in flight ahead of their MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i + AHEAD < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
+    // the probabilities are complete here: without this the compiler sinks
+    // their computation below the (rarely taken) rescale branch, out of
+    // reach of the score MFMAs it is meant to overlap
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pf[kb][h]));
+    rescale(corr);
+    pv(vr, pf);
+  };
+  for (int j = 0;; j += 6) {
+    iter(j, ks1, ks0, vs0, vs2, sc, sn);
+    if (j + 1 >= ntiles) break;
+    iter(j + 1, ks2, ks1, vs1, vs0, sn, sc);
+    if (j + 2 >= ntiles) break;
+    iter(j + 2, ks0, ks2, vs2, vs1, sc, sn);
+    if (j + 3 >= ntiles) break;
+    iter(j + 3, ks1, ks0, vs0, vs2, sn, sc);
+    if (j + 4 >= ntiles) break;
+    iter(j + 4, ks2, ks1, vs1, vs0, sc, sn);
+    if (j + 5 >= ntiles) break;
+    iter(j + 5, ks0, ks2, vs2, vs1, sn, sc);
+    if (j + 6 >= ntiles) break;
   }
   wait_vm0_attn();  // the clamped reloads have landed before the stages are reused
 
