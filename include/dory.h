@@ -198,7 +198,8 @@ dory_status dory_prefill(dory_model* m, dory_kv* kv, const int32_t* tokens, int3
  * hidden is [B, d] and states [k, B, d]. The split-K decode attention
  * covers at most 1,048,576 keys: a step at a longer context returns
  * DORY_ERR_UNSUPPORTED before anything is enqueued (prefill chunks have no
- * such limit). */
+ * such limit). Decode steps are replayed from captured HIP graphs (see
+ * dory_model_set_decode_graphs). */
 dory_status dory_decode_step(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B,
                              int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,
                              float* logits, int32_t* next, float* hidden, float* states,
@@ -338,6 +339,22 @@ size_t dory_mxfp8_bytes(const dory_config* cfg);
  * embedding and LM head stay bf16. The buffer must outlive the model's use
  * of it. DORY_ERR_CAPACITY if the buffer is too small. */
 dory_status dory_model_quantize_mxfp8(dory_model* m, void* buf, size_t bytes, void* stream);
+
+/* Decode-step graphs (on by default). A decode step at k loops is
+ * 32 + 40k sublayer applications (section Training with Loops), hundreds of
+ * short kernel launches; with graphs on, the first dory_decode_step with a
+ * given cache, batch, loop count, policy, weight format, set of buffers
+ * (tokens, workspace, outputs) and decode split size (one below and one
+ * above 65,536 cached keys) is captured into a HIP graph on a library stream
+ * and launched on the caller's stream, and later steps with the same
+ * parameters replay it: the kernels read the step position from the
+ * workspace, where the graph's first node writes it. Results are identical
+ * to running the kernels directly. Steps are run directly (not captured)
+ * while dory_profile_begin is active, when the caller's stream is itself
+ * being captured, and when capture fails. Graphs of a cache are released by
+ * dory_kv_destroy; on = 0 releases all of them. Calls on one model must not
+ * overlap from several threads. */
+dory_status dory_model_set_decode_graphs(dory_model* m, int32_t on);
 
 /* Switches between the bf16 weights (on = 0) and the MXFP8 copy (on != 0,
  * only after dory_model_quantize_mxfp8; DORY_ERR_ARG otherwise). */

@@ -97,6 +97,7 @@ SIGNATURES = {
     "dory_mxfp8_bytes": (_SZ, [ctypes.POINTER(dory_config)]),
     "dory_model_quantize_mxfp8": (_I32, [_P, _P, _SZ, _P]),
     "dory_model_use_mxfp8": (_I32, [_P, _I32]),
+    "dory_model_set_decode_graphs": (_I32, [_P, _I32]),
     "dory_status_string": (ctypes.c_char_p, [_I32]),
     "dory_last_error": (ctypes.c_char_p, []),
 }
@@ -253,6 +254,10 @@ def dory_model_quantize_mxfp8(m, buf, nbytes, stream):
 
 def dory_model_use_mxfp8(m, on):
     return lib().dory_model_use_mxfp8(m, on)
+
+
+def dory_model_set_decode_graphs(m, on):
+    return lib().dory_model_set_decode_graphs(m, on)
 
 
 DORY_K_NUM_CLASSES = 10

@@ -551,10 +551,11 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 4, r = lane & 15;
   const int64_t bg = (int64_t)b * a.n_kv + g;
-  const int64_t p = a.p0;
+  const int64_t p = a.p0_dev ? *a.p0_dev : a.p0;
   int64_t lo = 0;
   if (a.window > 0) lo = max((int64_t)0, p - a.window + 1);
   const int64_t A = (lo / 64) * 64 + (int64_t)split * SPLITK;
+  if (A > p) return;  // a split past the query's last key (launched for longer contexts)
   const int64_t ua = max(lo, A), ub = min(p + 1, A + SPLITK);
   const int64_t w0 = A + (int64_t)wave * DEC_WKEYS;
 
@@ -722,7 +723,8 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
 // sums keep eight splits' loads in flight per thread.
 __global__ void __launch_bounds__(128)
 attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const uint16_t* gate,
-                           uint16_t* z, RowLoops rl) {
+                           uint16_t* z, RowLoops rl, int sk, int window, int64_t p0,
+                           const int64_t* p0_dev) {
   __shared__ float wsc[2048];  // 2^(m_s - M) per split (nsplit <= 2048)
   __shared__ float pm[128];    // per-thread partial maxima (blockDim = dh <= 128)
   const int bh = blockIdx.x, d = threadIdx.x;
@@ -733,6 +735,14 @@ attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const
   }
   const int64_t stride = dh + 2;
   const float* pp = part + (int64_t)bh * nsplit * stride;
+  {
+    // the splits that hold keys of the query at position p (the first
+    // nsplit of the launch when the position is known on the host)
+    const int64_t p = p0_dev ? *p0_dev : p0;
+    const int64_t lo = window > 0 ? max((int64_t)0, p - window + 1) : 0;
+    const int64_t ns = (p + 1 - lo / 64 * 64 + sk - 1) / sk;
+    nsplit = (int)min((int64_t)nsplit, max((int64_t)1, ns));
+  }
   float M = -INFINITY;
   for (int s = d; s < nsplit; s += blockDim.x) M = fmaxf(M, pp[s * stride]);
   pm[d] = M;
@@ -777,6 +787,7 @@ hipError_t prefill_cfg(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+
 int decode_split_keys(int64_t lo, int64_t p, bool window) {
   if (window) return DEC_SWAK;
   return p + 1 - lo / 64 * 64 > DEC_LONG ? DEC_LONGK : DEC_MAXK;
@@ -796,7 +807,7 @@ hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q), dim3(DH), 0, st, part, nsplit,
-                     a.n_q, DH, a.gate, a.z, a.rl);
+                     a.n_q, DH, a.gate, a.z, a.rl, sk, a.window, a.p0, a.p0_dev);
   return hipGetLastError();
 }
 
@@ -814,6 +825,10 @@ hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
 
 int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit) {
   return (int64_t)B * n_q * nsplit * (dh + 2);
+}
+
+int decode_attn_split_keys(int64_t lo, int64_t p, bool window) {
+  return decode_split_keys(lo, p, window);
 }
 
 int decode_attn_pick_split(int64_t lo, int64_t p, bool window) {

@@ -134,15 +134,20 @@ struct QkDest {
   int64_t ring;
 };
 // With rl.k_rows, sequences that have left the loop store no K/V.
+// p0_dev (optional): the position is read from device memory instead.
 hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
                           int64_t p0, int n_q, int n_kv, int dh, const float* cs, const float* sn,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
-                          hipStream_t st, RowLoops rl = RowLoops());
+                          hipStream_t st, RowLoops rl = RowLoops(),
+                          const int64_t* p0_dev = nullptr);
 
 // RoPE table for positions p0 .. p0 + T - 1: cs/sn [T][dh/2] fp32 from fp64
 // angles (p0 + t) * base^(-2i/dh).
 hipError_t launch_rope_table(int64_t p0, int T, int dh, double base, float* cs, float* sn,
-                             hipStream_t st);
+                             hipStream_t st, const int64_t* p0_dev = nullptr);
+
+// *dst = v (one thread): the step position of a replayed decode graph.
+hipError_t launch_set_i64(int64_t* dst, int64_t v, hipStream_t st);
 
 // Copy cached K / V^T entries of positions [pos_a, pos_b) into the fresh
 // buffers (layout as QkDest with pos_origin = pos_a, no ring).
@@ -215,6 +220,8 @@ struct AttnArgs {
   float scale;           // logit scale (sqrt(dh))
   RowLoops rl;           // sequences past their loop count are skipped (z rows
                          // left as they are in prefill, zero in decode)
+  const int64_t* p0_dev = nullptr;  // decode: position read from device memory
+                                    // (replayed graphs), else p0
 };
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 
@@ -224,6 +231,12 @@ int64_t decode_attn_part_floats(int B, int n_q, int dh, int nsplit);
 // Splits for a decode query at position p whose keys are [lo, p]; window:
 // a sliding-window layer (shorter splits).
 int decode_attn_pick_split(int64_t lo, int64_t p, bool window);
+// Keys per split for that query (the split size changes above 65,536 keys).
+int decode_attn_split_keys(int64_t lo, int64_t p, bool window);
+// nsplit: the launched split count (the partials' stride). With a.p0_dev the
+// kernels read the position from device memory, splits past the query's
+// last key exit, and the merge takes the splits that hold keys; the split
+// size is the one a.p0 selects (a replayed graph is captured per size).
 hipError_t launch_attn_decode(const AttnArgs& a, int nsplit, float* part, hipStream_t st);
 
 }  // namespace dory

@@ -202,7 +202,8 @@ __global__ void swiglu_partials_kernel(const float* p, int nsplit, int64_t ss, i
 __global__ void __launch_bounds__(NT_ROW)
 qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq, int nkv,
                int dh, const float* cs_tab, const float* sn_tab, const float* s_qk, uint16_t* qh,
-               QkDest kv, uint16_t* gate, RowLoops rl) {
+               QkDest kv, uint16_t* gate, RowLoops rl, const int64_t* p0_dev) {
+  if (p0_dev) p0 = *p0_dev;
   const int m = blockIdx.x;
   const int b = m / C, t = m - b * C;
   const int64_t pos = p0 + t;
@@ -329,7 +330,8 @@ __global__ void kv_copy_kernel(const uint16_t* sk, const uint16_t* sv, int64_t s
 }
 
 __global__ void rope_table_kernel(int64_t p0, int T, int half, int dh, double base, float* cs,
-                                  float* sn) {
+                                  float* sn, const int64_t* p0_dev) {
+  if (p0_dev) p0 = *p0_dev;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * half) return;
   const int t = (int)(idx / half), i = (int)(idx % half);
@@ -497,13 +499,13 @@ hipError_t launch_swiglu_partials(const float* p, int nsplit, int64_t split_stri
 hipError_t launch_qk_prep(const float* P, int nsplit, int64_t split_stride, int B, int C,
                           int64_t p0, int n_q, int n_kv, int dh, const float* cs, const float* sn,
                           const float* s_qk, uint16_t* q_hat, QkDest kv, uint16_t* gate,
-                          hipStream_t st, RowLoops rl) {
+                          hipStream_t st, RowLoops rl, const int64_t* p0_dev) {
   if (dh != 32 && dh != 64 && dh != 128) return hipErrorInvalidValue;
   const int per_block = NT_ROW / (dh / 2);
   const int ngroups = (n_q + n_kv + per_block - 1) / per_block;
   const int nvg = (n_kv * dh + n_q * dh + NT_ROW - 1) / NT_ROW;
   hipLaunchKernelGGL(qk_prep_kernel, dim3(B * C, ngroups + nvg), dim3(NT_ROW), 0, st, P, nsplit,
-                     split_stride, C, p0, n_q, n_kv, dh, cs, sn, s_qk, q_hat, kv, gate, rl);
+                     split_stride, C, p0, n_q, n_kv, dh, cs, sn, s_qk, q_hat, kv, gate, rl, p0_dev);
   return hipGetLastError();
 }
 
@@ -542,11 +544,20 @@ hipError_t launch_kv_copy(const uint16_t* sk, const uint16_t* sv, int64_t s_rows
 }
 
 hipError_t launch_rope_table(int64_t p0, int T, int dh, double base, float* cs, float* sn,
-                             hipStream_t st) {
+                             hipStream_t st, const int64_t* p0_dev) {
   const int half = dh / 2;
   const int64_t n = (int64_t)T * half;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p0, T,
-                     half, dh, base, cs, sn);
+                     half, dh, base, cs, sn, p0_dev);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void set_i64_kernel(int64_t* dst, int64_t v) { *dst = v; }
+}  // namespace
+
+hipError_t launch_set_i64(int64_t* dst, int64_t v, hipStream_t st) {
+  hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(1), 0, st, dst, v);
   return hipGetLastError();
 }
 

@@ -126,7 +126,7 @@ size_t slot_bytes(const Shape& s, int kind, int batch, int64_t max_seq) {
 
 // Workspace layout for B sequences of T tokens.
 struct WsLayout {
-  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, rope, krows, total;
+  size_t h32, h16, x32, qh, kf, vf, gate, z, a, P, part, logits, rope, krows, state, total;
   int64_t f_rows;
 };
 
@@ -173,6 +173,8 @@ WsLayout plan_ws(const Shape& s, int B, int T, int64_t exact_p0 = -1) {
   L.rope = take((size_t)4 * T * (s.dh / 2) * 4);
   // per-sequence loop counts of a mixed-k step
   L.krows = take((size_t)B * 4);
+  // the step position, read by the kernels of a replayed decode graph
+  L.state = take(8);
   L.total = off;
   return L;
 }
@@ -218,6 +220,20 @@ struct MxMat {
   const uint16_t* deq = nullptr;
 };
 
+// A captured decode step, replayed for every later step with the same
+// cache, batch, loop count, policy, weight format, buffers and split size;
+// only the node that writes the step position changes between replays.
+struct DecodeGraph {
+  const dory_kv* kv;
+  int B, k, mode;
+  bool long_ctx, mx;
+  const void *tokens, *logits, *next, *hidden, *states, *ws;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipGraphNode_t pos_node = nullptr;
+  hipKernelNodeParams pos_params{};
+};
+
 struct dory_model {
   Shape s;
   Profiler prof;
@@ -230,7 +246,26 @@ struct dory_model {
   std::vector<std::array<MxMat, 2>> mx;
   bool mx_ready = false;
   bool use_mx = false;
-  ~dory_model() { prof.clear(); }
+  // decode-step graphs (section Training with Loops: 32 + 40k sublayer
+  // applications per token make a decode step hundreds of short launches)
+  bool graphs_on = true;
+  std::vector<DecodeGraph> graphs;
+  hipStream_t cap_stream = nullptr;  // capture only; replays go to the caller's stream
+  std::mutex graph_mu;
+  void drop_graphs(const dory_kv* kv) {
+    std::lock_guard<std::mutex> lock(graph_mu);
+    for (auto it = graphs.begin(); it != graphs.end();) {
+      if (kv && it->kv != kv) { ++it; continue; }
+      if (it->exec) hipGraphExecDestroy(it->exec);
+      if (it->graph) hipGraphDestroy(it->graph);
+      it = graphs.erase(it);
+    }
+  }
+  ~dory_model() {
+    prof.clear();
+    drop_graphs(nullptr);
+    if (cap_stream) hipStreamDestroy(cap_stream);
+  }
 };
 
 struct dory_kv {
@@ -298,6 +333,12 @@ struct Ctx {
   Profiler* prof() const { return &m->prof; }
   int32_t* krows() const { return reinterpret_cast<int32_t*>(ws + L.krows); }
   bool mixed = false;  // sequences run different loop counts (krows on the device)
+  // replayed decode graphs: the position is read from device memory (p0 is
+  // that of the capture), and the decode attention is launched for the
+  // highest position the graph serves (p_hi), its extra splits exiting
+  const int64_t* p0_dev = nullptr;
+  int64_t p_hi = -1;
+  int64_t* state() const { return reinterpret_cast<int64_t*>(ws + L.state); }
   RowLoops rl;         // loop masks while in the recurrent block of a mixed step
 };
 
@@ -381,9 +422,17 @@ dory_status attend(Ctx& c, const SlotPtr& sp, bool full, const uint16_t* q, cons
   aa.B = c.B; aa.C = c.T; aa.n_q = s.nq; aa.n_kv = s.nkv; aa.dh = s.dh;
   aa.p0 = c.p0; aa.window = full ? 0 : s.W; aa.scale = (float)s.scale;
   aa.rl = c.rl;
+  aa.p0_dev = c.p0_dev;
   if (c.T == 1) {
     const int64_t lo = full ? 0 : std::max<int64_t>(0, c.p0 - s.W + 1);
-    const int nsd = decode_attn_pick_split(lo, c.p0, !full);  // <= kMaxDecodeSplits (checked up front)
+    int nsd = decode_attn_pick_split(lo, c.p0, !full);  // <= kMaxDecodeSplits (checked up front)
+    if (c.p0_dev) {
+      // a replayed graph serves positions up to p_hi with the split size of
+      // its capture: launch the splits the highest of them needs
+      const int sk = decode_attn_split_keys(lo, c.p0, !full);
+      nsd = full ? (int)((c.p_hi + sk) / sk) : (int)((s.W + 63 + sk - 1) / sk);
+      nsd = std::max(nsd, 1);
+    }
     PROF(c, DORY_K_ATTN);
     HIPCHK(launch_attn_decode(aa, nsd, c.part(), c.st));
     return DORY_OK;
@@ -441,7 +490,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
     PROF(c, DORY_K_QK);
     HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh,
                           c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
-                          c.gate(), c.st, c.T == 1 ? c.rl : RowLoops()));
+                          c.gate(), c.st, c.T == 1 ? c.rl : RowLoops(), c.p0_dev));
   }
   st = attend(c, sp, full, c.qh(), c.gate(), c.z());
   if (st != DORY_OK) return st;
@@ -512,8 +561,8 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   {
     // cos / sin of the step's positions for both RoPE bases
     PROF(c, DORY_K_QK);
-    HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_swa, c.rope_cs(0), c.rope_sn(0), c.st));
-    HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_full, c.rope_cs(1), c.rope_sn(1), c.st));
+    HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_swa, c.rope_cs(0), c.rope_sn(0), c.st, c.p0_dev));
+    HIPCHK(launch_rope_table(c.p0, c.T, s.dh, s.base_full, c.rope_cs(1), c.rope_sn(1), c.st, c.p0_dev));
   }
   {
     PROF(c, DORY_K_OTHER);
@@ -597,6 +646,72 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   return DORY_OK;
 }
 
+// Decode step through a captured graph. *ran tells whether the graph ran;
+// when capture is not possible the caller runs the step directly.
+dory_status decode_graph_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_t* next,
+                              float* hidden, float* states, bool* ran) {
+  *ran = false;
+  dory_model* m = c.m;
+  // the split size of the full-attention decode changes above 65,536 keys;
+  // a graph serves the positions of one split size
+  const bool long_ctx = c.p0 + 1 > 65536;
+  const int64_t p_hi = std::min<int64_t>(c.kv->max_seq - 1, long_ctx ? 1048575 : 65535);
+  std::lock_guard<std::mutex> lock(m->graph_mu);
+  DecodeGraph* gph = nullptr;
+  for (auto& g : m->graphs)
+    if (g.kv == c.kv && g.B == c.B && g.k == k && g.mode == (int)c.kv->mode && g.long_ctx == long_ctx &&
+        g.mx == m->use_mx && g.tokens == tokens && g.logits == logits && g.next == next &&
+        g.hidden == hidden && g.states == states && g.ws == c.ws) {
+      gph = &g;
+      break;
+    }
+  if (!gph) {
+    if (!m->cap_stream && hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess) {
+      m->cap_stream = nullptr;
+      return DORY_OK;
+    }
+    Ctx cc = c;
+    cc.st = m->cap_stream;
+    cc.p0_dev = c.state();
+    cc.p_hi = p_hi;
+    if (hipStreamBeginCapture(cc.st, hipStreamCaptureModeThreadLocal) != hipSuccess) return DORY_OK;
+    dory_status st = DORY_OK;
+    if (launch_set_i64(c.state(), c.p0, cc.st) != hipSuccess) st = DORY_ERR_HIP;
+    if (st == DORY_OK) st = run_step(cc, tokens, k, logits, next, hidden, states);
+    hipGraph_t graph = nullptr;
+    const hipError_t e_end = hipStreamEndCapture(cc.st, &graph);
+    DecodeGraph g{c.kv, c.B, k, (int)c.kv->mode, long_ctx, m->use_mx,
+                  tokens, logits, next, hidden, states, c.ws};
+    g.graph = graph;
+    bool ok = st == DORY_OK && e_end == hipSuccess && graph;
+    size_t nroots = 0;
+    if (ok) ok = hipGraphGetRootNodes(graph, nullptr, &nroots) == hipSuccess && nroots == 1;
+    if (ok) ok = hipGraphGetRootNodes(graph, &g.pos_node, &nroots) == hipSuccess;
+    hipGraphNodeType type;
+    if (ok) ok = hipGraphNodeGetType(g.pos_node, &type) == hipSuccess && type == hipGraphNodeTypeKernel;
+    if (ok) ok = hipGraphKernelNodeGetParams(g.pos_node, &g.pos_params) == hipSuccess;
+    if (ok) ok = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0) == hipSuccess;
+    hipGetLastError();  // a failed capture leaves no sticky error behind
+    if (!ok) {
+      if (g.exec) hipGraphExecDestroy(g.exec);
+      if (graph) hipGraphDestroy(graph);
+      return DORY_OK;  // run the step directly
+    }
+    m->graphs.push_back(g);
+    gph = &m->graphs.back();
+  }
+  int64_t* dst = c.state();
+  int64_t pos = c.p0;
+  void* args[2] = {&dst, &pos};
+  hipKernelNodeParams kp = gph->pos_params;
+  kp.kernelParams = args;
+  kp.extra = nullptr;
+  HIPCHK(hipGraphExecKernelNodeSetParams(gph->exec, gph->pos_node, &kp));
+  HIPCHK(hipGraphLaunch(gph->exec, c.st));
+  *ran = true;
+  return DORY_OK;
+}
+
 // exact_ws: the workspace is laid out for exactly this step (plan_ws with the
 // step's position); otherwise for any step of B x T tokens.
 dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
@@ -651,7 +766,17 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
     if (hipMemcpyAsync(c.krows(), k_rows, (size_t)B * 4, hipMemcpyHostToDevice, c.st) != hipSuccess)
       return fail(DORY_ERR_HIP, "copy of the per-sequence loop counts failed");
   }
-  dory_status st = run_step(c, tokens, k, logits, next, hidden, states, next_all);
+  dory_status st = DORY_OK;
+  bool ran = false;
+  if (T == 1 && !k_rows && !next_all && !exact_ws && m->graphs_on && !m->prof.on) {
+    // replay a captured decode step unless the caller's stream is itself
+    // being captured (then its capture records the kernels)
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(c.st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+      st = decode_graph_step(c, tokens, k, logits, next, hidden, states, &ran);
+    hipGetLastError();
+  }
+  if (st == DORY_OK && !ran) st = run_step(c, tokens, k, logits, next, hidden, states, next_all);
   if (st != DORY_OK) {
     if (st == DORY_ERR_HIP) kv->invalid = true;
     return st;
@@ -802,9 +927,17 @@ dory_status dory_model_quantize_mxfp8(dory_model* m, void* buf, size_t bytes, vo
       mx[i][which] = MxMat{base, base + o_sc, reinterpret_cast<const uint16_t*>(base + o_deq)};
       off += t;
     }
+  m->drop_graphs(nullptr);  // graphs captured with an earlier copy name its buffers
   m->mx = mx;
   m->mx_ready = true;
   m->use_mx = true;
+  return DORY_OK;
+}
+
+dory_status dory_model_set_decode_graphs(dory_model* m, int32_t on) {
+  if (!m) return fail(DORY_ERR_ARG, "model is NULL");
+  m->graphs_on = on != 0;
+  if (!m->graphs_on) m->drop_graphs(nullptr);
   return DORY_OK;
 }
 
@@ -879,7 +1012,11 @@ dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dor
   return DORY_OK;
 }
 
-void dory_kv_destroy(dory_kv* kv) { delete kv; }
+void dory_kv_destroy(dory_kv* kv) {
+  if (!kv) return;
+  const_cast<dory_model*>(kv->m)->drop_graphs(kv);  // graphs name its slots
+  delete kv;
+}
 
 dory_status dory_kv_reset(dory_kv* kv) {
   if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");

@@ -145,6 +145,12 @@ class Model:
         C.check(C.dory_model_quantize_mxfp8(self.handle, _ptr(self.mx_buffer), n, _stream()),
                 "dory_model_quantize_mxfp8")
 
+    def set_decode_graphs(self, on):
+        """Decode steps replayed from captured HIP graphs (default) or launched
+        kernel by kernel."""
+        C.check(C.dory_model_set_decode_graphs(self.handle, 1 if on else 0),
+                "dory_model_set_decode_graphs")
+
     def use_mxfp8(self, on):
         C.check(C.dory_model_use_mxfp8(self.handle, 1 if on else 0), "dory_model_use_mxfp8")
 
