@@ -89,10 +89,21 @@ typedef struct dory_config {
    * dory_layer_kind. NULL: sublayers alternate attention and MLP starting
    * with attention, attention kinds by full_every. Copied at model creation. */
   const int32_t* layer_kinds;
+  /* DORY_PRECISION_BF16 (0, the default): bf16 weights, K/V cache and
+   * projection inputs, MFMA with fp32 accumulation, fp32 residual stream.
+   * DORY_PRECISION_FP32 (1): fp32 debug build, every tensor (weights, K/V,
+   * activations, logits) in fp32 on fp32 arithmetic, for checking the method
+   * at a tighter tolerance; sized for small models; MXFP8, prefix copies,
+   * the attention probes and decode graphs are bf16-build features. */
+  int32_t precision;
 } dory_config;
+
+#define DORY_PRECISION_BF16 0
+#define DORY_PRECISION_FP32 1
 
 /* Device pointers of one sublayer. Attention sublayers use the first group,
  * MLP sublayers the second; alpha is used by both. */
+/* Matrices below are bf16, or fp32 in the fp32 debug build (precision). */
 typedef struct dory_sublayer_weights {
   const void* w_qkvg;   /* bf16 [2*d_q + 2*d_kv, d]: rows q (d_q = n_q*head_dim), k (d_kv), v (d_kv), gate (d_q) */
   const void* w_o;      /* bf16 [d, d_q] */
@@ -114,7 +125,8 @@ typedef struct dory_weights {
 typedef struct dory_model dory_model;
 typedef struct dory_kv dory_kv;
 
-/* Location of one cache slot, for tests and tools. Keys of (b, g, position
+/* Location of one cache slot, for tests and tools. Entries are bf16 (fp32
+ * in the fp32 debug build); keys of (b, g, position
  * u) live at k + ((b * n_kv + g) * rows + r(u)) * head_dim, values
  * transposed at v + ((b * n_kv + g) * head_dim + dim) * rows + r(u), with
  * r(u) = u mod ring when ring > 0 (sliding-window slots) and r(u) = u

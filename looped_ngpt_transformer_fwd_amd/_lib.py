@@ -21,6 +21,9 @@ DORY_ERR_STATE = 7
 DORY_CACHE_LAST_LOOP = 0
 DORY_CACHE_PER_LOOP = 1
 
+DORY_PRECISION_BF16 = 0
+DORY_PRECISION_FP32 = 1
+
 DORY_LAYER_ATTN_SWA = 0
 DORY_LAYER_ATTN_FULL = 1
 DORY_LAYER_MLP = 2
@@ -37,6 +40,7 @@ class dory_config(ctypes.Structure):
         ("rope_base_swa", ctypes.c_double), ("rope_base_full", ctypes.c_double),
         ("softmax_scale", ctypes.c_double),
         ("layer_kinds", ctypes.POINTER(ctypes.c_int32)),
+        ("precision", ctypes.c_int32),
     ]
 
 

@@ -239,4 +239,32 @@ int decode_attn_split_keys(int64_t lo, int64_t p, bool window);
 // size is the one a.p0 selects (a replayed graph is captured per size).
 hipError_t launch_attn_decode(const AttnArgs& a, int nsplit, float* part, hipStream_t st);
 
+// ------------------------------------------------------- fp32 debug build
+// The same steps on fp32 tensors (weights, K/V, activations): embedding,
+// C = A B^T (optionally times scale[n]), the query/key transform into q_hat
+// [B][n_q][C][dh], K rows / V^T columns at cache_row(p0 + t - pos_origin,
+// ring) and sigma(gate), attention with keys below f_origin from the cache
+// and the rest from the fresh buffers (row u - f_origin), SwiGLU, and the
+// persistent store of fresh K/V.
+hipError_t launch_embed_f32(const int32_t* tok, const float* E, int vocab, int M, int d,
+                            float* h32, float* x32, hipStream_t st);
+hipError_t launch_sgemm(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
+                        int K, float* C, int64_t ldc, const float* scale, hipStream_t st);
+hipError_t launch_qk_prep_f32(const float* P, int B, int C, int64_t p0, int n_q, int n_kv, int dh,
+                              const float* cs, const float* sn, const float* s_qk, float* q_hat,
+                              float* kdst, float* vdst, int64_t k_rows, int64_t v_cols,
+                              int64_t pos_origin, int64_t ring, float* gate, hipStream_t st,
+                              RowLoops rl);
+hipError_t launch_attn_f32(const float* q, const float* kc, const float* vc, int64_t c_rows,
+                           int64_t ring, const float* kf, const float* vf, int64_t f_rows,
+                           int64_t f_origin, const float* gate, float* z, int B, int C, int n_q,
+                           int n_kv, int dh, int64_t p0, int window, float scale, RowLoops rl,
+                           hipStream_t st);
+hipError_t launch_swiglu_f32(const float* p, int M, int F, const float* s_u, const float* s_v,
+                             float* a, hipStream_t st);
+hipError_t launch_kv_write_f32(const float* kf, const float* vf, int64_t f_rows, int64_t f_origin,
+                               int B, int n_kv, int dh, int64_t pos_a, int64_t pos_b, float* kc,
+                               float* vc, int64_t c_rows, int64_t ring, hipStream_t st,
+                               RowLoops rl);
+
 }  // namespace dory

@@ -135,9 +135,11 @@ update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss,
     const int c = threadIdx.x + i * NT_ROW;
     if (c < nv) {
       reinterpret_cast<float4*>(h32 + (int64_t)m * d)[c] = hv[i];
-      ushort4 o;
-      o.x = f2bf(hv[i].x); o.y = f2bf(hv[i].y); o.z = f2bf(hv[i].z); o.w = f2bf(hv[i].w);
-      reinterpret_cast<ushort4*>(h16 + (int64_t)m * d)[c] = o;
+      if (h16) {  // no bf16 shadow in the fp32 build
+        ushort4 o;
+        o.x = f2bf(hv[i].x); o.y = f2bf(hv[i].y); o.z = f2bf(hv[i].z); o.w = f2bf(hv[i].w);
+        reinterpret_cast<ushort4*>(h16 + (int64_t)m * d)[c] = o;
+      }
     }
   }
 }
@@ -166,9 +168,11 @@ boundary_kernel(float* h32, uint16_t* h16, const float* x, int d) {
     if (c < nv) {
       float4 r = make_float4(v[i].x * it, v[i].y * it, v[i].z * it, v[i].w * it);
       reinterpret_cast<float4*>(h32 + (int64_t)m * d)[c] = r;
-      ushort4 o;
-      o.x = f2bf(r.x); o.y = f2bf(r.y); o.z = f2bf(r.z); o.w = f2bf(r.w);
-      reinterpret_cast<ushort4*>(h16 + (int64_t)m * d)[c] = o;
+      if (h16) {  // no bf16 shadow in the fp32 build
+        ushort4 o;
+        o.x = f2bf(r.x); o.y = f2bf(r.y); o.z = f2bf(r.z); o.w = f2bf(r.w);
+        reinterpret_cast<ushort4*>(h16 + (int64_t)m * d)[c] = o;
+      }
     }
   }
 }

@@ -48,6 +48,8 @@ int max_split_for(int64_t M) {
 struct Shape {
   int d, nq, nkv, dh, F, V, nin, nrec, nout, W, full_every, lm;
   double base_swa, base_full, scale;
+  bool f32 = false;  // fp32 debug build: weights, K/V and activations in fp32
+  int eb() const { return f32 ? 4 : 2; }  // bytes per weight / K / V / activation element
   int dq() const { return nq * dh; }
   int dkv() const { return nkv * dh; }
   int nsub() const { return nin + nrec + nout; }
@@ -62,6 +64,9 @@ dory_status read_shape(const dory_config* c, Shape* s) {
   s->lm = c->has_lm_head ? 1 : 0;
   s->base_swa = c->rope_base_swa; s->base_full = c->rope_base_full;
   s->scale = c->softmax_scale > 0 ? c->softmax_scale : std::sqrt((double)c->head_dim);
+  if (c->precision != DORY_PRECISION_BF16 && c->precision != DORY_PRECISION_FP32)
+    return fail(DORY_ERR_ARG, "unknown precision");
+  s->f32 = c->precision == DORY_PRECISION_FP32;
   if (s->d <= 0 || s->nq <= 0 || s->nkv <= 0 || s->dh <= 0 || s->F <= 0 || s->V <= 0 ||
       s->nin < 0 || s->nrec < 0 || s->nout < 0 || s->nsub() <= 0 || s->W <= 0)
     return fail(DORY_ERR_ARG, "non-positive dimension in config");
@@ -121,7 +126,7 @@ int64_t slot_rows(const Shape& s, int kind, int64_t max_seq) {
 }
 
 size_t slot_bytes(const Shape& s, int kind, int batch, int64_t max_seq) {
-  return (size_t)2 * batch * s.nkv * slot_rows(s, kind, max_seq) * s.dh * 2;
+  return (size_t)2 * batch * s.nkv * slot_rows(s, kind, max_seq) * s.dh * s.eb();
 }
 
 // Workspace layout for B sequences of T tokens.
@@ -142,12 +147,13 @@ WsLayout plan_ws(const Shape& s, int B, int T, int64_t exact_p0 = -1) {
   L.h32 = take(M * s.d * 4);
   L.h16 = take(M * s.d * 2);
   L.x32 = take(M * s.d * 4);
-  L.qh = take(M * s.dq() * 2);
-  L.kf = take((size_t)B * s.nkv * L.f_rows * s.dh * 2);
-  L.vf = take((size_t)B * s.nkv * L.f_rows * s.dh * 2);
-  L.gate = take(M * s.dq() * 2);
-  L.z = take(M * s.dq() * 2);
-  L.a = take(M * s.F * 2);
+  const int eb = s.eb();
+  L.qh = take(M * s.dq() * eb);
+  L.kf = take((size_t)B * s.nkv * L.f_rows * s.dh * eb);
+  L.vf = take((size_t)B * s.nkv * L.f_rows * s.dh * eb);
+  L.gate = take(M * s.dq() * eb);
+  L.z = take(M * s.dq() * eb);
+  L.a = take(M * s.F * eb);
   if (exact_p0 >= 0 && T == 1) {
     // the projections of a decode step: (N, K) of q/k/v/gate, attention
     // output, up/gate and down
@@ -296,7 +302,7 @@ struct SlotPtr {
 
 SlotPtr slot_ptr(const dory_kv* kv, int sub, int slot) {
   const Shape& s = kv->m->s;
-  const size_t half = (size_t)kv->batch * s.nkv * kv->rows[sub] * s.dh * 2;
+  const size_t half = (size_t)kv->batch * s.nkv * kv->rows[sub] * s.dh * s.eb();
   uint8_t* p = kv->base + kv->off[sub] + (size_t)slot * 2 * half;
   return SlotPtr{reinterpret_cast<uint16_t*>(p), reinterpret_cast<uint16_t*>(p + half),
                  kv->rows[sub], kv->ring[sub]};
@@ -546,7 +552,91 @@ dory_status mlp_sublayer(Ctx& c, int i, const UpdateOpts& uo) {
   return DORY_OK;
 }
 
+// fp32 debug build: the same sublayer steps on fp32 tensors. The step's own
+// K/V sit in the fresh buffers from row 0 (f_origin = p0) in prefill; decode
+// stores them in the cache slot and reads every key from there.
+dory_status attention_sublayer_f32(Ctx& c, int i, int slot, bool write, const UpdateOpts& uo) {
+  const Shape& s = c.s;
+  const dory_sublayer_weights& w = c.m->sub[i];
+  const bool full = c.m->kinds[i] == DORY_LAYER_ATTN_FULL;
+  const SlotPtr sp = slot_ptr(c.kv, i, slot);
+  float* kc = reinterpret_cast<float*>(sp.k);
+  float* vc = reinterpret_cast<float*>(sp.v);
+  float* qh = reinterpret_cast<float*>(c.qh());
+  float* kf = reinterpret_cast<float*>(c.kf());
+  float* vf = reinterpret_cast<float*>(c.vf());
+  float* gate = reinterpret_cast<float*>(c.gate());
+  float* z = reinterpret_cast<float*>(c.z());
+  const bool dec = c.T == 1;
+  {
+    PROF(c, DORY_K_GEMM_QKVG);
+    HIPCHK(launch_sgemm(c.h32(), s.d, reinterpret_cast<const float*>(w.w_qkvg), s.d, (int)c.M,
+                        s.nqkvg(), s.d, c.P(), s.nqkvg(), nullptr, c.st));
+  }
+  {
+    PROF(c, DORY_K_QK);
+    if (dec)
+      HIPCHK(launch_qk_prep_f32(c.P(), c.B, 1, c.p0, s.nq, s.nkv, s.dh, c.rope_cs(full ? 1 : 0),
+                                c.rope_sn(full ? 1 : 0), w.s_qk, qh, kc, vc, sp.rows, sp.rows, 0,
+                                sp.ring, gate, c.st, c.rl));
+    else
+      HIPCHK(launch_qk_prep_f32(c.P(), c.B, c.T, c.p0, s.nq, s.nkv, s.dh, c.rope_cs(full ? 1 : 0),
+                                c.rope_sn(full ? 1 : 0), w.s_qk, qh, kf, vf, c.L.f_rows, c.L.f_rows,
+                                c.p0, 0, gate, c.st, RowLoops()));
+  }
+  {
+    PROF(c, DORY_K_ATTN);
+    HIPCHK(launch_attn_f32(qh, kc, vc, sp.rows, sp.ring, kf, vf, c.L.f_rows, dec ? c.p0 + 1 : c.p0,
+                           gate, z, c.B, c.T, s.nq, s.nkv, s.dh, c.p0, full ? 0 : s.W,
+                           (float)s.scale, c.rl, c.st));
+  }
+  if (!dec && write) {
+    PROF(c, DORY_K_KV_WRITE);
+    int64_t pa = c.p0;
+    if (sp.ring > 0) pa = std::max<int64_t>(pa, c.p0 + c.T - sp.ring);
+    HIPCHK(launch_kv_write_f32(kf, vf, c.L.f_rows, c.p0, c.B, s.nkv, s.dh, pa, c.p0 + c.T, kc, vc,
+                               sp.rows, sp.ring, c.st, c.rl));
+  }
+  {
+    PROF(c, DORY_K_GEMM_O);
+    HIPCHK(launch_sgemm(z, s.dq(), reinterpret_cast<const float*>(w.w_o), s.dq(), (int)c.M, s.d,
+                        s.dq(), c.P(), s.d, nullptr, c.st));
+  }
+  PROF(c, DORY_K_UPDATE);
+  HIPCHK(launch_update(c.h32(), nullptr, c.P(), 1, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
+                       uo.aux, nullptr, c.st, c.rl, false));
+  return DORY_OK;
+}
+
+dory_status mlp_sublayer_f32(Ctx& c, int i, const UpdateOpts& uo) {
+  const Shape& s = c.s;
+  const dory_sublayer_weights& w = c.m->sub[i];
+  float* a = reinterpret_cast<float*>(c.a());
+  {
+    PROF(c, DORY_K_GEMM_UPGATE);
+    HIPCHK(launch_sgemm(c.h32(), s.d, reinterpret_cast<const float*>(w.w_upgate), s.d, (int)c.M,
+                        2 * s.F, s.d, c.P(), 2 * s.F, nullptr, c.st));
+  }
+  {
+    PROF(c, DORY_K_OTHER);
+    HIPCHK(launch_swiglu_f32(c.P(), (int)c.M, s.F, w.s_u, w.s_v, a, c.st));
+  }
+  {
+    PROF(c, DORY_K_GEMM_DOWN);
+    HIPCHK(launch_sgemm(a, s.F, reinterpret_cast<const float*>(w.w_down), s.F, (int)c.M, s.d, s.F,
+                        c.P(), s.d, nullptr, c.st));
+  }
+  PROF(c, DORY_K_UPDATE);
+  HIPCHK(launch_update(c.h32(), nullptr, c.P(), 1, c.M * s.d, s.d, w.alpha, (int)c.M, s.d, uo.x,
+                       uo.aux, nullptr, c.st, c.rl, false));
+  return DORY_OK;
+}
+
 dory_status run_sublayer(Ctx& c, int i, int slot, bool write, const UpdateOpts& uo) {
+  if (c.s.f32) {
+    if (c.m->kinds[i] == DORY_LAYER_MLP) return mlp_sublayer_f32(c, i, uo);
+    return attention_sublayer_f32(c, i, slot, write, uo);
+  }
   if (c.m->kinds[i] == DORY_LAYER_MLP) return mlp_sublayer(c, i, uo);
   return attention_sublayer(c, i, slot, write, uo);
 }
@@ -566,8 +656,12 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   }
   {
     PROF(c, DORY_K_OTHER);
-    HIPCHK(launch_embed(tokens, c.m->embed, s.V, (int)c.M, s.d, c.h32(), c.h16(),
-                        s.nin == 0 ? c.x32() : nullptr, c.st));
+    if (s.f32)
+      HIPCHK(launch_embed_f32(tokens, reinterpret_cast<const float*>(c.m->embed), s.V, (int)c.M, s.d,
+                              c.h32(), s.nin == 0 ? c.x32() : nullptr, c.st));
+    else
+      HIPCHK(launch_embed(tokens, c.m->embed, s.V, (int)c.M, s.d, c.h32(), c.h16(),
+                          s.nin == 0 ? c.x32() : nullptr, c.st));
   }
   for (int i = 0; i < s.nin; ++i) {
     UpdateOpts uo;
@@ -579,7 +673,7 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
   // out of an update; a bare embedding is normalized here
   if (s.nin == 0) {
     PROF(c, DORY_K_UPDATE);
-    HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
+    HIPCHK(launch_boundary(c.h32(), s.f32 ? nullptr : c.h16(), c.x32(), (int)c.M, s.d, c.st));
   }
   for (int it = 0; it < k; ++it) {
     const int slot = per_loop ? it : 0;
@@ -592,7 +686,7 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
     }
     float* st_out = states ? states + (int64_t)it * Md : nullptr;
     if (s.nrec == 0) {
-      if (it > 0) HIPCHK(launch_boundary(c.h32(), c.h16(), c.x32(), (int)c.M, s.d, c.st));
+      if (it > 0) HIPCHK(launch_boundary(c.h32(), s.f32 ? nullptr : c.h16(), c.x32(), (int)c.M, s.d, c.st));
       if (st_out) HIPCHK(hipMemcpyAsync(st_out, c.h32(), Md * 4, hipMemcpyDeviceToDevice, c.st));
       continue;
     }
@@ -612,7 +706,19 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
     if (st != DORY_OK) return st;
   }
   if (hidden) HIPCHK(hipMemcpyAsync(hidden, c.h32(), Md * 4, hipMemcpyDeviceToDevice, c.st));
-  if (logits || next) {
+  if ((logits || next) && s.f32) {
+    float* out = logits ? logits : c.logits_scratch();
+    {
+      PROF(c, DORY_K_GEMM_LM);
+      HIPCHK(launch_sgemm(c.h32() + (int64_t)(c.T - 1) * s.d, (int64_t)c.T * s.d,
+                          reinterpret_cast<const float*>(c.m->lm_head), s.d, c.B, s.V, s.d, out, s.V,
+                          c.m->s_z, c.st));
+    }
+    if (next) {
+      PROF(c, DORY_K_OTHER);
+      HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
+    }
+  } else if (logits || next) {
     float* out = logits ? logits : c.logits_scratch();
     GemmArgs g;
     g.A = c.h16() + (int64_t)(c.T - 1) * s.d; g.lda = (int64_t)c.T * s.d;
@@ -628,7 +734,18 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
       HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
     }
   }
-  if (next_all) {
+  if (next_all && s.f32) {
+    for (int t = 0; t < c.T; ++t) {
+      {
+        PROF(c, DORY_K_GEMM_LM);
+        HIPCHK(launch_sgemm(c.h32() + (int64_t)t * s.d, (int64_t)c.T * s.d,
+                            reinterpret_cast<const float*>(c.m->lm_head), s.d, c.B, s.V, s.d,
+                            c.logits_scratch(), s.V, c.m->s_z, c.st));
+      }
+      PROF(c, DORY_K_OTHER);
+      HIPCHK(launch_argmax(c.logits_scratch(), c.B, s.V, next_all + (int64_t)t * c.B, c.st));
+    }
+  } else if (next_all) {
     for (int t = 0; t < c.T; ++t) {
       GemmArgs g;
       g.A = c.h16() + (int64_t)t * s.d; g.lda = (int64_t)c.T * s.d;
@@ -768,7 +885,7 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
   }
   dory_status st = DORY_OK;
   bool ran = false;
-  if (T == 1 && !k_rows && !next_all && !exact_ws && m->graphs_on && !m->prof.on) {
+  if (T == 1 && !k_rows && !next_all && !exact_ws && m->graphs_on && !m->prof.on && !m->s.f32) {
     // replay a captured decode step unless the caller's stream is itself
     // being captured (then its capture records the kernels)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -863,7 +980,7 @@ void mx_region(int64_t rows, int cols, size_t* off_sc, size_t* off_deq, size_t* 
 
 size_t dory_mxfp8_bytes(const dory_config* cfg) {
   Shape s;
-  if (read_shape(cfg, &s) != DORY_OK) return 0;
+  if (read_shape(cfg, &s) != DORY_OK || s.f32) return 0;
   std::vector<int> kinds;
   if (build_schedule(cfg, s, &kinds) != DORY_OK) return 0;
   size_t total = 0;
@@ -893,6 +1010,7 @@ dory_status dory_mxfp8_quantize(const void* w, int64_t rows, int32_t cols, void*
 
 dory_status dory_model_quantize_mxfp8(dory_model* m, void* buf, size_t bytes, void* stream) {
   if (!m || !buf) return fail(DORY_ERR_ARG, "model and buffer must be non-NULL");
+  if (m->s.f32) return fail(DORY_ERR_UNSUPPORTED, "MXFP8 weights need the bf16 build");
   if (reinterpret_cast<uintptr_t>(buf) % 256 != 0) return fail(DORY_ERR_ARG, "buffer must be 256-byte aligned");
   const Shape& s = m->s;
   // everything is checked before the first launch
@@ -1216,6 +1334,7 @@ dory_status dory_kv_copy_prefix(const dory_kv* src, int32_t src_seq, dory_kv* ds
   if (dst->len != 0 && dst->len != n)
     return fail(DORY_ERR_STATE, "destination length must be 0 or n");
   if (src->invalid || dst->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure");
+  if (src->m->s.f32) return fail(DORY_ERR_UNSUPPORTED, "prefix copies run on the bf16 cache layout");
   if (src == dst && src_seq == dst_seq) return DORY_OK;
   const Shape& s = src->m->s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1331,6 +1450,7 @@ dory_status probe_check(const dory_model* m, const dory_kv* kv, int32_t sublayer
   if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
   if (kv->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure; call dory_kv_reset");
   const Shape& s = m->s;
+  if (s.f32) return fail(DORY_ERR_UNSUPPORTED, "the attention probes run the bf16 kernels");
   if (sublayer < 0 || sublayer >= s.nsub() || m->kinds[sublayer] == DORY_LAYER_MLP)
     return fail(DORY_ERR_ARG, "not an attention sublayer");
   int slot = 0;

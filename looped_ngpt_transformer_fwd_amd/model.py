@@ -29,6 +29,8 @@ def make_config(shape):
     cfg.rope_base_swa = shape.rope_base_swa
     cfg.rope_base_full = shape.rope_base_full
     cfg.softmax_scale = 0.0
+    cfg.precision = (C.DORY_PRECISION_FP32 if getattr(shape, "precision", "bf16") == "fp32"
+                     else C.DORY_PRECISION_BF16)
     kinds = getattr(shape, "layer_kinds", None)
     cfg._kinds_keepalive = None
     if kinds is not None:

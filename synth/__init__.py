@@ -49,6 +49,9 @@ class Shape:
     rope_base_full: float = 1.0e7
     layer_kinds: Optional[Tuple[str, ...]] = None
     has_lm_head: bool = True
+    # arithmetic of the GPU build the shape is run with: "bf16", or "fp32"
+    # (debug build; the weights are the same bf16-rounded draws, held in fp32)
+    precision: str = "bf16"
 
     @property
     def n_sublayers(self) -> int:
@@ -72,6 +75,9 @@ TINY_REC_FULL = dataclasses.replace(
     TINY, layer_kinds=(KIND_SWA, KIND_MLP,
                        KIND_SWA, KIND_MLP, KIND_FULL, KIND_MLP,
                        KIND_FULL, KIND_MLP))
+# The tiny models in the fp32 debug build.
+TINY_F32 = dataclasses.replace(TINY, precision="fp32")
+TINY_REC_FULL_F32 = dataclasses.replace(TINY_REC_FULL, precision="fp32")
 # Mid-size model whose projections take the large-M GEMM path with ragged
 # tiles: d=192 (3 K steps of 64), q/k/v/gate width 384, SwiGLU 320.
 MID = Shape(d_model=192, n_q_heads=4, n_kv_heads=2, head_dim=32, d_ff=320,

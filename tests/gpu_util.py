@@ -18,12 +18,16 @@ def log(*a):
 
 
 def upload(W: synth.Weights, device="cuda"):
-    """Device tensors of every weight: bf16 patterns as int16, vectors fp32."""
+    """Device tensors of every weight: bf16 patterns as int16 (fp32 values of
+    the same bf16 draws for a shape of the fp32 debug build), vectors fp32."""
     out = {}
+    f32 = getattr(W.shape, "precision", "bf16") == "fp32"
     for name in W.names():
         r = W.raw(name)
-        if r.dtype == np.uint16:
+        if r.dtype == np.uint16 and not f32:
             out[name] = torch.from_numpy(r.view(np.int16)).to(device)
+        elif r.dtype == np.uint16:
+            out[name] = torch.from_numpy(W.f64(name).astype(np.float32)).to(device)
         else:
             out[name] = torch.from_numpy(np.ascontiguousarray(r, dtype=np.float32)).to(device)
     return out

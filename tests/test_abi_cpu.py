@@ -416,3 +416,21 @@ def test_noalloc_decode_size_checked_before_any_hip_call():
                                       None, None, None) == C.DORY_ERR_ARG
     assert C.dory_kv_length(h) == 0
     C.dory_kv_destroy(h)
+
+
+def test_f32_build_sizes_and_refusals():
+    """fp32 debug build: the cache holds 4-byte entries (the closed form with
+    4-byte elements), the workspace grows, and the bf16-only features refuse."""
+    for sh, shf in ((synth.TINY, synth.TINY_F32), (synth.TINY_REC_FULL, synth.TINY_REC_FULL_F32)):
+        for mode in ("last_loop", "per_loop"):
+            for k in (1, 2, 4):
+                assert M.kv_bytes(shf, mode, k, 2, 64) == ref.kv_bytes(sh, mode, k, 2, 64, elem_bytes=4)
+                assert M.kv_bytes(shf, mode, k, 2, 64) == 2 * M.kv_bytes(sh, mode, k, 2, 64)
+        assert M.workspace_bytes(shf, 2, 16) > M.workspace_bytes(sh, 2, 16)
+    assert M.mxfp8_bytes(synth.TINY_F32) == 0
+    m = M.Model(synth.TINY_F32, _fake_tensor_map(synth.TINY_F32))
+    assert C.dory_model_quantize_mxfp8(m.handle, ctypes.c_void_p(0x1000000), 1 << 30, None) == \
+        C.DORY_ERR_UNSUPPORTED
+    cfg = M.make_config(synth.TINY)
+    cfg.precision = 7
+    assert C.dory_kv_bytes(cfg, 0, 1, 1, 64) == 0
