@@ -142,6 +142,70 @@ def greedy(logits: np.ndarray) -> np.ndarray:
     return np.argmax(logits, axis=-1).astype(np.int32)
 
 
+def softmax_t(logits: np.ndarray, temperature: float) -> np.ndarray:
+    """Sampling distribution softmax(logits / temperature) over the last axis
+    (max subtracted first)."""
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
+    z = z - np.max(z, axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def sample_inverse_cdf(probs: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Sampling by inversion: for each row, the smallest index i whose
+    cumulative weight exceeds u * (total), u in [0, 1) (so an entry of zero
+    weight is never chosen). probs [..., V] (unnormalized weights are fine),
+    u [...]."""
+    probs = np.asarray(probs, dtype=np.float64)
+    c = np.cumsum(probs, axis=-1)
+    target = np.asarray(u, dtype=np.float64)[..., None] * c[..., -1:]
+    idx = np.sum(c <= target, axis=-1)
+    # u * total can exceed the last cumulative sum only by rounding
+    return np.minimum(idx, probs.shape[-1] - 1).astype(np.int32)
+
+
+def speculative_sample(draft_logits: np.ndarray, verify_logits: np.ndarray, drafts: np.ndarray,
+                       u: np.ndarray, temperature: float):
+    """Rejection rule of self-speculative decoding (Self-Speculative
+    Decoding: the drafter proposes gamma tokens, the verifier scores them in
+    one pass, and rejection sampling with both models' probabilities accepts
+    proposals and corrects the first rejection so that the verifier's
+    sampling distribution is preserved). Written from the standard rule:
+
+      q_j = softmax(draft_logits_j / T), p_j = softmax(verify_logits_j / T);
+      draft x_j (sampled from q_j) is accepted while u_j < p_j(x_j) / q_j(x_j)
+      (always when p_j(x_j) >= q_j(x_j));
+      at the first rejection j the next token is drawn from the residual
+      max(0, p_j - q_j) (normalized) with the uniform u_gamma; if all gamma
+      drafts pass, the next token is drawn from p_{gamma+1} with u_gamma.
+
+    draft_logits [gamma, B, V], verify_logits [gamma + 1, B, V], drafts
+    [gamma, B], u [gamma + 1, B] uniforms in [0, 1). Returns (n_accepted [B],
+    next [B]): the tokens emitted for sequence b are drafts[:n_b, b] then
+    next[b]."""
+    draft_logits = np.asarray(draft_logits, dtype=np.float64)
+    verify_logits = np.asarray(verify_logits, dtype=np.float64)
+    gamma, B, V = draft_logits.shape
+    q = softmax_t(draft_logits, temperature)
+    p = softmax_t(verify_logits, temperature)
+    n = np.zeros(B, dtype=np.int32)
+    nxt = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        j = 0
+        while j < gamma:
+            x = int(drafts[j, b])
+            if not (u[j, b] < p[j, b, x] / q[j, b, x]):
+                break
+            j += 1
+        n[b] = j
+        if j < gamma:
+            resid = np.maximum(p[j, b] - q[j, b], 0.0)
+            nxt[b] = sample_inverse_cdf(resid, u[gamma, b])
+        else:
+            nxt[b] = sample_inverse_cdf(p[gamma, b], u[gamma, b])
+    return n, nxt
+
+
 def visible(qpos: np.ndarray, kpos: np.ndarray, window: Optional[int]) -> np.ndarray:
     """[T, L] boolean: key position u is visible to the query at position p iff
     u <= p and, for a sliding-window layer, p - u < window (reading R3)."""

@@ -632,3 +632,97 @@ def test_batch_rows_independent():
 def test_greedy_lowest_index_on_ties():
     lg = np.array([[0.0, 2.0, 2.0, 1.0], [5.0, 5.0, 5.0, 5.0]])
     np.testing.assert_array_equal(ref.greedy(lg), [1, 0])
+
+
+# ---------------------------------------------------------------- speculative sampling
+
+def _rand_dists(seed, V, B=1, spread=2.0):
+    g = np.random.default_rng(seed)
+    return spread * g.standard_normal((B, V)), spread * g.standard_normal((B, V))
+
+
+def test_speculative_rule_output_law_equals_verifier_distribution():
+    """Closed form of the rule (Self-Speculative Decoding: the verifier's
+    sampling distribution is preserved): with one draft x ~ q accepted with
+    probability a(x) = min(1, p(x) / q(x)) and the residual
+    r = max(0, p - q) / sum otherwise, P(first token = y) = q(y) a(y) +
+    (1 - sum_x q(x) a(x)) r(y) must equal p(y). The acceptance probability and
+    residual are read off the oracle's rule itself by integrating over u:
+    draft x is accepted exactly for u below the threshold the rule uses."""
+    for seed, T in ((1, 1.0), (2, 0.7), (3, 1.6)):
+        dl, vl = _rand_dists(seed, 23)
+        q = ref.softmax_t(dl[0], T)
+        p = ref.softmax_t(vl[0], T)
+        acc = np.zeros(23)
+        for x in range(23):
+            # the largest u the rule accepts for draft x, by bisection on u
+            lo, hi = 0.0, 1.0
+            n, _ = ref.speculative_sample(dl[None], np.stack([vl, vl]), np.array([[x]]),
+                                          np.array([[1.0 - 1e-15], [0.5]]), T)
+            if n[0] == 1:
+                acc[x] = 1.0
+                continue
+            for _ in range(60):
+                mid = 0.5 * (lo + hi)
+                n, _ = ref.speculative_sample(dl[None], np.stack([vl, vl]), np.array([[x]]),
+                                              np.array([[mid], [0.5]]), T)
+                lo, hi = (mid, hi) if n[0] == 1 else (lo, mid)
+            acc[x] = lo
+        # residual: the rule's correction token as a function of the second uniform
+        grid = (np.arange(200000) + 0.5) / 200000
+        _, corr = ref.speculative_sample(np.repeat(dl[None], 1, 0), np.stack([vl, vl]),
+                                         np.array([[int(np.argmax(q - p))]]),
+                                         np.array([[1.0 - 1e-15], [0.5]]), T)
+        resid_cdf = np.cumsum(np.maximum(p - q, 0))
+        resid_cdf /= resid_cdf[-1]
+        r = np.diff(np.concatenate([[0.0], resid_cdf]))
+        law = q * acc + (1.0 - np.sum(q * acc)) * r
+        np.testing.assert_allclose(acc, np.minimum(1.0, p / q), atol=1e-12)
+        np.testing.assert_allclose(law, p, atol=1e-12)
+        assert 0 <= corr[0] < 23
+
+
+def test_speculative_rule_monte_carlo_matches_verifier():
+    """Seeded uniforms through the oracle's rule (gamma = 2, drafts sampled
+    from q by inversion): the empirical law of the first emitted token is the
+    verifier's p_1 within 5 binomial standard deviations, and that of the
+    second emitted token (conditioned on the first being an accepted draft) is
+    p_2."""
+    V, N, T = 12, 60000, 1.0
+    g = np.random.default_rng(7)
+    dl = 1.5 * g.standard_normal((2, 1, V))
+    vl = 1.5 * g.standard_normal((3, 1, V))
+    q = ref.softmax_t(dl, T)
+    p = ref.softmax_t(vl, T)
+    u = g.random((N, 5))
+    first = np.zeros(V)
+    for i in range(N):
+        d1 = ref.sample_inverse_cdf(q[0, 0], u[i, 0])
+        d2 = ref.sample_inverse_cdf(q[1, 0], u[i, 1])
+        n, nxt = ref.speculative_sample(dl, vl, np.array([[d1], [d2]]),
+                                        u[i, 2:5].reshape(3, 1), T)
+        first[d1 if n[0] >= 1 else nxt[0]] += 1
+    sd = np.sqrt(N * p[0, 0] * (1 - p[0, 0]))
+    assert np.all(np.abs(first - N * p[0, 0]) <= 5 * sd + 1)
+
+
+def test_speculative_rule_special_cases():
+    """p = q: every draft is accepted and the extra token is drawn from the
+    verifier's last distribution; a draft the verifier gives probability 0 is
+    always rejected and corrected from the residual; inversion sampling at
+    u = 0 gives the first index with mass."""
+    g = np.random.default_rng(9)
+    dl = g.standard_normal((3, 4, 10))
+    vl = np.concatenate([dl, g.standard_normal((1, 4, 10))])
+    drafts = g.integers(0, 10, (3, 4))
+    u = g.random((4, 4)) * 0.999
+    n, nxt = ref.speculative_sample(dl, vl, drafts, u, 1.0)
+    assert np.all(n == 3)
+    np.testing.assert_array_equal(nxt, ref.sample_inverse_cdf(ref.softmax_t(vl[3], 1.0), u[3]))
+    vl2 = vl.copy()
+    vl2[0, :, 4] = -np.inf                         # the verifier never emits token 4
+    drafts2 = drafts.copy()
+    drafts2[0] = 4
+    n2, nxt2 = ref.speculative_sample(dl, vl2, drafts2, np.zeros((4, 4)), 1.0)
+    assert np.all(n2 == 0) and np.all(nxt2 != 4)
+    assert ref.sample_inverse_cdf(np.array([0.0, 0.0, 0.3, 0.7]), np.array(0.0)) == 2
