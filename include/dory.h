@@ -263,7 +263,13 @@ dory_status dory_decode_step_rows(dory_model* m, dory_kv* kv, const int32_t* tok
  * starts at that position. 0 <= length <= max_seq. Shortening forgets the
  * positions past `length` (for example rejected speculative tokens);
  * lengthening declares that the new positions already hold valid K/V of
- * every loop (for example a cache restored by the caller). */
+ * every loop (for example a cache restored by the caller). A
+ * sliding-window sublayer's ring holds its window plus DORY_KV_ROLLBACK
+ * positions, so where a ring is shorter than max_seq the cache can be
+ * shortened to no less than (longest length written since the last reset
+ * or copy) - DORY_KV_ROLLBACK; deeper returns DORY_ERR_ARG (the keys the
+ * next step's window needs would have been overwritten). */
+#define DORY_KV_ROLLBACK 64
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length);
 
 /* Prefix caching (section Last-Loop KV Caching: serving reuses cached
@@ -300,11 +306,12 @@ dory_status dory_kv_copy_prefix(const dory_kv* src, int32_t src_seq, dory_kv* ds
  * int32), the cache keeps positions up to L + n, and out rows 0 .. n are the
  * next n + 1 tokens of every sequence (row n, the verifier's own token after
  * the last accepted position, feeds the next round). With greedy selection
- * the emitted tokens are those of plain decoding at k_verify. Rejection
- * sampling for sampled decoding, and reuse of the drafts' input-block and
- * loop-1 activations in the verification pass, are not implemented: the
+ * the emitted tokens are those of plain decoding at k_verify (sampled
+ * decoding: dory_selfspec_step_sampled). Reuse of the drafts' input-block
+ * and loop-1 activations in the verification pass is not implemented: the
  * verification recomputes them (with per-loop caching it rewrites the same
- * input-block and loop-1 entries). Per-loop caches only (as on the pages;
+ * input-block and loop-1 entries). 1 <= gamma <= DORY_KV_ROLLBACK (the
+ * cache is shortened by up to gamma positions). Per-loop caches only (as on the pages;
  * DORY_ERR_MODE otherwise): under last-loop caching the verification chunk
  * reads its own tokens' current-loop entries where token-by-token decoding
  * reads final-loop ones. scratch: device int32 of 2 B (gamma + 1)
@@ -315,6 +322,60 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
                                int32_t gamma, int32_t k_draft, int32_t k_verify, dory_cache_mode mode,
                                void* ws, size_t ws_bytes, int32_t* scratch, int32_t* out,
                                int32_t* n_accepted, void* stream);
+
+/* ---- Sampled decoding ---------------------------------------------------
+ * Sampling by inversion (uniforms are inputs; nothing here draws random
+ * numbers): out[r] (device int32 [rows]) = the smallest index i whose
+ * cumulative weight exceeds u[r] times the row total, the weights being
+ * softmax(logits[r] / temperature) (logits: device fp32 [rows][V], u:
+ * device fp32 [rows] in [0, 1)); a token of zero probability is never
+ * chosen. temperature > 0. Asynchronous on `stream`. */
+dory_status dory_sample(const float* logits, int32_t rows, int32_t V, float temperature,
+                        const float* u, int32_t* out, void* stream);
+
+/* Rejection rule of self-speculative decoding (section Self-Speculative
+ * Decoding: rejection sampling with both the drafter's and the verifier's
+ * probabilities accepts proposals and corrects rejections, preserving the
+ * verifier's sampling distribution). For each sequence b, with
+ * q_j = softmax(draft_logits[j][b] / T) (j < gamma) and
+ * p_j = softmax(verify_logits[j][b] / T) (j <= gamma): draft j
+ * (drafts[j][b], sampled from q_j) is accepted while u[j][b] < p_j / q_j at
+ * it; at the first rejection j the next token is sampled by inversion with
+ * u[gamma][b] from max(0, p_j - q_j), and if all gamma drafts pass, from
+ * p_gamma. Device buffers: draft_logits fp32 [gamma][B][V], verify_logits
+ * fp32 [gamma + 1][B][V], drafts int32 [gamma][B], u fp32 [gamma + 1][B];
+ * outputs n_accepted int32 [B] and out int32 [gamma + 1][B] (the accepted
+ * drafts, then the next token, then -1). 1 <= gamma <= 1000. */
+dory_status dory_speculative_accept(const float* draft_logits, const float* verify_logits,
+                                    const int32_t* drafts, const float* u, int32_t B, int32_t V,
+                                    int32_t gamma, float temperature, int32_t* n_accepted,
+                                    int32_t* out, void* stream);
+
+/* One self-speculative round with sampled decoding (section
+ * Self-Speculative Decoding): gamma draft steps at k_draft, each sampling
+ * its token from softmax(logits / temperature) with uniforms
+ * u[0 .. gamma - 1][B]; the cache is rolled back; one verification step at
+ * k_verify over the gamma + 1 tokens writes the logits after every
+ * position; dory_speculative_accept with uniforms u[gamma .. 2 gamma][B]
+ * decides each sequence's accepted count n_b and next token. The cache
+ * keeps n = min over b of n_b drafts (one length per batch) and
+ * *n_accepted (host) = n; out (device int32 [gamma + 1][B]) holds every
+ * sequence's own accepted drafts and next token (dory_speculative_accept's
+ * layout): rows 0 .. n are the next n + 1 tokens of every sequence (for a
+ * sequence with n_b > n, row n is its accepted draft n + 1: a prefix of a
+ * correctly distributed continuation is correctly distributed), and row n
+ * feeds the next round. logits_buf: device fp32 [2 gamma + 1][B][V] (the
+ * drafts' logits, then the verification's), scratch: device int32 of
+ * 2 B (gamma + 1) elements, u: device fp32 [2 gamma + 1][B] in [0, 1).
+ * 1 <= gamma <= DORY_KV_ROLLBACK, temperature > 0. Per-loop caches only;
+ * other arguments and errors as for dory_selfspec_step. Synchronous (the
+ * accepted counts are read back). */
+dory_status dory_selfspec_step_sampled(dory_model* m, dory_kv* kv, const int32_t* last, int32_t B,
+                                       int32_t gamma, int32_t k_draft, int32_t k_verify,
+                                       dory_cache_mode mode, float temperature, const float* u,
+                                       void* ws, size_t ws_bytes, int32_t* scratch,
+                                       float* logits_buf, int32_t* out, int32_t* n_accepted,
+                                       void* stream);
 
 /* ---- MXFP8 weights (W8A16) ------------------------------------------------
  * Section Quantization (Post-Training Quantization): an MXFP8 checkpoint made

@@ -97,6 +97,10 @@ SIGNATURES = {
     "dory_profile_end": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double)]),
     "dory_selfspec_step": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P,
                                   ctypes.POINTER(_I32), _P]),
+    "dory_sample": (_I32, [_P, _I32, _I32, ctypes.c_float, _P, _P, _P]),
+    "dory_speculative_accept": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P]),
+    "dory_selfspec_step_sampled": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                          _P, _P, _SZ, _P, _P, _P, ctypes.POINTER(_I32), _P]),
     "dory_mxfp8_quantize": (_I32, [_P, _I64, _I32, _P, _P, _P, _P]),
     "dory_mxfp8_bytes": (_SZ, [ctypes.POINTER(dory_config)]),
     "dory_model_quantize_mxfp8": (_I32, [_P, _P, _SZ, _P]),
@@ -198,6 +202,7 @@ def dory_decode_step_noalloc(m, kv, tokens, B, k, mode, logits, nxt, hidden, sta
 
 
 NOALLOC_SCRATCH_BYTES = 256 << 20
+DORY_KV_ROLLBACK = 64        # positions a cache can be shortened by (sliding-window rings)
 
 
 def dory_prefill_rows(m, kv, tokens, B, T, k_rows, mode, ws, ws_bytes, logits, nxt, hidden, states,
@@ -242,6 +247,23 @@ def dory_selfspec_step(m, kv, last, B, gamma, k_draft, k_verify, mode, ws, ws_by
                        n_accepted, stream):
     return lib().dory_selfspec_step(m, kv, last, B, gamma, k_draft, k_verify, mode, ws, ws_bytes,
                                     scratch, out, ctypes.byref(n_accepted), stream)
+
+
+def dory_sample(logits, rows, V, temperature, u, out, stream):
+    return lib().dory_sample(logits, rows, V, temperature, u, out, stream)
+
+
+def dory_speculative_accept(draft_logits, verify_logits, drafts, u, B, V, gamma, temperature,
+                            n_accepted, out, stream):
+    return lib().dory_speculative_accept(draft_logits, verify_logits, drafts, u, B, V, gamma,
+                                         temperature, n_accepted, out, stream)
+
+
+def dory_selfspec_step_sampled(m, kv, last, B, gamma, k_draft, k_verify, mode, temperature, u, ws,
+                               ws_bytes, scratch, logits_buf, out, n_accepted, stream):
+    return lib().dory_selfspec_step_sampled(m, kv, last, B, gamma, k_draft, k_verify, mode,
+                                            temperature, u, ws, ws_bytes, scratch, logits_buf, out,
+                                            ctypes.byref(n_accepted), stream)
 
 
 def dory_mxfp8_quantize(w, rows, cols, codes, scales, deq, stream):

@@ -239,6 +239,19 @@ int decode_attn_split_keys(int64_t lo, int64_t p, bool window);
 // size is the one a.p0 selects (a replayed graph is captured per size).
 hipError_t launch_attn_decode(const AttnArgs& a, int nsplit, float* part, hipStream_t st);
 
+// ------------------------------------------------------- sampled decoding
+// Sampling by inversion from softmax(logits / T): out[r] = the smallest i
+// whose cumulative weight exceeds u[r] * total.
+hipError_t launch_sample(const float* logits, int rows, int V, float temperature, const float* u,
+                         int32_t* out, hipStream_t st);
+// Self-speculative rejection rule over draft_logits [gamma][B][V],
+// verify_logits [gamma + 1][B][V], drafts [gamma][B] and uniforms
+// u [gamma + 1][B]: n_out [B] accepted drafts, out [gamma + 1][B] the accepted
+// drafts then the next token then -1.
+hipError_t launch_spec_accept(const float* draft_logits, const float* verify_logits,
+                              const int32_t* drafts, const float* u, int B, int V, int gamma,
+                              float temperature, int32_t* n_out, int32_t* out, hipStream_t st);
+
 // ------------------------------------------------------- fp32 debug build
 // The same steps on fp32 tensors (weights, K/V, activations): embedding,
 // C = A B^T (optionally times scale[n]), the query/key transform into q_hat

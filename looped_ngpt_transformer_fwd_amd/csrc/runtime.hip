@@ -121,7 +121,11 @@ int64_t max_seq_limit(const Shape& s) {
 }
 
 int64_t slot_rows(const Shape& s, int kind, int64_t max_seq) {
-  if (kind == DORY_LAYER_ATTN_SWA) return round8(std::min<int64_t>(max_seq, s.W));
+  // a sliding-window ring keeps DORY_KV_ROLLBACK positions beyond the
+  // window, so that the cache can be shortened by up to DORY_KV_ROLLBACK
+  // positions (rejected speculative tokens) with every key the next step's
+  // window needs still in place
+  if (kind == DORY_LAYER_ATTN_SWA) return round8(std::min<int64_t>(max_seq, s.W + DORY_KV_ROLLBACK));
   return round8(max_seq);
 }
 
@@ -229,6 +233,10 @@ struct MxMat {
 // A captured decode step, replayed for every later step with the same
 // cache, batch, loop count, policy, weight format, buffers and split size;
 // only the node that writes the step position changes between replays.
+// graphs kept per model (one per cache, batch, loop count, policy, weight
+// format, buffers and split size); the oldest is dropped beyond this
+constexpr size_t kMaxDecodeGraphs = 32;
+
 struct DecodeGraph {
   const dory_kv* kv;
   int B, k, mode;
@@ -282,6 +290,10 @@ struct dory_kv {
   int k_max, batch;
   int64_t max_seq;
   int64_t len;
+  // highest length written since the last reset: rows of a sliding-window
+  // ring hold positions up to hi - 1, so shortening is bounded by it
+  int64_t hi = 0;
+  bool wraps = false;  // some sliding-window ring is shorter than max_seq
   // per-loop caching: filled[j] (j = 1 .. k_max) = number of leading
   // positions whose loop-j entries are written (non-increasing in j)
   std::vector<int64_t> filled;
@@ -641,10 +653,12 @@ dory_status run_sublayer(Ctx& c, int i, int slot, bool write, const UpdateOpts& 
   return attention_sublayer(c, i, slot, write, uo);
 }
 
-// next_all (device int32 [T][B], or null): greedy token after every position
+// next_all (device int32 [T][B], or null): greedy token after every position;
+// logits_all (device fp32 [T][B][V], or null): the logits after every position
 // of the step, one LM-head call of B rows per position.
 dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_t* next,
-                     float* hidden, float* states, int32_t* next_all = nullptr) {
+                     float* hidden, float* states, int32_t* next_all = nullptr,
+                     float* logits_all = nullptr) {
   const Shape& s = c.s;
   const int64_t Md = c.M * s.d;
   const bool per_loop = c.kv->mode == DORY_CACHE_PER_LOOP;
@@ -734,30 +748,29 @@ dory_status run_step(Ctx& c, const int32_t* tokens, int k, float* logits, int32_
       HIPCHK(launch_argmax(out, c.B, s.V, next, c.st));
     }
   }
-  if (next_all && s.f32) {
+  if (next_all || logits_all) {
+    // the LM head after every position of the step (B rows each)
     for (int t = 0; t < c.T; ++t) {
+      float* out = logits_all ? logits_all + (int64_t)t * c.B * s.V : c.logits_scratch();
       {
         PROF(c, DORY_K_GEMM_LM);
-        HIPCHK(launch_sgemm(c.h32() + (int64_t)t * s.d, (int64_t)c.T * s.d,
-                            reinterpret_cast<const float*>(c.m->lm_head), s.d, c.B, s.V, s.d,
-                            c.logits_scratch(), s.V, c.m->s_z, c.st));
+        if (s.f32) {
+          HIPCHK(launch_sgemm(c.h32() + (int64_t)t * s.d, (int64_t)c.T * s.d,
+                              reinterpret_cast<const float*>(c.m->lm_head), s.d, c.B, s.V, s.d, out,
+                              s.V, c.m->s_z, c.st));
+        } else {
+          GemmArgs g;
+          g.A = c.h16() + (int64_t)t * s.d; g.lda = (int64_t)c.T * s.d;
+          g.B = c.m->lm_head; g.ldb = s.d;
+          g.M = c.B; g.N = s.V; g.K = s.d; g.nsplit = 1;
+          g.C = out; g.ldc = s.V; g.s1 = c.m->s_z;
+          HIPCHK(launch_gemm(g, EPI_LOGITS, c.st));
+        }
       }
-      PROF(c, DORY_K_OTHER);
-      HIPCHK(launch_argmax(c.logits_scratch(), c.B, s.V, next_all + (int64_t)t * c.B, c.st));
-    }
-  } else if (next_all) {
-    for (int t = 0; t < c.T; ++t) {
-      GemmArgs g;
-      g.A = c.h16() + (int64_t)t * s.d; g.lda = (int64_t)c.T * s.d;
-      g.B = c.m->lm_head; g.ldb = s.d;
-      g.M = c.B; g.N = s.V; g.K = s.d; g.nsplit = 1;
-      g.C = c.logits_scratch(); g.ldc = s.V; g.s1 = c.m->s_z;
-      {
-        PROF(c, DORY_K_GEMM_LM);
-        HIPCHK(launch_gemm(g, EPI_LOGITS, c.st));
+      if (next_all) {
+        PROF(c, DORY_K_OTHER);
+        HIPCHK(launch_argmax(out, c.B, s.V, next_all + (int64_t)t * c.B, c.st));
       }
-      PROF(c, DORY_K_OTHER);
-      HIPCHK(launch_argmax(c.logits_scratch(), c.B, s.V, next_all + (int64_t)t * c.B, c.st));
     }
   }
   return DORY_OK;
@@ -783,6 +796,14 @@ dory_status decode_graph_step(Ctx& c, const int32_t* tokens, int k, float* logit
       break;
     }
   if (!gph) {
+    if (m->graphs.size() >= kMaxDecodeGraphs) {
+      // the oldest graph goes; its replays are finished first
+      HIPCHK(hipStreamSynchronize(c.st));
+      DecodeGraph& old = m->graphs.front();
+      if (old.exec) hipGraphExecDestroy(old.exec);
+      if (old.graph) hipGraphDestroy(old.graph);
+      m->graphs.erase(m->graphs.begin());
+    }
     if (!m->cap_stream && hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess) {
       m->cap_stream = nullptr;
       return DORY_OK;
@@ -835,7 +856,8 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
                         int32_t k, const int32_t* k_rows, dory_cache_mode mode, void* ws,
                         size_t ws_bytes, float* logits, int32_t* next, float* hidden,
                         float* states, void* stream, int32_t* next_all = nullptr,
-                        bool exact_ws = false) {
+                        bool exact_ws = false, float* logits_all = nullptr,
+                        bool allow_graph = true) {
   if (!m || !kv || !tokens) return fail(DORY_ERR_ARG, "model, cache and tokens must be non-NULL");
   if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
   if (B <= 0 || T <= 0) return fail(DORY_ERR_ARG, "B and T must be >= 1");
@@ -885,7 +907,8 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
   }
   dory_status st = DORY_OK;
   bool ran = false;
-  if (T == 1 && !k_rows && !next_all && !exact_ws && m->graphs_on && !m->prof.on && !m->s.f32) {
+  if (T == 1 && !k_rows && !next_all && !logits_all && !exact_ws && allow_graph && m->graphs_on &&
+      !m->prof.on && !m->s.f32) {
     // replay a captured decode step unless the caller's stream is itself
     // being captured (then its capture records the kernels)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -893,12 +916,14 @@ dory_status step_common(dory_model* m, dory_kv* kv, const int32_t* tokens, int32
       st = decode_graph_step(c, tokens, k, logits, next, hidden, states, &ran);
     hipGetLastError();
   }
-  if (st == DORY_OK && !ran) st = run_step(c, tokens, k, logits, next, hidden, states, next_all);
+  if (st == DORY_OK && !ran)
+    st = run_step(c, tokens, k, logits, next, hidden, states, next_all, logits_all);
   if (st != DORY_OK) {
     if (st == DORY_ERR_HIP) kv->invalid = true;
     return st;
   }
   kv->len += T;
+  kv->hi = std::max(kv->hi, kv->len);
   if (mode == DORY_CACHE_PER_LOOP)
     for (int j = 1; j <= k; ++j) kv->filled[j] = kv->len;
   return DORY_OK;
@@ -1105,7 +1130,7 @@ dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dor
   dory_kv* kv = new dory_kv();
   kv->m = m; kv->base = reinterpret_cast<uint8_t*>(kv_dev); kv->bytes = kv_bytes;
   kv->mode = mode; kv->k_max = k_max; kv->batch = batch; kv->max_seq = max_seq;
-  kv->len = 0; kv->invalid = false;
+  kv->len = 0; kv->hi = 0; kv->invalid = false;
   kv->filled.assign(k_max + 1, 0);
   kv->off.assign(s.nsub(), (size_t)-1);
   kv->nslots.assign(s.nsub(), 0);
@@ -1120,6 +1145,7 @@ dory_status dory_kv_bind(const dory_model* m, void* kv_dev, size_t kv_bytes, dor
     kv->nslots[i] = slots;
     kv->rows[i] = slot_rows(s, kind, max_seq);
     kv->ring[i] = kind == DORY_LAYER_ATTN_SWA ? kv->rows[i] : 0;
+    if (kv->ring[i] > 0 && kv->ring[i] < max_seq) kv->wraps = true;
     off += slots * slot_bytes(s, kind, batch, max_seq);
   }
   if (kv_bytes < off) {
@@ -1139,6 +1165,7 @@ void dory_kv_destroy(dory_kv* kv) {
 dory_status dory_kv_reset(dory_kv* kv) {
   if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");
   kv->len = 0;
+  kv->hi = 0;
   std::fill(kv->filled.begin(), kv->filled.end(), 0);
   kv->invalid = false;
   return DORY_OK;
@@ -1258,7 +1285,7 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
   if (!m || !kv || !last || !scratch || !out || !n_accepted)
     return fail(DORY_ERR_ARG, "model, cache, tokens, scratch, out and n_accepted must be non-NULL");
   if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
-  if (gamma < 1) return fail(DORY_ERR_ARG, "gamma must be >= 1");
+  if (gamma < 1 || gamma > DORY_KV_ROLLBACK) return fail(DORY_ERR_ARG, "need 1 <= gamma <= DORY_KV_ROLLBACK");
   if (k_draft < 1 || k_verify < k_draft) return fail(DORY_ERR_ARG, "need 1 <= k_draft <= k_verify");
   if (!m->s.lm) return fail(DORY_ERR_ARG, "model has no LM head");
   if (B != kv->batch) return fail(DORY_ERR_ARG, "B must equal the bound batch");
@@ -1286,7 +1313,7 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
   for (int j = 1; j <= gamma; ++j) {
     dory_status s1 = step_common(m, kv, scratch + (int64_t)(j - 1) * B, B, 1, k_draft, nullptr, mode,
                                  ws, ws_bytes, nullptr, scratch + (int64_t)j * B, nullptr, nullptr,
-                                 stream);
+                                 stream, nullptr, false, nullptr, false);
     if (s1 != DORY_OK) {
       dory_kv_set_length(kv, L0);
       return s1;
@@ -1317,6 +1344,107 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
     while (nb < gamma && drafts[(size_t)(nb + 1) * B + b] == greedy[(size_t)nb * B + b]) ++nb;
     n = std::min(n, nb);
   }
+  dory_kv_set_length(kv, L0 + n + 1);
+  *n_accepted = n;
+  return DORY_OK;
+}
+
+dory_status dory_sample(const float* logits, int32_t rows, int32_t V, float temperature,
+                        const float* u, int32_t* out, void* stream) {
+  if (!logits || !u || !out) return fail(DORY_ERR_ARG, "logits, u and out must be non-NULL");
+  if (rows < 1 || V < 1) return fail(DORY_ERR_ARG, "rows and V must be >= 1");
+  if (!(temperature > 0.f)) return fail(DORY_ERR_ARG, "temperature must be > 0");
+  hipError_t e = launch_sample(logits, rows, V, temperature, u, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DORY_ERR_HIP, hipGetErrorString(e));
+  return DORY_OK;
+}
+
+dory_status dory_speculative_accept(const float* draft_logits, const float* verify_logits,
+                                    const int32_t* drafts, const float* u, int32_t B, int32_t V,
+                                    int32_t gamma, float temperature, int32_t* n_accepted,
+                                    int32_t* out, void* stream) {
+  if (!draft_logits || !verify_logits || !drafts || !u || !n_accepted || !out)
+    return fail(DORY_ERR_ARG, "pointer arguments must be non-NULL");
+  if (B < 1 || V < 1 || gamma < 1 || gamma > 1000) return fail(DORY_ERR_ARG, "need B, V >= 1 and 1 <= gamma <= 1000");
+  if (!(temperature > 0.f)) return fail(DORY_ERR_ARG, "temperature must be > 0");
+  hipError_t e = launch_spec_accept(draft_logits, verify_logits, drafts, u, B, V, gamma, temperature,
+                                    n_accepted, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DORY_ERR_HIP, hipGetErrorString(e));
+  return DORY_OK;
+}
+
+dory_status dory_selfspec_step_sampled(dory_model* m, dory_kv* kv, const int32_t* last, int32_t B,
+                                       int32_t gamma, int32_t k_draft, int32_t k_verify,
+                                       dory_cache_mode mode, float temperature, const float* u,
+                                       void* ws, size_t ws_bytes, int32_t* scratch,
+                                       float* logits_buf, int32_t* out, int32_t* n_accepted,
+                                       void* stream) {
+  if (!m || !kv || !last || !u || !scratch || !logits_buf || !out || !n_accepted)
+    return fail(DORY_ERR_ARG, "pointer arguments must be non-NULL");
+  if (kv->m != m) return fail(DORY_ERR_ARG, "cache bound to another model");
+  if (gamma < 1 || gamma > DORY_KV_ROLLBACK) return fail(DORY_ERR_ARG, "need 1 <= gamma <= DORY_KV_ROLLBACK");
+  if (k_draft < 1 || k_verify < k_draft) return fail(DORY_ERR_ARG, "need 1 <= k_draft <= k_verify");
+  if (!(temperature > 0.f)) return fail(DORY_ERR_ARG, "temperature must be > 0");
+  if (!m->s.lm) return fail(DORY_ERR_ARG, "model has no LM head");
+  if (B != kv->batch) return fail(DORY_ERR_ARG, "B must equal the bound batch");
+  if (mode != kv->mode) return fail(DORY_ERR_MODE, "cache mode differs from the bound mode");
+  if (mode != DORY_CACHE_PER_LOOP) return fail(DORY_ERR_MODE, "self-speculative decoding needs the per-loop cache");
+  if (kv->invalid) return fail(DORY_ERR_STATE, "cache invalid after a HIP failure; call dory_kv_reset");
+  const int64_t L0 = kv->len;
+  if (L0 + gamma + 1 > kv->max_seq) return fail(DORY_ERR_CAPACITY, "cache capacity exceeded");
+  if (k_verify > kv->k_max) return fail(DORY_ERR_MODE, "per-loop cache: k_verify exceeds k_max");
+  if (kv->filled[k_verify] < L0)
+    return fail(DORY_ERR_MODE, "per-loop cache: earlier positions lack loop-k_verify entries");
+  const size_t need = std::max(plan_ws(m->s, B, 1).total, plan_ws(m->s, B, gamma + 1).total);
+  if (!ws || ws_bytes < need) return fail(DORY_ERR_WORKSPACE, "workspace smaller than dory_workspace_bytes(B, gamma + 1)");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int G = gamma + 1, V = m->s.V;
+  const int64_t BV = (int64_t)B * V;
+  // scratch rows 0 .. gamma: the token fed to draft step j (row 0: `last`),
+  // row j the draft of step j; then the same as [B][gamma + 1], whose space
+  // receives the accepted counts after the verification pass
+  if (hipMemcpyAsync(scratch, last, (size_t)B * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return fail(DORY_ERR_HIP, "copy of the last tokens failed");
+  for (int j = 1; j <= gamma; ++j) {
+    float* dl = logits_buf + (int64_t)(j - 1) * BV;
+    dory_status s1 = step_common(m, kv, scratch + (int64_t)(j - 1) * B, B, 1, k_draft, nullptr, mode,
+                                 ws, ws_bytes, dl, nullptr, nullptr, nullptr, stream, nullptr, false,
+                                 nullptr, false);
+    if (s1 == DORY_OK && launch_sample(dl, B, V, temperature, u + (int64_t)(j - 1) * B,
+                                       scratch + (int64_t)j * B, st) != hipSuccess) {
+      kv->invalid = true;
+      s1 = fail(DORY_ERR_HIP, "draft sampling launch failed");
+    }
+    if (s1 != DORY_OK) {
+      dory_kv_set_length(kv, L0);
+      return s1;
+    }
+  }
+  dory_kv_set_length(kv, L0);  // roll back the drafts' positions
+  int32_t* bt = scratch + (int64_t)G * B;
+  if (launch_transpose_i32(scratch, G, B, bt, st) != hipSuccess)
+    return fail(DORY_ERR_HIP, "token transpose failed");
+  dory_status s2 = step_common(m, kv, bt, B, G, k_verify, nullptr, mode, ws, ws_bytes, nullptr,
+                               nullptr, nullptr, nullptr, stream, nullptr, false,
+                               logits_buf + (int64_t)gamma * BV);
+  if (s2 != DORY_OK) {
+    dory_kv_set_length(kv, L0);
+    return s2;
+  }
+  int32_t* n_dev = bt;  // the verification input is consumed
+  if (launch_spec_accept(logits_buf, logits_buf + (int64_t)gamma * BV, scratch + B, u + (int64_t)gamma * B,
+                         B, V, gamma, temperature, n_dev, out, st) != hipSuccess) {
+    kv->invalid = true;
+    return fail(DORY_ERR_HIP, "acceptance launch failed");
+  }
+  std::vector<int32_t> nb(B);
+  if (hipMemcpyAsync(nb.data(), n_dev, (size_t)B * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    kv->invalid = true;
+    return fail(DORY_ERR_HIP, "copy of the accepted counts failed");
+  }
+  int n = gamma;
+  for (int b = 0; b < B; ++b) n = std::min(n, nb[b]);
   dory_kv_set_length(kv, L0 + n + 1);
   *n_accepted = n;
   return DORY_OK;
@@ -1362,6 +1490,7 @@ dory_status dory_kv_copy_prefix(const dory_kv* src, int32_t src_seq, dory_kv* ds
   }
   if (dst->len == 0) {
     dst->len = n;
+    dst->hi = n;
     for (int j = 0; j <= dst->k_max; ++j) dst->filled[j] = (j == 0 || j <= loops) ? n : 0;
   } else {
     // the other sequences' loops stay as they are; loops this one lacks are not held
@@ -1373,12 +1502,16 @@ dory_status dory_kv_copy_prefix(const dory_kv* src, int32_t src_seq, dory_kv* ds
 dory_status dory_kv_set_length(dory_kv* kv, int64_t length) {
   if (!kv) return fail(DORY_ERR_ARG, "cache is NULL");
   if (length < 0 || length > kv->max_seq) return fail(DORY_ERR_CAPACITY, "length outside [0, max_seq]");
+  if (length < kv->len && kv->wraps && kv->hi - length > DORY_KV_ROLLBACK)
+    return fail(DORY_ERR_ARG, "a sliding-window cache can be shortened by at most DORY_KV_ROLLBACK "
+                              "positions below the longest length written");
   if (length <= kv->len) {
     // roll back: positions at or past `length` are forgotten
     for (auto& f : kv->filled) f = std::min(f, length);
   } else {
     // extend: the caller declares every loop's entries of the new positions
     for (auto& f : kv->filled) f = length;
+    kv->hi = std::max(kv->hi, length);
   }
   kv->len = length;
   return DORY_OK;

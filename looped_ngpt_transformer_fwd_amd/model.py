@@ -139,6 +139,25 @@ class Model:
                                      _stream()), "dory_selfspec_step")
         return n.value, out[:n.value + 1].t().contiguous()
 
+    def selfspec_step_sampled(self, kv, last, gamma, k_draft, k_verify, temperature, u, ws=None):
+        """One sampled self-speculative round; u: device fp32 [2 gamma + 1, B]
+        uniforms. Returns (n accepted by the batch, out [gamma + 1, B] device
+        int32 per-sequence tokens, logits buffer [2 gamma + 1, B, V], the
+        drafted tokens [gamma, B])."""
+        B = kv.batch
+        dev = last.device
+        if ws is None:
+            ws = self.workspace(B, gamma + 1)
+        scratch = torch.empty(2 * B * (gamma + 1), dtype=torch.int32, device=dev)
+        lbuf = torch.empty(2 * gamma + 1, B, self.shape.vocab, dtype=torch.float32, device=dev)
+        out = torch.empty(gamma + 1, B, dtype=torch.int32, device=dev)
+        n = ctypes.c_int32()
+        C.check(C.dory_selfspec_step_sampled(self.handle, kv.handle, _ptr(last), B, gamma, k_draft,
+                                             k_verify, kv.mode_code, float(temperature), _ptr(u),
+                                             _ptr(ws), ws.numel(), _ptr(scratch), _ptr(lbuf),
+                                             _ptr(out), n, _stream()), "dory_selfspec_step_sampled")
+        return n.value, out, lbuf, scratch[B:(gamma + 1) * B].view(gamma, B)
+
     def quantize_mxfp8(self, device="cuda"):
         """Quantizes the projection matrices to MXFP8 (weight-only) into a
         buffer owned by this object and switches the model to them."""
@@ -282,6 +301,28 @@ class KVCache:
         except Exception:  # interpreter shutdown
             pass
         self.handle = None
+
+
+def sample(logits, temperature, u):
+    """Sampling by inversion from softmax(logits / temperature), one uniform
+    per row (device fp32 [rows]): device int32 [rows]."""
+    rows, n = logits.shape
+    out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    C.check(C.dory_sample(_ptr(logits), rows, n, float(temperature), _ptr(u), _ptr(out), _stream()),
+            "dory_sample")
+    return out
+
+
+def speculative_accept(draft_logits, verify_logits, drafts, u, temperature):
+    """draft_logits [gamma, B, V], verify_logits [gamma + 1, B, V], drafts
+    [gamma, B], u [gamma + 1, B] (device): (n_accepted [B], out [gamma + 1, B])."""
+    gamma, B, V = draft_logits.shape
+    n = torch.empty(B, dtype=torch.int32, device=draft_logits.device)
+    out = torch.empty(gamma + 1, B, dtype=torch.int32, device=draft_logits.device)
+    C.check(C.dory_speculative_accept(_ptr(draft_logits), _ptr(verify_logits), _ptr(drafts), _ptr(u),
+                                      B, V, gamma, float(temperature), _ptr(n), _ptr(out), _stream()),
+            "dory_speculative_accept")
+    return n, out
 
 
 def greedy(logits):

@@ -289,20 +289,22 @@ def block_of(shape, s: int) -> str:
 
 
 def kv_bytes(shape, mode: str, k: int, batch: int, length: int,
-             elem_bytes: int = 2, ring: bool = True) -> int:
+             elem_bytes: int = 2, ring: bool = True, extra: int = 0) -> int:
     """Cache bytes for `length` tokens per sequence (Last-Loop KV Caching):
     each attention sublayer of the recurrent block holds k slots under
     per-loop caching and one under last-loop caching; input and output
     attention sublayers hold one. A slot stores K and V for n_kv heads of
     head_dim; a sliding-window slot stored as a ring holds min(length, W)
-    tokens."""
+    tokens, or min(length, W + extra) when the ring also keeps `extra`
+    older tokens (so that a cache can be shortened by that many positions,
+    as speculative decoding does when it drops rejected drafts)."""
     per_tok = 2 * shape.n_kv_heads * shape.head_dim * elem_bytes
     total = 0
     for s, kind in enumerate(layer_kinds(shape)):
         if kind == KIND_MLP:
             continue
         slots = k if (mode == MODE_PER and block_of(shape, s) == "recurrent") else 1
-        toks = min(length, shape.window) if (kind == KIND_SWA and ring) else length
+        toks = min(length, shape.window + extra) if (kind == KIND_SWA and ring) else length
         total += slots * batch * per_tok * toks
     return total
 

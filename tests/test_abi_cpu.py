@@ -47,15 +47,22 @@ def test_schedule_matches_oracle(shape):
 
 
 def test_kv_bytes_matches_oracle_closed_form():
+    """The cache size is the closed form with sliding-window rings of
+    W + DORY_KV_ROLLBACK tokens (lengths and windows multiples of 8, so the
+    runtime's rows equal the formula's tokens)."""
+    ex = C.DORY_KV_ROLLBACK
     for sh in (synth.TINY, synth.TINY_REC_FULL):
         for mode in ("last_loop", "per_loop"):
             for k in (1, 2, 4):
-                # lengths that are multiples of 8 and windows below them: rows = formula rows
-                assert M.kv_bytes(sh, mode, k, 2, 64) == ref.kv_bytes(sh, mode, k, 2, 64)
+                for L in (64, 200):
+                    assert M.kv_bytes(sh, mode, k, 2, L) == ref.kv_bytes(sh, mode, k, 2, L, extra=ex)
     for mode in ("last_loop", "per_loop"):
         for k in (1, 2, 4):
             assert M.kv_bytes(synth.FULL, mode, k, 64, 33024) == \
-                ref.kv_bytes(synth.FULL, mode, k, 64, 33024)
+                ref.kv_bytes(synth.FULL, mode, k, 64, 33024, extra=ex)
+    # the slack is small next to the window at the full shape
+    assert ref.kv_bytes(synth.FULL, "last_loop", 1, 64, 33024, extra=ex) < \
+        1.01 * ref.kv_bytes(synth.FULL, "last_loop", 1, 64, 33024)
 
 
 def test_kv_bytes_constant_in_k_for_last_loop():
@@ -188,7 +195,7 @@ def test_bind_refuses_a_slab_of_2_pow_32_bytes():
     assert M.kv_bytes(synth.PAIR, "last_loop", 1, 1, big) == 0
     assert M.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 7) == 0   # rounds up to 2^24 rows
     n = M.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 8)
-    assert n == ref.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 8)
+    assert n == ref.kv_bytes(synth.PAIR, "last_loop", 1, 1, big - 8, extra=C.DORY_KV_ROLLBACK)
     assert C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), 1 << 40, 0, 1, 1, big, h) == \
         C.DORY_ERR_ARG
     assert "2^32" in C.dory_last_error()
@@ -343,6 +350,51 @@ def test_selfspec_validated_before_enqueue():
         C.dory_kv_destroy(x)
 
 
+def test_sampled_entries_validated_before_enqueue():
+    """dory_sample, dory_speculative_accept and dory_selfspec_step_sampled
+    reject bad arguments on the host, before anything is enqueued (the
+    pointers below are never dereferenced)."""
+    P = ctypes.c_void_p
+    a, b, c, d, e, f = (P(0x100000 * i) for i in range(1, 7))
+    assert C.dory_sample(None, 4, 10, 1.0, b, c, None) == C.DORY_ERR_ARG
+    assert C.dory_sample(a, 0, 10, 1.0, b, c, None) == C.DORY_ERR_ARG
+    assert C.dory_sample(a, 4, 0, 1.0, b, c, None) == C.DORY_ERR_ARG
+    assert C.dory_sample(a, 4, 10, 0.0, b, c, None) == C.DORY_ERR_ARG
+    assert C.dory_sample(a, 4, 10, float("nan"), b, c, None) == C.DORY_ERR_ARG
+    acc = C.dory_speculative_accept
+    assert acc(a, b, c, None, 2, 10, 3, 1.0, e, f, None) == C.DORY_ERR_ARG
+    assert acc(a, b, c, d, 2, 10, 0, 1.0, e, f, None) == C.DORY_ERR_ARG
+    assert acc(a, b, c, d, 2, 10, 1001, 1.0, e, f, None) == C.DORY_ERR_ARG
+    assert acc(a, b, c, d, 0, 10, 3, 1.0, e, f, None) == C.DORY_ERR_ARG
+    assert acc(a, b, c, d, 2, 10, 3, -1.0, e, f, None) == C.DORY_ERR_ARG
+
+    m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
+    h = ctypes.c_void_p()
+    kvb = M.kv_bytes(synth.TINY, "per_loop", 2, 2, 16)
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), kvb, C.DORY_CACHE_PER_LOOP, 2, 2, 16, h),
+            "bind")
+    ws_bytes = M.workspace_bytes(synth.TINY, 2, 5)
+    n = ctypes.c_int32(-1)
+
+    def call(B=2, gamma=4, kd=1, kv_=2, T=0.7, u=0x880000, wsb=ws_bytes, lbuf=0x800000):
+        return C.dory_selfspec_step_sampled(m.handle, h, P(0x500000), B, gamma, kd, kv_,
+                                            C.DORY_CACHE_PER_LOOP, T, P(u) if u else None, P(0x700000),
+                                            wsb, P(0x600000), P(lbuf) if lbuf else None, P(0x680000),
+                                            n, None)
+    assert call(T=0.0) == C.DORY_ERR_ARG
+    assert call(u=0) == C.DORY_ERR_ARG
+    assert call(lbuf=0) == C.DORY_ERR_ARG
+    assert call(gamma=0) == C.DORY_ERR_ARG
+    assert call(kd=3) == C.DORY_ERR_ARG
+    assert call(B=1) == C.DORY_ERR_ARG
+    assert call(kv_=3) == C.DORY_ERR_MODE
+    assert call(wsb=16) == C.DORY_ERR_WORKSPACE
+    C.check(C.dory_kv_set_length(h, 12), "set_length")
+    assert call() == C.DORY_ERR_CAPACITY
+    assert C.dory_kv_length(h) == 12 and n.value == -1
+    C.dory_kv_destroy(h)
+
+
 def test_decode_context_limit_rejected_before_enqueue():
     """Decode attention covers at most 1,048,576 keys (2,048 splits of 512 at
     long contexts): a decode step at position 1,048,576 is refused on the
@@ -424,7 +476,8 @@ def test_f32_build_sizes_and_refusals():
     for sh, shf in ((synth.TINY, synth.TINY_F32), (synth.TINY_REC_FULL, synth.TINY_REC_FULL_F32)):
         for mode in ("last_loop", "per_loop"):
             for k in (1, 2, 4):
-                assert M.kv_bytes(shf, mode, k, 2, 64) == ref.kv_bytes(sh, mode, k, 2, 64, elem_bytes=4)
+                assert M.kv_bytes(shf, mode, k, 2, 64) == ref.kv_bytes(sh, mode, k, 2, 64, elem_bytes=4,
+                                                                             extra=C.DORY_KV_ROLLBACK)
                 assert M.kv_bytes(shf, mode, k, 2, 64) == 2 * M.kv_bytes(sh, mode, k, 2, 64)
         assert M.workspace_bytes(shf, 2, 16) > M.workspace_bytes(sh, 2, 16)
     assert M.mxfp8_bytes(synth.TINY_F32) == 0
@@ -434,3 +487,33 @@ def test_f32_build_sizes_and_refusals():
     cfg = M.make_config(synth.TINY)
     cfg.precision = 7
     assert C.dory_kv_bytes(cfg, 0, 1, 1, 64) == 0
+
+
+def test_rollback_depth_bounded_on_wrapping_rings():
+    """A sliding-window ring holds W + DORY_KV_ROLLBACK positions: where it
+    is shorter than max_seq, shortening below (longest length written) -
+    DORY_KV_ROLLBACK is refused and the length stays; a cache whose rings
+    never wrap can be shortened to any length; reset clears the record."""
+    m = M.Model(synth.TINY, _fake_tensor_map(synth.TINY))
+    R = C.DORY_KV_ROLLBACK
+    h = ctypes.c_void_p()
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), M.kv_bytes(synth.TINY, "last_loop", 1, 2, 400),
+                           C.DORY_CACHE_LAST_LOOP, 1, 2, 400, h), "bind")
+    C.check(C.dory_kv_set_length(h, 300), "extend")
+    assert C.dory_kv_set_length(h, 300 - R - 1) == C.DORY_ERR_ARG
+    assert C.dory_kv_length(h) == 300
+    C.check(C.dory_kv_set_length(h, 300 - R), "shorten by DORY_KV_ROLLBACK")
+    C.check(C.dory_kv_set_length(h, 290), "lengthen again")
+    # measured from the longest length written (300), not the current one
+    assert C.dory_kv_set_length(h, 300 - R - 1) == C.DORY_ERR_ARG
+    C.check(C.dory_kv_reset(h), "reset")
+    C.check(C.dory_kv_set_length(h, 100), "extend")
+    C.check(C.dory_kv_set_length(h, 100 - R), "shorten")
+    C.dory_kv_destroy(h)
+    # rings of W + DORY_KV_ROLLBACK rows never wrap below that length
+    n = synth.TINY.window + R
+    C.check(C.dory_kv_bind(m.handle, ctypes.c_void_p(0x900000), M.kv_bytes(synth.TINY, "last_loop", 1, 2, n),
+                           C.DORY_CACHE_LAST_LOOP, 1, 2, n, h), "bind")
+    C.check(C.dory_kv_set_length(h, n), "extend")
+    C.check(C.dory_kv_set_length(h, 0), "shorten to 0")
+    C.dory_kv_destroy(h)

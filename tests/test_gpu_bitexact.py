@@ -54,10 +54,10 @@ def _oracle_mask(p0, T, window):
 MASK_CASES = [
     # shape, sublayer, p0, T, max_seq, batch
     ("tiny", 0, 0, 64, 64, 1),        # sliding window 16, one shot
-    ("tiny", 0, 37, 29, 128, 2),      # ring of 16 rows wrapped, chunk start not a multiple of 8
+    ("tiny", 0, 117, 29, 256, 2),     # ring of 80 rows wrapped, chunk start not a multiple of 8
     ("tiny", 4, 0, 64, 64, 1),        # full attention (recurrent full layer)
     ("tiny", 4, 100, 1, 128, 2),      # full-attention decode
-    ("tiny", 0, 70, 1, 128, 1),       # sliding-window decode, ring wrapped 4 times
+    ("tiny", 0, 330, 1, 400, 1),      # sliding-window decode, ring wrapped 4 times
     ("pair", 0, 1500, 600, 2100, 1),  # window 1024, ring wrapped, 600-query chunk
     ("pair", 0, 0, 1100, 1100, 1),    # window 1024 inside one chunk (fresh keys only)
     ("pair", 2, 0, 1100, 1100, 1),    # causal over 18 key tiles
@@ -186,14 +186,16 @@ def test_cache_rows_of_positions(M):
         for pos_a, n in ((0, 200), (37, 100), (199, 1)):
             got = M.debug_kv_slots(kv, sub, pos_a, n).cpu().numpy()
             pos = np.arange(pos_a, pos_a + n)
-            want = pos % shape.window if kind == ref.KIND_SWA else pos
-            assert info.ring == (shape.window if kind == ref.KIND_SWA else 0)
+            # a ring holds the window and DORY_KV_ROLLBACK (64) more positions
+            ring = shape.window + 64
+            want = pos % ring if kind == ref.KIND_SWA else pos
+            assert info.ring == (ring if kind == ref.KIND_SWA else 0)
             np.testing.assert_array_equal(got, want)
-    # a full-shape window of 1,024 rows
+    # a full-shape window of 1,024 positions: 1,088 rows
     mp, _ = _probe_model(M, synth.PAIR)
     kvp = mp.kv_cache("last_loop", 1, 1, 5000)
     got = M.debug_kv_slots(kvp, 0, 1000, 4000).cpu().numpy()
-    np.testing.assert_array_equal(got, np.arange(1000, 5000) % 1024)
+    np.testing.assert_array_equal(got, np.arange(1000, 5000) % 1088)
     got = M.debug_kv_slots(kvp, 2, 1000, 4000).cpu().numpy()
     np.testing.assert_array_equal(got, np.arange(1000, 5000))
 

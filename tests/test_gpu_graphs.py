@@ -107,3 +107,25 @@ def test_graph_across_split_size_change():
         torch.cuda.synchronize()
         _same(a, b, f"position {L0 + step}")
     assert kvg.length == L0 + 12
+
+
+def test_graph_list_bounded_with_new_buffers_each_step():
+    """Forty decode steps, each with new output buffers (a new capture every
+    step, more than the 32 graphs a model keeps, so the oldest are dropped
+    while decoding continues): every step equals the direct launches."""
+    shape = synth.TINY_REC_FULL
+    log("graphs: new buffers every step")
+    gm, em = _models(shape)
+    B, P, S, k = 2, 8, 40, 2
+    toks = torch.from_numpy(synth.tokens(8, B, P + S, shape.vocab)).cuda()
+    kvg = gm.kv_cache("last_loop", k, B, 64)
+    kve = em.kv_cache("last_loop", k, B, 64)
+    gm.prefill(kvg, toks[:, :P].contiguous(), k, logits=False)
+    em.prefill(kve, toks[:, :P].contiguous(), k, logits=False)
+    for step in range(S):
+        t = toks[:, P + step].contiguous()
+        a = gm.decode_step(kvg, t, k, hidden=True, states=True)
+        b = em.decode_step(kve, t, k, hidden=True, states=True)
+        torch.cuda.synchronize()
+        _same(a, b, f"step {step}")
+    assert kvg.length == P + S

@@ -264,6 +264,9 @@ def test_long_context_per_loop_decode_matches_prefill(full):
     torch.cuda.synchronize()
     kv.buffer.copy_(snap)
     del snap
+    # the device memory is restored: declare its positions valid again (a
+    # plain roll-back by a whole chunk is refused once the rings wrapped)
+    kv.reset()
     kv.set_length(L - CH)
     gm.prefill(kv, dtoks[:, L - CH:L - n_dec], k, ws=ws, logits=False)
     for j in range(n_dec):
@@ -339,8 +342,8 @@ def test_selfspec_full_shape_matches_plain_decode(full):
 
 
 def test_prefix_copy_full_shape_continuation(full):
-    """Prefix caching at full shape: an 1100-token prefix (the 1024-row
-    sliding-window rings have wrapped) prefilled once for one sequence and
+    """Prefix caching at full shape: an 1100-token prefix (the sliding-window
+    rings of 1,024 + 64 rows have wrapped) prefilled once for one sequence and
     copied into two, then a 40-token suffix and one decode step, matches
     prefilling the whole prompt for both sequences, bit for bit: the prefix
     runs the large-M kernels either way (1,100 or 2,200 rows), which compute

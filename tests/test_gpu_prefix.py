@@ -72,8 +72,9 @@ def _check_continuation(M, shape, mode, k, n, T, n_dec, B, seed, dst_max=None, s
 @pytest.mark.parametrize("k", [1, 3])
 @pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
 def test_tiny_prefix_copy(M, mode, k):
-    # 21-token prefix: the window-16 rings have wrapped in the source
-    _check_continuation(M, synth.TINY_REC_FULL, mode, k, n=21, T=7, n_dec=2, B=3, seed=41)
+    # 101-token prefix: the sliding-window rings (window 16 + 64 rows) have
+    # wrapped in the source
+    _check_continuation(M, synth.TINY_REC_FULL, mode, k, n=101, T=7, n_dec=2, B=3, seed=41)
 
 
 @pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
@@ -84,6 +85,7 @@ def test_tiny_prefix_copy_within_one_cache(M, mode):
 
 def test_tiny_prefix_copy_into_smaller_ring(M):
     # destination max_seq 8: its sliding-window rings hold 8 rows, the source's 16
+    # (max_seq 13 rounded up to 8 rows)
     _check_continuation(M, synth.TINY_REC_FULL, "last_loop", 2, n=5, T=2, n_dec=1, B=2, seed=44,
                         dst_max=8)
 

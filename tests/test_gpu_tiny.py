@@ -76,6 +76,60 @@ def test_tiny_parity(lib, shape_name, k, mode, pattern):
     assert kv.length == 64
 
 
+LONG = [(0, 50), (50, 97), (97, 98), (98, 187), (187, 190)] + [(t, t + 1) for t in range(190, 210)]
+
+
+@pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
+@pytest.mark.parametrize("k", [1, 3])
+@pytest.mark.parametrize("shape_name", list(SHAPES))
+def test_tiny_parity_ring_wraps(lib, shape_name, k, mode):
+    """210 positions (the sliding-window rings of W + 64 = 80 rows wrap more
+    than twice; one chunk of 89 tokens is longer than a ring), chunked then
+    decoded, against the oracle."""
+    shape = SHAPES[shape_name]
+    log(f"ring wraps {shape_name} k={k} {mode}")
+    W, gm, om = _setup(lib, shape)
+    B = 2
+    toks = synth.tokens(6, B, 210, shape.vocab)
+    kv = gm.kv_cache(mode, 4, B, 256)
+    oc = ref.Cache(shape, mode, B)
+    for a, b in LONG:
+        tt = torch.from_numpy(toks[:, a:b].copy()).cuda()
+        if b - a == 1:
+            out = gm.decode_step(kv, tt[:, 0].contiguous(), k, hidden=True, states=False)
+        else:
+            out = gm.prefill(kv, tt, k, hidden=True)
+        torch.cuda.synchronize()
+        o = om.step(oc, toks[:, a:b], k)
+        per_token_check(out["hidden"].cpu().numpy().reshape(B, b - a, -1), o["hidden"], f"hidden[{a}:{b}]")
+        per_token_check(out["logits"].cpu().numpy(), o["logits"], f"logits[{a}:{b}]")
+    assert kv.length == 210
+
+
+def test_rollback_then_redecode_equals_first_pass(lib):
+    """On a cache whose rings have wrapped, decoding 40 positions, shortening
+    by DORY_KV_ROLLBACK (64) from the longest length and decoding the same
+    tokens again gives bit-identical outputs: the ring slack kept every key
+    the windows need."""
+    from looped_ngpt_transformer_fwd_amd import _lib as C
+    shape = synth.TINY_REC_FULL
+    log("rollback then re-decode")
+    W, gm, om = _setup(lib, shape)
+    B, k, P = 2, 2, 150
+    toks = synth.tokens(7, B, P + 64, shape.vocab)
+    kv = gm.kv_cache("per_loop", 2, B, 256)
+    gm.prefill(kv, torch.from_numpy(toks[:, :P].copy()).cuda(), k, logits=False)
+    first = []
+    for t in range(P, P + 64):
+        first.append(gm.decode_step(kv, torch.from_numpy(toks[:, t].copy()).cuda(), k, hidden=True)["hidden"])
+    torch.cuda.synchronize()
+    kv.set_length(P + 64 - C.DORY_KV_ROLLBACK)
+    for i, t in enumerate(range(P, P + 64)):
+        h = gm.decode_step(kv, torch.from_numpy(toks[:, t].copy()).cuda(), k, hidden=True)["hidden"]
+        torch.cuda.synchronize()
+        assert torch.equal(h, first[i]), f"position {t}"
+
+
 @pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
 def test_kv_cache_contents_at_ring_slots(lib, mode):
     """The persistent K entries sit at position mod ring (sliding window) or
@@ -84,16 +138,16 @@ def test_kv_cache_contents_at_ring_slots(lib, mode):
     log(f"kv contents {mode}")
     W, gm, om = _setup(lib, shape)
     B, k = 2, 3
-    toks = synth.tokens(4, B, 50, shape.vocab)
-    kv = gm.kv_cache(mode, 4, B, 64)
+    toks = synth.tokens(4, B, 200, shape.vocab)
+    kv = gm.kv_cache(mode, 4, B, 256)
     oc = ref.Cache(shape, mode, B)
-    for a, b in [(0, 21), (21, 45), (45, 50)]:
+    for a, b in [(0, 21), (21, 45), (45, 50), (50, 139), (139, 171), (171, 200)]:
         gm.prefill(kv, torch.from_numpy(toks[:, a:b].copy()).cuda(), k, logits=False)
         om.step(oc, toks[:, a:b], k)
     torch.cuda.synchronize()
     kinds = ref.layer_kinds(shape)
     dh, nkv = shape.head_dim, shape.n_kv_heads
-    L = 50
+    L = 200
     for s, kind in enumerate(kinds):
         if kind == "mlp":
             continue
