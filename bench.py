@@ -151,7 +151,39 @@ def time_steps(fn, steps):
     return time.perf_counter() - t0
 
 
-def decode_mxfp8(gm, shape, B=64, steps=4):
+def fill_random(kv, g):
+    """Synthesized cache contents: N(0, 0.02^2) bf16 in every slot."""
+    buf = kv.buffer.view(torch.bfloat16)
+    chunk = 1 << 28
+    for o in range(0, buf.numel(), chunk):
+        n = min(chunk, buf.numel() - o)
+        buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
+
+
+def greedy_decode(gm, kv, first, k, ws, ctx, warmup, steps):
+    """Greedy decoding from position ctx, each step's input token being the
+    previous step's greedy choice (fixed token and logits buffers, so the
+    steps replay captured graphs). The cache is declared to hold ctx valid
+    positions (its K/V synthesized beforehand). Returns the seconds of the
+    `steps` timed steps, which follow `warmup` untimed ones."""
+    B = first.shape[0]
+    toks = [first.clone(), torch.empty_like(first)]
+    lg = torch.empty(B, gm.shape.vocab, dtype=torch.float32, device="cuda")
+    kv.reset()
+    kv.set_length(ctx)
+    i = [0]
+
+    def step():
+        gm.decode_step(kv, toks[i[0] % 2], k, ws=ws, into={"logits": lg, "next": toks[(i[0] + 1) % 2]})
+        i[0] += 1
+    for _ in range(warmup):
+        step()
+    dt = time_steps(step, steps)
+    assert kv.length == ctx + warmup + steps
+    return dt
+
+
+def decode_mxfp8(gm, shape, B=64, steps=256):
     """Decode tokens/s with MXFP8 weights (W8A16) against bf16: at the same
     32768-token context (last-loop, k = 1, 2, 4) and at a 2048-token context
     (k = 4), where the weight stream is a larger share of a step. The model
@@ -173,51 +205,36 @@ def decode_mxfp8(gm, shape, B=64, steps=4):
     return out
 
 
-def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=4, mixed=True):
-    """Decode tokens/s at a fixed position with `ctx` cached tokens whose K/V
-    are synthesized at random (the cost of a step depends on the context
-    length, not on the cached values)."""
+def decode_table(gm, shape, ks, modes, B=64, ctx=32768, steps=256, warmup=2, mixed=True):
+    """Decode tokens/s: `steps` greedy steps (token fed back) after `ctx`
+    cached tokens whose K/V are synthesized at random (the cost of a step
+    depends on the context length, not on the cached values), per (mode, k),
+    with the cache size of each."""
     out = {}
     ws = gm.workspace(B, 1)
     g = torch.Generator(device="cuda")
     g.manual_seed(1)
     toks = torch.randint(0, shape.vocab, (B,), dtype=torch.int32, device="cuda", generator=g)
+    n_seq = ctx + warmup + steps
     for mode in modes:
         for k in ks:
-            kv = gm.kv_cache(mode, k, B, ctx + 1)
-            buf = kv.buffer.view(torch.bfloat16)
-            chunk = 1 << 28
-            for o in range(0, buf.numel(), chunk):
-                n = min(chunk, buf.numel() - o)
-                buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
-
-            def one():
-                kv.set_length(ctx)
-                gm.decode_step(kv, toks, k, ws=ws, logits=True, next_token=True)
-            one()
-            dt = time_steps(one, steps)
+            kv = gm.kv_cache(mode, k, B, n_seq)
+            fill_random(kv, g)
+            dt = greedy_decode(gm, kv, toks, k, ws, ctx, warmup, steps)
             out[f"{mode}_k{k}"] = round(B * steps / dt, 1)
             out[f"{mode}_k{k}_kv_gb"] = round(kv.buffer.numel() / 1e9, 2)
-            del kv, buf
+            progress(f"decode B={B} ctx={ctx} {mode} k={k}: {out[f'{mode}_k{k}']} tokens/s")
+            del kv
             torch.cuda.empty_cache()
     if mixed and "last_loop" in modes and max(ks) >= 4:
         # one batch whose sequences run different loop counts, 4:1:1:1 over
         # k = 1, 2, 3, 4 (36 / 9 / 9 / 10 of 64 sequences)
         k_rows = [1] * 36 + [2] * 9 + [3] * 9 + [4] * 10
-        kv = gm.kv_cache("last_loop", 4, B, ctx + 1)
-        buf = kv.buffer.view(torch.bfloat16)
-        chunk = 1 << 28
-        for o in range(0, buf.numel(), chunk):
-            n = min(chunk, buf.numel() - o)
-            buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
-
-        def mixed():
-            kv.set_length(ctx)
-            gm.decode_step(kv, toks, k_rows, ws=ws, logits=True, next_token=True)
-        mixed()
-        dt = time_steps(mixed, steps)
+        kv = gm.kv_cache("last_loop", 4, B, n_seq)
+        fill_random(kv, g)
+        dt = greedy_decode(gm, kv, toks, k_rows, ws, ctx, warmup, steps)
         out["last_loop_mixed_k1k2k3k4_4111"] = round(B * steps / dt, 1)
-        del kv, buf
+        del kv
         torch.cuda.empty_cache()
     return out
 
@@ -227,17 +244,15 @@ def decode_selfspec(gm, shape, B=64, ctx=32768, gamma=4, k_draft=1, k_verify=4, 
     k_draft, then one verification pass over gamma + 1 positions at k_verify.
     With random weights the acceptance rate carries no information, so the
     round time is reported against the k_verify decode step: a round pays
-    off when the batch accepts more than (round / step - 1) drafts."""
+    off when the batch accepts more than (round / step - 1) drafts. The
+    sampled round (temperature 1) drafts by sampling and applies the
+    rejection rule per sequence."""
     ws = gm.workspace(B, gamma + 1)
     g = torch.Generator(device="cuda")
     g.manual_seed(2)
     toks = torch.randint(0, shape.vocab, (B,), dtype=torch.int32, device="cuda", generator=g)
     kv = gm.kv_cache("per_loop", k_verify, B, ctx + gamma + 1)
-    buf = kv.buffer.view(torch.bfloat16)
-    chunk = 1 << 28
-    for o in range(0, buf.numel(), chunk):
-        n = min(chunk, buf.numel() - o)
-        buf[o:o + n] = (0.02 * torch.randn(n, device="cuda", generator=g)).to(torch.bfloat16)
+    fill_random(kv, g)
     acc = []
 
     def rnd():
@@ -247,13 +262,21 @@ def decode_selfspec(gm, shape, B=64, ctx=32768, gamma=4, k_draft=1, k_verify=4, 
     def plain():
         kv.set_length(ctx)
         gm.decode_step(kv, toks, k_verify, ws=ws, logits=True, next_token=True)
+    u = torch.rand(2 * gamma + 1, B, generator=g, device="cuda")
+
+    def rnd_sampled():
+        kv.set_length(ctx)
+        gm.selfspec_step_sampled(kv, toks, gamma, k_draft, k_verify, 1.0, u, ws=ws)
     rnd()
     plain()
+    rnd_sampled()
     t_round = time_steps(rnd, steps) / steps
     t_step = time_steps(plain, steps) / steps
-    del kv, buf
+    t_sampled = time_steps(rnd_sampled, steps) / steps
+    del kv
     torch.cuda.empty_cache()
     return {"round_ms": round(t_round * 1e3, 3), "decode_step_ms": round(t_step * 1e3, 3),
+            "round_sampled_ms": round(t_sampled * 1e3, 3),
             "break_even_accepted": round(t_round / t_step - 1, 2),
             "tok_s_all_accepted": round(B * (gamma + 1) / t_round, 1),
             "tok_s_none_accepted": round(B / t_round, 1),
@@ -335,18 +358,11 @@ class _RowGather:
         return synth.f64_from_bf16_bits(self.bits[idx])
 
 
-def cpu_baseline(k, n_tokens=512):
-    """The float64 oracle, unchanged, timed on this host's cores over a bounded
-    sample of the same workload: the first n_tokens tokens of sequence 0 at
-    loop count k, full model shape. Every attention sublayer is given one
-    drawn weight set and every MLP sublayer another (identical shapes and
-    arithmetic, a fraction of the host memory)."""
+def _oracle_full_model():
+    """The float64 oracle at the full model shape. Every attention sublayer
+    is given one drawn weight set and every MLP sublayer another (identical
+    shapes and arithmetic, a fraction of the host memory)."""
     from oracle import ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     sh = synth.FULL
     kinds = ref.layer_kinds(sh)
     W = synth.Weights(sh, kinds, 0)
@@ -362,7 +378,59 @@ def cpu_baseline(k, n_tokens=512):
     for n in ("lm_head", "s_z", "sub0.w_qkvg", "sub0.w_o", "sub0.s_qk", "sub0.alpha",
               "sub1.w_upgate", "sub1.w_down", "sub1.s_u", "sub1.s_v", "sub1.alpha"):
         weight(n)
-    om = ref.OracleModel(sh, weight)
+    return ref.OracleModel(sh, weight)
+
+
+def _oracle_context(ctx, cap, seed):
+    """A last-loop oracle cache (B=1) holding `ctx` positions of synthesized
+    K/V, `cap` positions long. Full-attention slots get a random block of
+    4096 positions repeated over the context; sliding-window slots get random
+    values in the last window only (the oracle reads no older key of them;
+    the rest of the array stays untouched zero pages)."""
+    from oracle import ref
+    sh = synth.FULL
+    rng = np.random.default_rng(seed)
+    c = ref.Cache(sh, ref.MODE_LAST, 1)
+    shp = (1, sh.n_kv_heads, cap, sh.head_dim)
+    for s, kind in enumerate(ref.layer_kinds(sh)):
+        if kind == ref.KIND_MLP:
+            continue
+        K, V = np.zeros(shp), np.zeros(shp)
+        if kind == ref.KIND_FULL:
+            blk = rng.standard_normal((2, 1, sh.n_kv_heads, 4096, sh.head_dim)) * 0.3
+            for a in range(0, ctx, 4096):
+                n = min(4096, ctx - a)
+                K[:, :, a:a + n] = blk[0, :, :, :n]
+                V[:, :, a:a + n] = blk[1, :, :, :n]
+        else:
+            lo = max(0, ctx - sh.window)
+            K[:, :, lo:ctx] = rng.standard_normal((1, sh.n_kv_heads, ctx - lo, sh.head_dim)) * 0.3
+            V[:, :, lo:ctx] = rng.standard_normal((1, sh.n_kv_heads, ctx - lo, sh.head_dim)) * 0.3
+        c.K[(s, 0)], c.V[(s, 0)] = K, V
+    c.length = ctx
+    return c
+
+
+def cpu_baseline(k, n_tokens=512, slices=True):
+    """The float64 oracle, unchanged, timed on this host's cores over bounded
+    samples of the workloads. Main figure: the first n_tokens tokens of
+    sequence 0 of the prefill at loop count k, full model shape. Slices:
+    one decode step of one sequence after 32,768 cached tokens (k = 1 and 4,
+    last-loop; per-loop caching computes the same), and one decode step at
+    the end of a 262,144-token context (k = 4, last-loop), with synthesized
+    cached K/V (the oracle's attention contracts over the whole prefix per
+    query in one thread, so a slice of 16 such queries already takes
+    minutes). Both slices run the oracle's literal
+    last-loop form (write the step's entries, then read the cache), which
+    leaves its cache arrays in place."""
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sh = synth.FULL
+    om = _oracle_full_model()
     toks = synth.tokens(0, 1, n_tokens, sh.vocab)
     t0 = time.perf_counter()
     om.step(ref.Cache(sh, ref.MODE_LAST, 1), toks, k)
@@ -373,11 +441,40 @@ def cpu_baseline(k, n_tokens=512):
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 oracle, full 72-sublayer shape, k={k}, sequence 0 tokens "
-                      f"0..{n_tokens - 1} (of 4 x 8192), one prefill step, {dt:.1f} s",
-            "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
+    out = {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"float64 oracle, full 72-sublayer shape, k={k}, sequence 0 tokens "
+                     f"0..{n_tokens - 1} (of 4 x 8192), one prefill step, {dt:.1f} s",
+           "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+           "precision": "float64"}
+    if not slices:
+        return out
+    sl = {}
+    progress(f"oracle prefill sample: {n_tokens / dt:.2f} tokens/s")
+    ctx = 32768
+    cache = _oracle_context(ctx, ctx + 1, seed=11)
+    tok = synth.tokens(1, 1, 1, sh.vocab)
+    for kk in (1, 4):
+        cache.length = ctx
+        t0 = time.perf_counter()
+        om.step(cache, tok, kk, literal_overwrite=True, logits="last")
+        d = time.perf_counter() - t0
+        sl[f"decode_ctx32768_k{kk}"] = {"tokens_s": round(1 / d, 4), "s": round(d, 2),
+                                        "sample": "B=1, one decode step at position 32,768, last-loop"}
+    del cache
+    progress("oracle decode slices done")
+    total, nq = 262144, 1
+    cache = _oracle_context(total - nq, total, seed=12)
+    toks = synth.tokens(2, 1, nq, sh.vocab)
+    t0 = time.perf_counter()
+    om.step(cache, toks, 4, literal_overwrite=True, logits="last")
+    d = time.perf_counter() - t0
+    sl["long_context_k4"] = {"tokens_s": round(nq / d, 4), "s": round(d, 2),
+                             "sample": f"B=1, the last {nq} position(s) of a {total}-token sequence "
+                                       f"in one step over {total - nq} cached positions, k=4, last-loop"}
+    del cache
+    out["slices"] = sl
+    return out
 
 
 def main():
@@ -489,6 +586,9 @@ def main():
             pre[f"k{kk}"] = round(B * T * 2 / d2, 1)
             del kv2
         result["prefill_tok_s"] = dict(sorted(pre.items()))
+        # cache size of the prefill configuration per policy and loop count
+        result["prefill_kv_gb"] = {f"{md}_k{kk}": round(M.kv_bytes(shape, md, kk, B, T) / 1e9, 3)
+                                   for md in ("last_loop", "per_loop") for kk in (1, 2, 4)}
         del kv, ws
         torch.cuda.empty_cache()
         progress("prefill k-sweep done")
@@ -502,7 +602,8 @@ def main():
         result["prefix_copy"] = prefix_copy(gm, shape)
         result["long_context"] = long_context(gm, shape)
         progress("long context done")
-        result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), greedy, 4 steps each; "
+        result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), then 256 greedy "
+                                   "steps with each step's token fed back (2 untimed first); "
                                    "mixed: per-sequence loop counts 1/2/3/4 for 36/9/9/10 sequences; "
                                    "mxfp8: projection weights in MXFP8 (W8A16), embedding and LM head "
                                    "bf16; ctx2048: 2048 cached tokens")

@@ -203,19 +203,25 @@ class Model:
         return self._step(kv, tokens, B, T, k, ws, logits, next_token, hidden, states, decode=False)
 
     def decode_step(self, kv, tokens, k, ws=None, logits=True, next_token=True, hidden=False,
-                    states=False):
-        """tokens: int32 device tensor [B]."""
+                    states=False, into=None):
+        """tokens: int32 device tensor [B]. `into` (optional dict) supplies the
+        "logits" [B, V] fp32 and/or "next" [B] int32 tensors to write into
+        (fixed buffers let repeated steps replay one captured graph)."""
         B = tokens.shape[0]
-        return self._step(kv, tokens, B, 1, k, ws, logits, next_token, hidden, states, decode=True)
+        return self._step(kv, tokens, B, 1, k, ws, logits, next_token, hidden, states, decode=True,
+                          into=into)
 
-    def _step(self, kv, tokens, B, T, k, ws, logits, next_token, hidden, states, decode):
+    def _step(self, kv, tokens, B, T, k, ws, logits, next_token, hidden, states, decode, into=None):
         dev = tokens.device
         sh = self.shape
         if ws is None:
             ws = self.workspace(B, T, dev)
         out = {}
-        lg = torch.empty(B, sh.vocab, dtype=torch.float32, device=dev) if logits else None
-        nx = torch.empty(B, dtype=torch.int32, device=dev) if next_token else None
+        into = into or {}
+        lg = (into.get("logits") if "logits" in into else
+              torch.empty(B, sh.vocab, dtype=torch.float32, device=dev)) if logits else None
+        nx = (into.get("next") if "next" in into else
+              torch.empty(B, dtype=torch.int32, device=dev)) if next_token else None
         hd = torch.empty(B, T, sh.d_model, dtype=torch.float32, device=dev) if hidden else None
         rows = None
         if isinstance(k, (list, tuple)):
