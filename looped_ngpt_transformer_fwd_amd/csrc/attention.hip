@@ -719,18 +719,24 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   }
 }
 
-// grid B * n_q, block DH. The split maxima go through LDS once; the weighted
-// sums keep eight splits' loads in flight per thread.
-__global__ void __launch_bounds__(128)
+// grid B * n_q, block 1024 = G groups of dh threads (thread d of a group
+// holds output dim d). Group j merges splits j, j + G, ... online (running
+// maximum, rescaled sum and output), loading eight splits at a time, so a
+// long context (hundreds of splits) costs a few round trips; the G group
+// results are merged through LDS.
+constexpr int COMB_NT = 1024;
+__global__ void __launch_bounds__(COMB_NT)
 attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const uint16_t* gate,
                            uint16_t* z, RowLoops rl, int sk, int window, int64_t p0,
                            const int64_t* p0_dev) {
-  __shared__ float wsc[2048];  // 2^(m_s - M) per split (nsplit <= 2048)
-  __shared__ float pm[128];    // per-thread partial maxima (blockDim = dh <= 128)
-  const int bh = blockIdx.x, d = threadIdx.x;
+  __shared__ float gm[COMB_NT / 32], gl[COMB_NT / 32];
+  __shared__ float go[COMB_NT];
+  const int bh = blockIdx.x;
   const int b = bh / n_q, h = bh % n_q;
+  const int G = COMB_NT / dh, grp = threadIdx.x / dh, d = threadIdx.x - grp * dh;
+  const int64_t idx = (int64_t)b * n_q * dh + h * dh + d;
   if (rl.k_rows && rl.loop >= rl.k_rows[b]) {  // left the loop: no partials were written
-    z[(int64_t)b * n_q * dh + h * dh + d] = 0;
+    if (grp == 0) z[idx] = 0;
     return;
   }
   const int64_t stride = dh + 2;
@@ -743,40 +749,44 @@ attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const
     const int64_t ns = (p + 1 - lo / 64 * 64 + sk - 1) / sk;
     nsplit = (int)min((int64_t)nsplit, max((int64_t)1, ns));
   }
-  float M = -INFINITY;
-  for (int s = d; s < nsplit; s += blockDim.x) M = fmaxf(M, pp[s * stride]);
-  pm[d] = M;
-  __syncthreads();
-  M = -INFINITY;
-  for (int t = 0; t < (int)blockDim.x; ++t) M = fmaxf(M, pm[t]);
-  float L = 0.f;
-  for (int s = d; s < nsplit; s += blockDim.x) {
-    const float m = pp[s * stride];
-    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-    wsc[s] = w;
-  }
-  __syncthreads();
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 8 <= nsplit; s += 8) {
-    float o[8], l[8];
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = grp; s0 < nsplit; s0 += 8 * G) {
+    float mm[8], ll[8], oo[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      o[j] = pp[(s + j) * stride + 2 + d];
-      l[j] = pp[(s + j) * stride + 1];
+      const int sp = s0 + j * G;
+      const bool ok = sp < nsplit;
+      mm[j] = ok ? pp[sp * stride] : -INFINITY;
+      ll[j] = ok ? pp[sp * stride + 1] : 0.f;
+      oo[j] = ok ? pp[sp * stride + 2 + d] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      acc += o[j] * wsc[s + j];
-      L += l[j] * wsc[s + j];
+      if (mm[j] == -INFINITY) continue;  // no split, or a split without keys
+      const float mn = fmaxf(M, mm[j]);
+      const float fa = exp2f(M - mn), fb = exp2f(mm[j] - mn);
+      L = L * fa + ll[j] * fb;
+      O = O * fa + oo[j] * fb;
+      M = mn;
     }
   }
-  for (; s < nsplit; ++s) {
-    acc += pp[s * stride + 2 + d] * wsc[s];
-    L += pp[s * stride + 1] * wsc[s];
+  if (d == 0) {
+    gm[grp] = M;
+    gl[grp] = L;
   }
-  const int64_t idx = (int64_t)b * n_q * dh + h * dh + d;
-  z[idx] = f2bf(acc / L * bf2f(gate[idx]));
+  go[threadIdx.x] = O;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mx = -INFINITY;
+  for (int j = 0; j < G; ++j) Mx = fmaxf(Mx, gm[j]);
+  float Lt = 0.f, Ot = 0.f;
+  for (int j = 0; j < G; ++j) {
+    if (gm[j] == -INFINITY) continue;
+    const float w = exp2f(gm[j] - Mx);
+    Lt += gl[j] * w;
+    Ot += go[j * dh + d] * w;
+  }
+  z[idx] = f2bf(Ot / Lt * bf2f(gate[idx]));
 }
 
 template <int DH, int GRP>
@@ -806,7 +816,7 @@ hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st
     hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_MAXK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q), dim3(DH), 0, st, part, nsplit,
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q), dim3(COMB_NT), 0, st, part, nsplit,
                      a.n_q, DH, a.gate, a.z, a.rl, sk, a.window, a.p0, a.p0_dev);
   return hipGetLastError();
 }

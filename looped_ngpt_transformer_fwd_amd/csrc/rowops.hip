@@ -33,14 +33,48 @@ embed_kernel(const int32_t* tok, const uint16_t* E, int vocab, int d, float* h32
   }
 }
 
+// Sum of split-K partials p[s * ss], s < nsplit (<= 32), in split order;
+// the loads of up to 16 splits are all issued before the first add (the
+// partials come from another kernel: L2 or further away, so each round trip
+// is long against the arithmetic).
+__device__ __forceinline__ float4 sum_splits4(const float* p, int nsplit, int64_t ss) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nsplit; s0 += 16) {
+    float4 t[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      t[j] = s0 + j < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + j) * ss) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc.x += t[j].x; acc.y += t[j].y; acc.z += t[j].z; acc.w += t[j].w;
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float sum_splits(const float* p, int nsplit, int64_t ss) {
+  float acc = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += 16) {
+    float t[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = s0 + j < nsplit ? p[(s0 + j) * ss] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += t[j];
+  }
+  return acc;
+}
+
 // h <- N(h + alpha (N(y) - h)); optional aux copy of the result, optional
 // boundary h <- N(result + x). Y16: y is one bf16 matrix (the large-M
-// projections' output), else nsplit fp32 split-K partials.
-template <bool Y16>
-__global__ void __launch_bounds__(NT_ROW)
+// projections' output), else nsplit fp32 split-K partials. One workgroup
+// per row, NT threads, each holding d / (4 NT) float4 columns; every load
+// of the row (h, alpha, x, the partials) is issued up front.
+template <bool Y16, int NT>
+__global__ void __launch_bounds__(NT)
 update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss, int64_t ldy,
               const float* alpha, int d, const float* x, float* aux, RowLoops rl) {
-  __shared__ float red[NT_ROW / 64];
+  constexpr int MV = 4 * MAXV * NT_ROW / (4 * NT);  // float4 per thread for d <= 4096
+  __shared__ float red[NT / 64];
   const int m = blockIdx.x;
   if (rl.k_rows) {
     const int kb = rl.k_rows[m / rl.T];
@@ -48,53 +82,32 @@ update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss,
     if (rl.loop == kb - 1) x = nullptr;  // its last loop: no boundary into another one
   }
   const int nv = d >> 2;
-  float4 hv[MAXV], yv[MAXV];
+  float4 hv[MV], yv[MV], av[MV], xv[MV];
   float syy = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int c = threadIdx.x + i * NT_ROW;
+  for (int i = 0; i < MV; ++i) {
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
       hv[i] = reinterpret_cast<const float4*>(h32 + (int64_t)m * d)[c];
+      av[i] = reinterpret_cast<const float4*>(alpha)[c];
+      if (x) xv[i] = reinterpret_cast<const float4*>(x + (int64_t)m * d)[c];
       if (Y16) {
         const ushort4 t = reinterpret_cast<const ushort4*>(reinterpret_cast<const uint16_t*>(y) +
                                                            (int64_t)m * ldy)[c];
-        const float4 acc = make_float4(bf2f(t.x), bf2f(t.y), bf2f(t.z), bf2f(t.w));
-        yv[i] = acc;
-        syy += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
-        continue;
+        yv[i] = make_float4(bf2f(t.x), bf2f(t.y), bf2f(t.z), bf2f(t.w));
+      } else {
+        yv[i] = sum_splits4(y + (int64_t)m * ldy + 4 * c, nsplit, ss);
       }
-      // split-K partials: four independent accumulators keep loads in flight
-      float4 a4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      int s = 0;
-      for (; s + 4 <= nsplit; s += 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 t = reinterpret_cast<const float4*>(y + (s + j) * ss + (int64_t)m * ldy)[c];
-          a4[j].x += t.x; a4[j].y += t.y; a4[j].z += t.z; a4[j].w += t.w;
-        }
-      }
-      for (; s < nsplit; ++s) {
-        const float4 t = reinterpret_cast<const float4*>(y + s * ss + (int64_t)m * ldy)[c];
-        a4[0].x += t.x; a4[0].y += t.y; a4[0].z += t.z; a4[0].w += t.w;
-      }
-      float4 acc;
-      acc.x = (a4[0].x + a4[1].x) + (a4[2].x + a4[3].x);
-      acc.y = (a4[0].y + a4[1].y) + (a4[2].y + a4[3].y);
-      acc.z = (a4[0].z + a4[1].z) + (a4[2].z + a4[3].z);
-      acc.w = (a4[0].w + a4[1].w) + (a4[2].w + a4[3].w);
-      yv[i] = acc;
-      syy += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+      syy += yv[i].x * yv[i].x + yv[i].y * yv[i].y + yv[i].z * yv[i].z + yv[i].w * yv[i].w;
     }
   }
-  const float iy = 1.0f / sqrtf(block_sum<NT_ROW>(syy, red));
+  const float iy = 1.0f / sqrtf(block_sum<NT>(syy, red));
   float stt = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int c = threadIdx.x + i * NT_ROW;
+  for (int i = 0; i < MV; ++i) {
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
-      const float4 a = reinterpret_cast<const float4*>(alpha)[c];
+      const float4 a = av[i];
       float4 t;
       t.x = hv[i].x + a.x * (yv[i].x * iy - hv[i].x);
       t.y = hv[i].y + a.y * (yv[i].y * iy - hv[i].y);
@@ -104,10 +117,10 @@ update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss,
       stt += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
     }
   }
-  float it = 1.0f / sqrtf(block_sum<NT_ROW>(stt, red));
+  float it = 1.0f / sqrtf(block_sum<NT>(stt, red));
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int c = threadIdx.x + i * NT_ROW;
+  for (int i = 0; i < MV; ++i) {
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
       hv[i].x *= it; hv[i].y *= it; hv[i].z *= it; hv[i].w *= it;
       if (aux) reinterpret_cast<float4*>(aux + (int64_t)m * d)[c] = hv[i];
@@ -116,23 +129,22 @@ update_kernel(float* h32, uint16_t* h16, const float* y, int nsplit, int64_t ss,
   if (x) {
     float suu = 0.f;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int c = threadIdx.x + i * NT_ROW;
+    for (int i = 0; i < MV; ++i) {
+      const int c = threadIdx.x + i * NT;
       if (c < nv) {
-        const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)m * d)[c];
-        hv[i].x += xv.x; hv[i].y += xv.y; hv[i].z += xv.z; hv[i].w += xv.w;
+        hv[i].x += xv[i].x; hv[i].y += xv[i].y; hv[i].z += xv[i].z; hv[i].w += xv[i].w;
         suu += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
       }
     }
-    it = 1.0f / sqrtf(block_sum<NT_ROW>(suu, red));
+    it = 1.0f / sqrtf(block_sum<NT>(suu, red));
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
+    for (int i = 0; i < MV; ++i) {
       hv[i].x *= it; hv[i].y *= it; hv[i].z *= it; hv[i].w *= it;
     }
   }
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int c = threadIdx.x + i * NT_ROW;
+  for (int i = 0; i < MV; ++i) {
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
       reinterpret_cast<float4*>(h32 + (int64_t)m * d)[c] = hv[i];
       if (h16) {  // no bf16 shadow in the fp32 build
@@ -188,11 +200,8 @@ __global__ void swiglu_partials_kernel(const float* p, int nsplit, int64_t ss, i
   if (idx >= (int64_t)M * F) return;
   const int64_t m = idx / F;
   const int f = (int)(idx - m * F);
-  float up = 0.f, gt = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    up += p[s * ss + m * 2 * F + f];
-    gt += p[s * ss + m * 2 * F + F + f];
-  }
+  float up = sum_splits(p + m * 2 * F + f, nsplit, ss);
+  float gt = sum_splits(p + m * 2 * F + F + f, nsplit, ss);
   up *= s_u[f];
   gt *= s_v[f];
   a[idx] = f2bf(gt / (1.f + __expf(-gt)) * up);
@@ -224,11 +233,8 @@ qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq
     if (hh >= nq + nkv) return;  // whole head groups exit together
     const float c = cs_tab[(int64_t)t * half + i], sn = sn_tab[(int64_t)t * half + i];
     const int col = hh < nq ? hh * dh : dq + (hh - nq) * dh;
-    float x1 = 0.f, x2 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      x1 += row[s * ss + col + i];
-      x2 += row[s * ss + col + i + half];
-    }
+    const float x1 = sum_splits(row + col + i, nsplit, ss);
+    const float x2 = sum_splits(row + col + i + half, nsplit, ss);
     const float r1 = x1 * c - x2 * sn;
     const float r2 = x2 * c + x1 * sn;
     float sq = r1 * r1 + r2 * r2;
@@ -248,14 +254,7 @@ qk_prep_kernel(const float* P, int nsplit, int64_t ss, int C, int64_t p0, int nq
   // v and gate columns: NT_ROW consecutive columns per block
   const int idx = ((int)blockIdx.y - ngroups) * NT_ROW + threadIdx.x;
   if (idx >= dkv + dq) return;
-  float v0 = 0.f, v1 = 0.f;
-  int s = 0;
-  for (; s + 2 <= nsplit; s += 2) {
-    v0 += row[s * ss + dq + dkv + idx];
-    v1 += row[(s + 1) * ss + dq + dkv + idx];
-  }
-  if (s < nsplit) v0 += row[s * ss + dq + dkv + idx];
-  const float v = v0 + v1;
+  const float v = sum_splits(row + dq + dkv + idx, nsplit, ss);
   if (idx < dkv) {
     if (rl.k_rows && rl.loop >= rl.k_rows[b]) return;  // left the loop: no K/V store
     const int g = idx / dh, d = idx - g * dh;
@@ -454,10 +453,13 @@ hipError_t launch_update(float* h32, uint16_t* h16, const float* y, int nsplit,
   if (state_out && copy_out) return hipErrorInvalidValue;
   if (y_bf16) {
     if (nsplit != 1 || ldy % 4 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(update_kernel<true>, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
+    hipLaunchKernelGGL((update_kernel<true, NT_ROW>), dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
                        split_stride, ldy, alpha, d, x, aux, rl);
   } else {
-    hipLaunchKernelGGL(update_kernel<false>, dim3(M), dim3(NT_ROW), 0, st, h32, h16, y, nsplit,
+    // split partials (short launches: decode, verification, chunks): one
+    // float4 column per thread, all partial loads in flight at once
+    if (nsplit < 1 || nsplit > 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((update_kernel<false, 1024>), dim3(M), dim3(1024), 0, st, h32, h16, y, nsplit,
                        split_stride, ldy, alpha, d, x, aux, rl);
   }
   return hipGetLastError();
