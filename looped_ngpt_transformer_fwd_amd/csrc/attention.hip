@@ -535,20 +535,29 @@ __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
 // Keys outside [lo, p] are never read (cache rows past p may not be written)
 // and enter as zero K/V rows with probability 0. The four waves merge their
 // (max, sum, o) in LDS into the split's partial.
-template <int DH, int GRP, int SPLITK>
-__global__ void __launch_bounds__(DEC_NT)
+// DIRECT (batches with at least one workgroup per CU per (sequence, KV
+// head)): one workgroup of NT threads takes every key of its (sequence, KV
+// head), wave w the 32-key blocks w, w + NT / 64, ..., and the merge writes
+// the gated output z itself (no partials, no combine launch).
+template <int DH, int GRP, int SPLITK, bool DIRECT = false, int NT = DEC_NT>
+__global__ void __launch_bounds__(NT)
 attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
-  constexpr int DEC_WKEYS = SPLITK / (DEC_NT / 64);  // keys per wave
+  constexpr int NWV = NT / 64;
+  constexpr int DEC_WKEYS = DIRECT ? 64 : SPLITK / NWV;  // keys per wave (split form)
   constexpr int NS = DH / 32;   // 32-dim slices of the q.k contraction
   constexpr int NB = DH / 16;   // 16-dim blocks of the output
   static_assert(GRP <= 16, "query heads per KV head must fit the 16-wide MFMA side");
-  __shared__ float wmax[DEC_NT / 64][GRP];
-  __shared__ float wsum[DEC_NT / 64][GRP];
-  __shared__ float wout[DEC_NT / 64][GRP][DH];
+  __shared__ float wmax[NWV][GRP];
+  __shared__ float wsum[NWV][GRP];
+  __shared__ float wout[NWV][GRP][DH];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  if (a.rl.k_rows && a.rl.loop >= a.rl.k_rows[b]) return;  // left the loop (merge writes zeros)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.rl.k_rows && a.rl.loop >= a.rl.k_rows[b]) {  // left the loop
+    if (DIRECT)  // (the split form's combine writes the zeros)
+      for (int i = tid; i < GRP * DH; i += NT) a.z[((int64_t)b * a.n_q + g * GRP) * DH + i] = 0;
+    return;
+  }
   const int G = lane >> 4, r = lane & 15;
   const int64_t bg = (int64_t)b * a.n_kv + g;
   const int64_t p = a.p0_dev ? *a.p0_dev : a.p0;
@@ -556,7 +565,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   if (a.window > 0) lo = max((int64_t)0, p - a.window + 1);
   const int64_t A = (lo / 64) * 64 + (int64_t)split * SPLITK;
   if (A > p) return;  // a split past the query's last key (launched for longer contexts)
-  const int64_t ua = max(lo, A), ub = min(p + 1, A + SPLITK);
+  const int64_t ua = max(lo, A), ub = DIRECT ? p + 1 : min(p + 1, A + SPLITK);
   const int64_t w0 = A + (int64_t)wave * DEC_WKEYS;
 
   bf16x8 qb[NS];
@@ -580,9 +589,9 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
       const_cast<uint16_t*>(a.vc + bg * DH * a.c_rows), (short)0, (int)kbytes, 0x00020000);
   const uint32_t OOB = 0xFFFFFFF0u;
 
-  // loads of block blk into (kf, vf): keys outside [lo, p] read as zeros
-  auto load = [&](int blk, bf16x8 (&kf)[2][NS], bf16x8 (&vf)[NB]) {
-    const int64_t u0 = w0 + 32 * blk;
+  // loads of the 32-key block from key u0 into (kf, vf): keys outside
+  // [lo, p] read as zeros
+  auto load = [&](int64_t u0, bf16x8 (&kf)[2][NS], bf16x8 (&vf)[NB]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int64_t u = u0 + 8 * (r >> 2) + 4 * t + (r & 3);
@@ -605,8 +614,7 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
       vf[nb] = __builtin_bit_cast(bf16x8, v);
     }
   };
-  auto compute = [&](int blk, const bf16x8 (&kf)[2][NS], bf16x8 (&vf)[NB]) {
-    const int64_t u0 = w0 + 32 * blk;
+  auto compute = [&](int64_t u0, const bf16x8 (&kf)[2][NS], bf16x8 (&vf)[NB]) {
     if (u0 + 31 < ua || u0 >= ub) return;  // the whole block is outside [lo, p]
     const int64_t uv = u0 + 8 * G;
     if (!(uv >= ua && uv + 7 < ub)) {
@@ -666,19 +674,36 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf[nb], o[nb], 0, 0, 0);
   };
 
-  // two register sets: the loads of block blk + 1 are in flight while block
-  // blk computes
-  constexpr int NBLK = DEC_WKEYS / 32;
-  static_assert(NBLK % 2 == 0, "blocks per wave come in pairs");
+  // two register sets: the loads of the next block are in flight while a
+  // block computes
   bf16x8 kfa[2][NS], vfa[NB], kfb[2][NS], vfb[NB];
-  load(0, kfa, vfa);
-  load(1, kfb, vfb);
+  if constexpr (DIRECT) {
+    // this wave's blocks: keys A + 32 (wave + NWV i), i < nbw
+    const int64_t nblk = (p + 1 - A + 31) / 32;
+    const int nbw = (int)((nblk - wave + NWV - 1) / NWV);
+    auto ub0 = [&](int i) { return A + 32 * ((int64_t)wave + (int64_t)NWV * i); };
+    if (nbw > 0) load(ub0(0), kfa, vfa);
+    if (nbw > 1) load(ub0(1), kfb, vfb);
+    for (int i = 0; i < nbw; i += 2) {
+      compute(ub0(i), kfa, vfa);
+      if (i + 2 < nbw) load(ub0(i + 2), kfa, vfa);
+      if (i + 1 < nbw) {
+        compute(ub0(i + 1), kfb, vfb);
+        if (i + 3 < nbw) load(ub0(i + 3), kfb, vfb);
+      }
+    }
+  } else {
+    constexpr int NBLK = DEC_WKEYS / 32;
+    static_assert(NBLK % 2 == 0, "blocks per wave come in pairs");
+    load(w0, kfa, vfa);
+    load(w0 + 32, kfb, vfb);
 #pragma unroll
-  for (int blk = 0; blk < NBLK; blk += 2) {
-    compute(blk, kfa, vfa);
-    if (blk + 2 < NBLK) load(blk + 2, kfa, vfa);
-    compute(blk + 1, kfb, vfb);
-    if (blk + 3 < NBLK) load(blk + 3, kfb, vfb);
+    for (int blk = 0; blk < NBLK; blk += 2) {
+      compute(w0 + 32 * blk, kfa, vfa);
+      if (blk + 2 < NBLK) load(w0 + 32 * (blk + 2), kfa, vfa);
+      compute(w0 + 32 * (blk + 1), kfb, vfb);
+      if (blk + 3 < NBLK) load(w0 + 32 * (blk + 3), kfb, vfb);
+    }
   }
 
   l_run += __shfl_xor(l_run, 16, 64);
@@ -696,19 +721,24 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < GRP * DH; i += DEC_NT) {
+  for (int i = tid; i < GRP * DH; i += NT) {
     const int h = i / DH, d = i % DH;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < DEC_NT / 64; ++w) M = fmaxf(M, wmax[w][h]);
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, wmax[w][h]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < DEC_NT / 64; ++w) {
+      for (int w = 0; w < NWV; ++w) {
         const float f = __builtin_amdgcn_exp2f(wmax[w][h] - M);
         L += wsum[w][h] * f;
         O += wout[w][h][d] * f;
       }
+    }
+    if constexpr (DIRECT) {
+      const int64_t zi = ((int64_t)b * a.n_q + g * GRP + h) * DH + d;
+      a.z[zi] = f2bf(O / L * bf2f(a.gate[zi]));
+      continue;
     }
     float* dst = part + (((int64_t)b * a.n_q + g * GRP + h) * nsplit + split) * (DH + 2);
     dst[2 + d] = O;
@@ -719,21 +749,24 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   }
 }
 
-// grid B * n_q, block 1024 = G groups of dh threads (thread d of a group
-// holds output dim d). Group j merges splits j, j + G, ... online (running
-// maximum, rescaled sum and output), loading eight splits at a time, so a
-// long context (hundreds of splits) costs a few round trips; the G group
-// results are merged through LDS.
+// grid B * n_q * (dh / dc), block G groups of dc threads: a workgroup
+// takes dc output dims of one (sequence, head), thread i of a group dim i.
+// Group j merges splits j, j + G, ... online (running maximum, rescaled sum
+// and output), loading eight splits at a time, so a long context (hundreds
+// of splits) costs a few round trips; the G group results are merged
+// through LDS.
 constexpr int COMB_NT = 1024;
 __global__ void __launch_bounds__(COMB_NT)
-attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const uint16_t* gate,
-                           uint16_t* z, RowLoops rl, int sk, int window, int64_t p0,
-                           const int64_t* p0_dev) {
+attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, int dc,
+                           const uint16_t* gate, uint16_t* z, RowLoops rl, int sk, int window,
+                           int64_t p0, const int64_t* p0_dev) {
   __shared__ float gm[COMB_NT / 32], gl[COMB_NT / 32];
   __shared__ float go[COMB_NT];
-  const int bh = blockIdx.x;
+  const int nch = dh / dc;
+  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
   const int b = bh / n_q, h = bh % n_q;
-  const int G = COMB_NT / dh, grp = threadIdx.x / dh, d = threadIdx.x - grp * dh;
+  const int G = blockDim.x / dc, grp = threadIdx.x / dc, dl = threadIdx.x - grp * dc;
+  const int d = ch * dc + dl;
   const int64_t idx = (int64_t)b * n_q * dh + h * dh + d;
   if (rl.k_rows && rl.loop >= rl.k_rows[b]) {  // left the loop: no partials were written
     if (grp == 0) z[idx] = 0;
@@ -770,7 +803,7 @@ attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const
       M = mn;
     }
   }
-  if (d == 0) {
+  if (dl == 0) {
     gm[grp] = M;
     gl[grp] = L;
   }
@@ -784,7 +817,7 @@ attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, const
     if (gm[j] == -INFINITY) continue;
     const float w = exp2f(gm[j] - Mx);
     Lt += gl[j] * w;
-    Ot += go[j * dh + d] * w;
+    Ot += go[j * dc + dl] * w;
   }
   z[idx] = f2bf(Ot / Lt * bf2f(gate[idx]));
 }
@@ -803,8 +836,18 @@ int decode_split_keys(int64_t lo, int64_t p, bool window) {
   return p + 1 - lo / 64 * 64 > DEC_LONG ? DEC_LONGK : DEC_MAXK;
 }
 
+// Batches with at least 256 (sequence, KV head) pairs take the direct form:
+// every CU holds one of them, without split partials or a combine launch.
+constexpr int DEC_DIRECT_MIN = 256;
+constexpr int DEC_DIRECT_NT = 512;
+
 template <int DH, int GRP>
 hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st) {
+  if (a.B * a.n_kv >= DEC_DIRECT_MIN) {
+    hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, 0, true, DEC_DIRECT_NT>), dim3(1, a.n_kv, a.B),
+                       dim3(DEC_DIRECT_NT), 0, st, a, 1, part);
+    return hipGetLastError();
+  }
   dim3 grid(nsplit, a.n_kv, a.B);
   const int64_t lo = a.window > 0 ? std::max<int64_t>(0, a.p0 - a.window + 1) : 0;
   const int sk = decode_split_keys(lo, a.p0, a.window > 0);
@@ -816,8 +859,12 @@ hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st
     hipLaunchKernelGGL((attn_decode_kernel<DH, GRP, DEC_MAXK>), grid, dim3(DEC_NT), 0, st, a, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q), dim3(COMB_NT), 0, st, part, nsplit,
-                     a.n_q, DH, a.gate, a.z, a.rl, sk, a.window, a.p0, a.p0_dev);
+  // few splits: one group per head; up to 64: groups of DH threads;
+  // more (long contexts): 32-dim chunks of a head per workgroup, 32 groups
+  const int dc = nsplit > 64 ? 32 : DH;
+  const int nt = nsplit <= 8 ? DH : COMB_NT;
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q * (DH / dc)), dim3(nt), 0, st, part,
+                     nsplit, a.n_q, DH, dc, a.gate, a.z, a.rl, sk, a.window, a.p0, a.p0_dev);
   return hipGetLastError();
 }
 
