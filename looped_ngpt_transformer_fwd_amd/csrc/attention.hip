@@ -540,7 +540,7 @@ __device__ __forceinline__ bf16x8 load16_or_zero(const uint16_t* p, bool ok) {
 // head), wave w the 32-key blocks w, w + NT / 64, ..., and the merge writes
 // the gated output z itself (no partials, no combine launch).
 template <int DH, int GRP, int SPLITK, bool DIRECT = false, int NT = DEC_NT>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, 2)  // two waves per SIMD
 attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   constexpr int NWV = NT / 64;
   constexpr int DEC_WKEYS = DIRECT ? 64 : SPLITK / NWV;  // keys per wave (split form)
@@ -568,11 +568,9 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   const int64_t ua = max(lo, A), ub = DIRECT ? p + 1 : min(p + 1, A + SPLITK);
   const int64_t w0 = A + (int64_t)wave * DEC_WKEYS;
 
+  const bool holds_p = DIRECT || p < A + SPLITK;  // this workgroup's keys include p
+  __shared__ __attribute__((aligned(16))) uint16_t qs[GRP][DH];
   bf16x8 qb[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qb[s] = load16_or_zero(a.q + ((int64_t)b * a.n_q + g * GRP + (r < GRP ? r : 0)) * DH + 32 * s + 8 * G,
-                           r < GRP);
   floatx4 o[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -674,16 +672,82 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf[nb], o[nb], 0, 0, 0);
   };
 
+  auto prep = [&]() {
+    // Fused query/key transform: the group's query heads from the projection
+    // partials (RoPE, per-head L2 norm, s_qk) into LDS; the workgroup whose
+    // keys include p also computes the token's key and value and stores them
+    // in the cache before its key loads (the only workgroup that reads them).
+    if (a.qkv_part) {
+      constexpr int HALF = DH / 2;
+      const int64_t N = 2 * (int64_t)a.n_q * DH + 2 * (int64_t)a.n_kv * DH;
+      const float* row = a.qkv_part + (int64_t)b * N;
+      const int64_t prow = cache_row(p, a.ring);
+      const int nh = GRP + (holds_p ? 1 : 0);
+      for (int hh = wave; hh < nh; hh += NWV) {  // head GRP: the KV head's key
+        const int col = hh < GRP ? (g * GRP + hh) * DH : a.n_q * DH + g * DH;
+        float r1 = 0.f, r2 = 0.f;
+        if (lane < HALF) {
+          const float x1 = sum_splits(row + col + lane, a.qkv_nsplit, a.qkv_ss);
+          const float x2 = sum_splits(row + col + lane + HALF, a.qkv_nsplit, a.qkv_ss);
+          const float c = a.cs[lane], sn = a.sn[lane];
+          r1 = x1 * c - x2 * sn;
+          r2 = x2 * c + x1 * sn;
+        }
+        const float inv = 1.0f / sqrtf(wave_sum(r1 * r1 + r2 * r2));
+        if (lane < HALF) {
+          const uint16_t v1 = f2bf(a.s_qk[lane] * r1 * inv), v2 = f2bf(a.s_qk[lane + HALF] * r2 * inv);
+          if (hh < GRP) {
+            qs[hh][lane] = v1;
+            qs[hh][lane + HALF] = v2;
+          } else {
+            uint16_t* kr = const_cast<uint16_t*>(a.kc) + (bg * a.c_rows + prow) * DH;
+            kr[lane] = v1;
+            kr[lane + HALF] = v2;
+          }
+        }
+      }
+      if (holds_p) {
+        for (int d = tid; d < DH; d += NT) {
+          const float v = sum_splits(row + (int64_t)a.n_q * DH + (int64_t)a.n_kv * DH + g * DH + d,
+                                     a.qkv_nsplit, a.qkv_ss);
+          const_cast<uint16_t*>(a.vc)[(bg * DH + d) * a.c_rows + prow] = f2bf(v);
+        }
+        __threadfence_block();  // the token's K/V stores complete before the key loads
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (a.qkv_part) {
+        qb[s] = *reinterpret_cast<const bf16x8*>(&qs[r < GRP ? r : 0][32 * s + 8 * G]);
+        if (r >= GRP) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qb[s][j] = (__bf16)0.f;
+        }
+      } else {
+        qb[s] = load16_or_zero(a.q + ((int64_t)b * a.n_q + g * GRP + (r < GRP ? r : 0)) * DH + 32 * s + 8 * G,
+                               r < GRP);
+      }
+    }
+  };
+
   // two register sets: the loads of the next block are in flight while a
   // block computes
   bf16x8 kfa[2][NS], vfa[NB], kfb[2][NS], vfb[NB];
+  // a block may be loaded before the transform unless it holds key p (whose
+  // K/V the transform stores), so its loads overlap the transform's
+  auto early_ok = [&](int64_t u0) { return !(a.qkv_part && holds_p) || u0 + 31 < p; };
   if constexpr (DIRECT) {
     // this wave's blocks: keys A + 32 (wave + NWV i), i < nbw
     const int64_t nblk = (p + 1 - A + 31) / 32;
     const int nbw = (int)((nblk - wave + NWV - 1) / NWV);
     auto ub0 = [&](int i) { return A + 32 * ((int64_t)wave + (int64_t)NWV * i); };
-    if (nbw > 0) load(ub0(0), kfa, vfa);
-    if (nbw > 1) load(ub0(1), kfb, vfb);
+    const bool e0 = nbw > 0 && early_ok(ub0(0)), e1 = nbw > 1 && early_ok(ub0(1));
+    if (e0) load(ub0(0), kfa, vfa);
+    if (e1) load(ub0(1), kfb, vfb);
+    prep();
+    if (nbw > 0 && !e0) load(ub0(0), kfa, vfa);
+    if (nbw > 1 && !e1) load(ub0(1), kfb, vfb);
     for (int i = 0; i < nbw; i += 2) {
       compute(ub0(i), kfa, vfa);
       if (i + 2 < nbw) load(ub0(i + 2), kfa, vfa);
@@ -695,8 +759,12 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
   } else {
     constexpr int NBLK = DEC_WKEYS / 32;
     static_assert(NBLK % 2 == 0, "blocks per wave come in pairs");
-    load(w0, kfa, vfa);
-    load(w0 + 32, kfb, vfb);
+    const bool e0 = early_ok(w0), e1 = early_ok(w0 + 32);
+    if (e0) load(w0, kfa, vfa);
+    if (e1) load(w0 + 32, kfb, vfb);
+    prep();
+    if (!e0) load(w0, kfa, vfa);
+    if (!e1) load(w0 + 32, kfb, vfb);
 #pragma unroll
     for (int blk = 0; blk < NBLK; blk += 2) {
       compute(w0 + 32 * blk, kfa, vfa);
@@ -737,7 +805,17 @@ attn_decode_kernel(AttnArgs a, int nsplit, float* part) {
     }
     if constexpr (DIRECT) {
       const int64_t zi = ((int64_t)b * a.n_q + g * GRP + h) * DH + d;
-      a.z[zi] = f2bf(O / L * bf2f(a.gate[zi]));
+      float gv;
+      if (a.qkv_part) {
+        const int64_t N = 2 * (int64_t)a.n_q * DH + 2 * (int64_t)a.n_kv * DH;
+        const float x = sum_splits(a.qkv_part + (int64_t)b * N + (int64_t)a.n_q * DH +
+                                       2 * (int64_t)a.n_kv * DH + (g * GRP + h) * DH + d,
+                                   a.qkv_nsplit, a.qkv_ss);
+        gv = bf2f(f2bf(1.0f / (1.0f + __expf(-x))));
+      } else {
+        gv = bf2f(a.gate[zi]);
+      }
+      a.z[zi] = f2bf(O / L * gv);
       continue;
     }
     float* dst = part + (((int64_t)b * a.n_q + g * GRP + h) * nsplit + split) * (DH + 2);
@@ -759,7 +837,8 @@ constexpr int COMB_NT = 1024;
 __global__ void __launch_bounds__(COMB_NT)
 attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, int dc,
                            const uint16_t* gate, uint16_t* z, RowLoops rl, int sk, int window,
-                           int64_t p0, const int64_t* p0_dev) {
+                           int64_t p0, const int64_t* p0_dev, const float* qkv_part, int qkv_nsplit,
+                           int64_t qkv_ss, int n_kv) {
   __shared__ float gm[COMB_NT / 32], gl[COMB_NT / 32];
   __shared__ float go[COMB_NT];
   const int nch = dh / dc;
@@ -819,7 +898,16 @@ attn_decode_combine_kernel(const float* part, int nsplit, int n_q, int dh, int d
     Lt += gl[j] * w;
     Ot += go[j * dc + dl] * w;
   }
-  z[idx] = f2bf(Ot / Lt * bf2f(gate[idx]));
+  float gv;
+  if (qkv_part) {  // sigma(gate) from the projection partials, rounded as stored
+    const int64_t N = 2 * (int64_t)n_q * dh + 2 * (int64_t)n_kv * dh;
+    const float x = sum_splits(qkv_part + (int64_t)b * N + (int64_t)n_q * dh + 2 * (int64_t)n_kv * dh +
+                                   h * dh + d, qkv_nsplit, qkv_ss);
+    gv = bf2f(f2bf(1.0f / (1.0f + __expf(-x))));
+  } else {
+    gv = bf2f(gate[idx]);
+  }
+  z[idx] = f2bf(Ot / Lt * gv);
 }
 
 template <int DH, int GRP>
@@ -864,7 +952,8 @@ hipError_t decode_cfg(const AttnArgs& a, int nsplit, float* part, hipStream_t st
   const int dc = nsplit > 64 ? 32 : DH;
   const int nt = nsplit <= 8 ? DH : COMB_NT;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q * (DH / dc)), dim3(nt), 0, st, part,
-                     nsplit, a.n_q, DH, dc, a.gate, a.z, a.rl, sk, a.window, a.p0, a.p0_dev);
+                     nsplit, a.n_q, DH, dc, a.gate, a.z, a.rl, sk, a.window, a.p0, a.p0_dev, a.qkv_part,
+                     a.qkv_nsplit, a.qkv_ss, a.n_kv);
   return hipGetLastError();
 }
 

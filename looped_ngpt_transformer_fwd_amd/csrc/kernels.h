@@ -222,6 +222,17 @@ struct AttnArgs {
                          // left as they are in prefill, zero in decode)
   const int64_t* p0_dev = nullptr;  // decode: position read from device memory
                                     // (replayed graphs), else p0
+  // decode with the query/key transform fused in (else q and gate are read
+  // from q / gate): split-K partials of the q/k/v/gate projection, row b =
+  // sequence b ([qkv_nsplit][B][2 dq + 2 dkv], split stride qkv_ss), the
+  // RoPE cos/sin of the step's position ([dh / 2] each) and s_qk. The
+  // workgroup holding key p also stores the token's k and v in the cache.
+  const float* qkv_part = nullptr;
+  int qkv_nsplit = 0;
+  int64_t qkv_ss = 0;
+  const float* cs = nullptr;
+  const float* sn = nullptr;
+  const float* s_qk = nullptr;
 };
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 

@@ -33,37 +33,6 @@ embed_kernel(const int32_t* tok, const uint16_t* E, int vocab, int d, float* h32
   }
 }
 
-// Sum of split-K partials p[s * ss], s < nsplit (<= 32), in split order;
-// the loads of up to 16 splits are all issued before the first add (the
-// partials come from another kernel: L2 or further away, so each round trip
-// is long against the arithmetic).
-__device__ __forceinline__ float4 sum_splits4(const float* p, int nsplit, int64_t ss) {
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < nsplit; s0 += 16) {
-    float4 t[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      t[j] = s0 + j < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + j) * ss) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      acc.x += t[j].x; acc.y += t[j].y; acc.z += t[j].z; acc.w += t[j].w;
-    }
-  }
-  return acc;
-}
-
-__device__ __forceinline__ float sum_splits(const float* p, int nsplit, int64_t ss) {
-  float acc = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += 16) {
-    float t[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) t[j] = s0 + j < nsplit ? p[(s0 + j) * ss] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc += t[j];
-  }
-  return acc;
-}
-
 // h <- N(h + alpha (N(y) - h)); optional aux copy of the result, optional
 // boundary h <- N(result + x). Y16: y is one bf16 matrix (the large-M
 // projections' output), else nsplit fp32 split-K partials. One workgroup

@@ -430,10 +430,23 @@ struct UpdateOpts {
 // last key up to the next multiple of 8 (the kernel reads whole 8-key
 // chunks); keys below f_origin come from the cache slot. Decode reads the
 // cache slot only: the token's K/V are stored there first.
+// Decode with the query/key transform fused into the attention (the
+// projection's split partials instead of q / gate).
+struct FusedQk {
+  const float* part = nullptr;
+  int nsplit = 0;
+  int64_t ss = 0;
+  const float *cs = nullptr, *sn = nullptr, *s_qk = nullptr;
+};
+
 dory_status attend(Ctx& c, const SlotPtr& sp, bool full, const uint16_t* q, const uint16_t* gate,
-                   uint16_t* z) {
+                   uint16_t* z, const FusedQk* fq = nullptr) {
   const Shape& s = c.s;
   AttnArgs aa{};
+  if (fq) {
+    aa.qkv_part = fq->part; aa.qkv_nsplit = fq->nsplit; aa.qkv_ss = fq->ss;
+    aa.cs = fq->cs; aa.sn = fq->sn; aa.s_qk = fq->s_qk;
+  }
   aa.q = q;
   aa.kc = sp.k; aa.vc = sp.v; aa.c_rows = sp.rows; aa.ring = sp.ring;
   aa.gate = gate; aa.z = z;
@@ -481,6 +494,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
   int ns = 1;
   dory_status st = DORY_OK;
   const int64_t f_origin = c.p0 / 8 * 8;
+  FusedQk fq;
   if (c.fused_qkv()) {
     // projections with RoPE / per-head norm / s_qk / K-V placement / gate in
     // the GEMM epilogue
@@ -499,18 +513,23 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                   DORY_K_GEMM_QKVG);
     if (st != DORY_OK) return st;
     const int64_t split_stride = c.M * s.nqkvg();
-    // decode: the current token's K/V go straight into the cache slot (the
-    // last-loop rule read literally: overwrite at every loop), then the
-    // attention reads the cache only; prefill: the step's K/V go to the
-    // fresh buffers
-    const QkDest kd = c.T == 1 ? QkDest{sp.k, sp.v, sp.rows, sp.rows, 0, sp.ring}
-                               : QkDest{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
-    PROF(c, DORY_K_QK);
-    HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh,
-                          c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
-                          c.gate(), c.st, c.T == 1 ? c.rl : RowLoops(), c.p0_dev));
+    if (c.T == 1) {
+      // decode: the attention kernel transforms q and k from the partials
+      // and stores the token's K/V straight into the cache slot (the
+      // last-loop rule read literally: overwrite at every loop) before it
+      // reads the cache
+      fq.part = c.P(); fq.nsplit = ns; fq.ss = split_stride;
+      fq.cs = c.rope_cs(full ? 1 : 0); fq.sn = c.rope_sn(full ? 1 : 0); fq.s_qk = w.s_qk;
+    } else {
+      // prefill: the step's K/V go to the fresh buffers
+      const QkDest kd{c.kf(), c.vf(), c.L.f_rows, c.L.f_rows, f_origin, 0};
+      PROF(c, DORY_K_QK);
+      HIPCHK(launch_qk_prep(c.P(), ns, split_stride, c.B, c.T, c.p0, s.nq, s.nkv, s.dh,
+                            c.rope_cs(full ? 1 : 0), c.rope_sn(full ? 1 : 0), w.s_qk, c.qh(), kd,
+                            c.gate(), c.st, RowLoops(), c.p0_dev));
+    }
   }
-  st = attend(c, sp, full, c.qh(), c.gate(), c.z());
+  st = attend(c, sp, full, c.qh(), c.gate(), c.z(), fq.part ? &fq : nullptr);
   if (st != DORY_OK) return st;
   if (c.T > 1 && write) {
     PROF(c, DORY_K_KV_WRITE);
