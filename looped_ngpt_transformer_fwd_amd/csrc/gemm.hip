@@ -589,15 +589,20 @@ gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 
-  // 4 DMA instructions per wave per step
+  // 2 + na DMA instructions per wave per step: the A blocks (8 rows each)
+  // past the last row are not loaded (with few rows, as in decode, the
+  // clamped rows would only repeat the last one); the MFMA rows they feed
+  // are never stored
+  const int mrows = g.M - m0;
+  const bool a0 = wave * 8 < mrows, a1 = (wave + 4) * 8 < mrows;
   auto issue = [&](int ks, uint8_t* sa, uint8_t* sb) {
     const uint32_t ko = (uint32_t)ks * (BK * 2);
+    if (a0) dma16(ra, aoff[0], ko, sa + wave * 1024);
+    if (a1) dma16(ra, aoff[1], ko, sa + (wave + 4) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      dma16(ra, aoff[i], ko, sa + (wave + 4 * i) * 1024);
-      dma16(rb, boff[i], ko, sb + (wave + 4 * i) * 1024);
-    }
+    for (int i = 0; i < 2; ++i) dma16(rb, boff[i], ko, sb + (wave + 4 * i) * 1024);
   };
+  const int na = (a0 ? 1 : 0) + (a1 ? 1 : 0);
   auto compute = [&](const uint8_t* sa0, const uint8_t* sb0) {
     const uint8_t* sa = sa0 + wm * 32 * 128;
     const uint8_t* sb = sb0 + wn * 32 * 128;
@@ -614,10 +619,13 @@ gemm_skinny_kernel(GemmArgs g) {
     issue(ks0 + min(2, n - 1), sA2, sB2);
     // the ring runs a multiple of 4 steps; steps past n only keep the wait
     // and load pattern uniform (no branch around the DMA) and compute nothing
-    auto step = [&](int i, const uint8_t* ca, const uint8_t* cb, uint8_t* na, uint8_t* nb) {
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): steps i + 1, i + 2 stay in flight
+    auto step = [&](int i, const uint8_t* ca, const uint8_t* cb, uint8_t* sna, uint8_t* snb) {
+      // steps i + 1, i + 2 stay in flight: vmcnt(2 (2 + na))
+      if (na == 2) __builtin_amdgcn_s_waitcnt(0x0F78);
+      else if (na == 1) __builtin_amdgcn_s_waitcnt(0x0F76);
+      else __builtin_amdgcn_s_waitcnt(0x0F74);
       barrier_lds();                        // all parts of step i landed; stage (i + 3) % 4 is free
-      issue(ks0 + min(i + 3, n - 1), na, nb);
+      issue(ks0 + min(i + 3, n - 1), sna, snb);
       if (i < n) compute(ca, cb);
     };
     for (int i = 0; i < n; i += 4) {
