@@ -7,11 +7,11 @@
 // K-contiguous), B the weight in [out, in] layout (also K-contiguous), so
 // both operand tiles are loaded along K with 16-byte vector loads.
 //
-// Two bf16 kernels cover every row count: the large-M kernel (M >= 1024,
-// prefill; 256 x 256 tiles on four DMA-fed LDS stages, fused epilogues) and
-// the skinny kernel (M < 1024: decode, the LM head, verification chunks and
-// short prefills; 64 x 64 tiles, split-K, weight streaming), plus the skinny
-// kernel's MXFP8-weight variant (M <= 64).
+// Three bf16 kernels cover every row count: the large-M kernel (M >= 1024,
+// prefill; 256 x 256 tiles on four DMA-fed LDS stages, fused epilogues), the
+// skinny kernel (64 < M < 1024: verification chunks and short prefills;
+// 64 x 64 tiles, split-K) and its wide form for decode (M <= 64: 64 x 128
+// tiles, split-K, weight streaming), plus an MXFP8-weight variant (M <= 64).
 #include "common.h"
 #include "kernels.h"
 
@@ -788,7 +788,122 @@ gemm_skinny_fp8_kernel(GemmArgs g) {
   }
 }
 
+// Up to 64 rows (decode): 64 x 128 output tiles, 8 waves of 32 x 32 (2 row x
+// 4 column), K in steps of 64 through four LDS stages (A 8 KB + B 16 KB:
+// one workgroup of 8 waves per CU). The activation tile, which every
+// column tile reads again, is half the DMA of a 64 x 64 tile; here a third.
+template <int EPI>
+__global__ void __launch_bounds__(512)
+gemm_skinny_wide_kernel(GemmArgs g) {
+  constexpr int SA = 64 * 128, SBW = 128 * 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[SBW];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[SBW];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[SBW];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA3[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB3[SBW];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tile = blockIdx.x, split = blockIdx.z;
+  const int n0 = tile * 128;
+  const int ksteps = g.K / BK;
+  const int per = (ksteps + g.nsplit - 1) / g.nsplit;
+  const int ks0 = split * per;
+  const int n = max(0, min(ksteps, ks0 + per) - ks0);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)(g.N - 1) * g.ldb * 2 + g.K * 2));
+  const int lr = lane >> 3;
+  // DMA: A block `wave` (rows 8 wave ..), B blocks wave and wave + 8
+  const int ra_row = wave * 8 + lr;
+  const uint32_t aoff = (uint32_t)((int64_t)min(ra_row, g.M - 1) * g.lda * 2 +
+                                   (((lane & 7) ^ ((ra_row >> 1) & 7)) << 4));
+  uint32_t boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave + 8 * i) * 8 + lr;
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);
+    boff[i] = (uint32_t)((int64_t)min(n0 + r, g.N - 1) * g.ldb * 2 + lc * 16);
+  }
+  const int fr = lane & 31, fh = lane >> 5;
+  int loff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = fr * 128 + (((2 * kk + fh) ^ ((fr >> 1) & 7)) << 4);
+
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+  // A blocks past the last row are not loaded (their MFMA rows are never
+  // stored): 2 or 3 DMA per wave per step
+  const bool has_a = wave * 8 < g.M;
+  auto issue = [&](int ks, uint8_t* sa, uint8_t* sb) {
+    const uint32_t ko = (uint32_t)ks * (BK * 2);
+    if (has_a) dma16(ra, aoff, ko, sa + wave * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(rb, boff[i], ko, sb + (wave + 8 * i) * 1024);
+  };
+  auto compute = [&](const uint8_t* sa0, const uint8_t* sb0) {
+    const uint8_t* sa = sa0 + wm * 32 * 128;
+    const uint8_t* sb = sb0 + wn * 32 * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(sa + loff[kk]);
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(sb + loff[kk]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+    }
+  };
+  if (n > 0) {
+    issue(ks0, sA0, sB0);
+    issue(ks0 + min(1, n - 1), sA1, sB1);
+    issue(ks0 + min(2, n - 1), sA2, sB2);
+    auto step = [&](int i, const uint8_t* ca, const uint8_t* cb, uint8_t* sna, uint8_t* snb) {
+      // steps i + 1, i + 2 stay in flight
+      if (has_a) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);        // vmcnt(4)
+      barrier_lds();
+      issue(ks0 + min(i + 3, n - 1), sna, snb);
+      if (i < n) compute(ca, cb);
+    };
+    for (int i = 0; i < n; i += 4) {
+      step(i, sA0, sB0, sA3, sB3);
+      step(i + 1, sA1, sB1, sA0, sB0);
+      step(i + 2, sA2, sB2, sA1, sB1);
+      step(i + 3, sA3, sB3, sA2, sB2);
+    }
+    wait_vm0();
+  }
+
+  const int col = n0 + wn * 32 + (lane & 31);
+  if (col < g.N) {
+    const float sc = (EPI == EPI_LOGITS) ? g.s1[col] : 1.f;
+    float* C = g.C + (int64_t)split * g.split_stride;
+    const int rbase = wm * 32 + (lane >> 5) * 4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = rbase + (e >> 2) * 8 + (e & 3);
+      if (row < g.M) C[(int64_t)row * g.ldc + col] = acc[e] * sc;
+    }
+  }
+}
+
+
 hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t st) {
+  if (a.M <= 64) {
+    // the same split as 64-column tiles gives (N a multiple of 128: tiles x
+    // split <= 256, one workgroup per CU)
+    dim3 gw((a.N + 127) / 128, 1, a.nsplit);
+    switch (epi) {
+      case EPI_F32: hipLaunchKernelGGL((gemm_skinny_wide_kernel<EPI_F32>), gw, dim3(512), 0, st, a); break;
+      case EPI_LOGITS: hipLaunchKernelGGL((gemm_skinny_wide_kernel<EPI_LOGITS>), gw, dim3(512), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((a.N + 63) / 64, 1, a.nsplit), block(256);
   if (a.M > 64) {
     // 1-D grid: 8 pairs per round, every row block of each
