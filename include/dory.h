@@ -329,7 +329,8 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
  * cumulative weight exceeds u[r] times the row total, the weights being
  * softmax(logits[r] / temperature) (logits: device fp32 [rows][V], u:
  * device fp32 [rows] in [0, 1)); a token of zero probability is never
- * chosen. temperature > 0. Asynchronous on `stream`. */
+ * chosen (a row needs one finite logit; a row without gives token 0).
+ * temperature > 0. Asynchronous on `stream`. */
 dory_status dory_sample(const float* logits, int32_t rows, int32_t V, float temperature,
                         const float* u, int32_t* out, void* stream);
 
@@ -345,7 +346,10 @@ dory_status dory_sample(const float* logits, int32_t rows, int32_t V, float temp
  * p_gamma. Device buffers: draft_logits fp32 [gamma][B][V], verify_logits
  * fp32 [gamma + 1][B][V], drafts int32 [gamma][B], u fp32 [gamma + 1][B];
  * outputs n_accepted int32 [B] and out int32 [gamma + 1][B] (the accepted
- * drafts, then the next token, then -1). 1 <= gamma <= 1000. */
+ * drafts, then the next token, then -1). 1 <= gamma <= 1000. A rejection
+ * whose residual has no mass in fp32 (p and q agree up to rounding; in
+ * exact arithmetic a rejection implies positive residual mass) samples
+ * from p_j instead. */
 dory_status dory_speculative_accept(const float* draft_logits, const float* verify_logits,
                                     const int32_t* drafts, const float* u, int32_t B, int32_t V,
                                     int32_t gamma, float temperature, int32_t* n_accepted,

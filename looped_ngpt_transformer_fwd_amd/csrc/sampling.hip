@@ -62,7 +62,7 @@ __device__ __forceinline__ float block_scan_1024(float v, float* red, float* lo,
 // Inversion over the weights w(i) of one row (a functor of the index): the
 // smallest i whose cumulative weight exceeds u * total. A target at or past
 // the end of the claimed ranges (rounding) takes the last index of nonzero
-// weight.
+// weight; a row without positive weight gives -1.
 template <class Wt>
 __device__ __forceinline__ int invert_row(const Wt& weight, int V, float u, float* red,
                                           int* pick) {
@@ -92,7 +92,9 @@ __device__ __forceinline__ int invert_row(const Wt& weight, int V, float u, floa
   __syncthreads();
   if (*pick < 0 && last_nz >= 0) atomicMax(pick, last_nz);
   __syncthreads();
-  return *pick < 0 ? 0 : *pick;
+  const int r = *pick;
+  __syncthreads();  // *pick may be reused by the caller
+  return r;
 }
 
 // max and normalizer of softmax(row / T)
@@ -119,7 +121,7 @@ sample_kernel(const float* logits, int V, float temperature, const float* u, int
   m = block_max_1024(m, red);
   auto w = [&](int i) { return expf((row[i] - m) * it); };
   const int r = invert_row(w, V, u[blockIdx.x], red, &pick);
-  if (threadIdx.x == 0) out[blockIdx.x] = r;
+  if (threadIdx.x == 0) out[blockIdx.x] = max(r, 0);  // (no finite logit: token 0)
 }
 
 // One workgroup per sequence b. draft_logits [gamma][B][V], verify_logits
@@ -154,13 +156,19 @@ spec_accept_kernel(const float* draft_logits, const float* verify_logits, const 
       return fmaxf(expf((prow[i] - mp) * it) / zp - expf((qrow[i] - mq) * it) / zq, 0.f);
     };
     nxt = invert_row(w, V, u[(int64_t)gamma * B + b], red, &pick);
+    if (nxt < 0) {
+      // no residual mass (p <= q everywhere in fp32, so p and q agree up to
+      // rounding): the verifier's own distribution
+      auto wp = [&](int i) { return expf((prow[i] - mp) * it); };
+      nxt = max(invert_row(wp, V, u[(int64_t)gamma * B + b], red, &pick), 0);
+    }
   } else {
     const float* prow = verify_logits + ((int64_t)gamma * B + b) * V;
     float m = -INFINITY;
     for (int i = threadIdx.x; i < V; i += NT_S) m = fmaxf(m, prow[i]);
     m = block_max_1024(m, red);
     auto w = [&](int i) { return expf((prow[i] - m) * it); };
-    nxt = invert_row(w, V, u[(int64_t)gamma * B + b], red, &pick);
+    nxt = max(invert_row(w, V, u[(int64_t)gamma * B + b], red, &pick), 0);
   }
   if (threadIdx.x <= gamma) {
     const int r = threadIdx.x;

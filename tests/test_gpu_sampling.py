@@ -87,6 +87,10 @@ def test_sample_never_picks_zero_probability(M):
     got1 = M.sample(torch.from_numpy(one).cuda(), 0.5,
                     torch.tensor([0.0, 0.5, 0.999, 0.3], device="cuda")).cpu().numpy()
     np.testing.assert_array_equal(got1, [0, 5, V - 1, 1234])
+    # a row without a finite logit has no distribution: token 0 (documented)
+    none = np.full((2, V), -np.inf, dtype=np.float32)
+    got2 = M.sample(torch.from_numpy(none).cuda(), 1.0, torch.tensor([0.0, 0.7], device="cuda")).cpu().numpy()
+    np.testing.assert_array_equal(got2, [0, 0])
 
 
 def _spec_inputs(rng, gamma, B, V, spread):
