@@ -344,6 +344,55 @@ def long_context(gm, shape, k=4, total=262144, chunk=8192, n_dec=128):
                       f"then {n_dec} greedy decode steps"}
 
 
+def pair_kernels(M, steps=3):
+    """One recurrent pair at full width ([SWA attention, MLP, full attention,
+    MLP], no input / output blocks, no LM head), B=1 x T=4096 prefill at
+    k = 1..4, last-loop cache: tokens/s and per-kernel-class time and rate
+    (the kernel classes without the rest of the model)."""
+    shape = synth.PAIR
+    kinds = M.schedule(shape)
+    gp = M.Model(shape, gpu_weights(shape, kinds, seed=5))
+    B, T = 1, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    toks = torch.randint(0, shape.vocab, (B, T), dtype=torch.int32, device="cuda", generator=g)
+    ws = gp.workspace(B, T)
+    work = class_work(shape, B * T)
+    out = {}
+    for k in (1, 2, 3, 4):
+        kv = gp.kv_cache("last_loop", k, B, T)
+
+        def one():
+            kv.reset()
+            gp.prefill(kv, toks, k, ws=ws, logits=False, next_token=False)
+        one()
+        torch.cuda.synchronize()
+        gp.profile_begin(max_launches=64 * k * steps + 64)
+        dt = time_steps(one, steps)
+        prof = gp.profile_end()
+        attn_flop = attention_flops(shape, kinds, B, T, k)
+        kern = {}
+        for cls, (n, ms) in prof.items():
+            if n == 0:
+                continue
+            e = {"launches": n, "ms_avg": round(ms / n, 4)}
+            if cls in work:
+                amt, unit, bound = work[cls]
+                e["rate"] = round(amt / (ms / n * 1e-3) / (1e12 if unit == "flop" else 1e9), 1)
+                e["rate_unit"] = "TFLOP/s" if unit == "flop" else "GB/s"
+            if cls == "attn":
+                e["rate"] = round(attn_flop * steps / (ms * 1e-3) / 1e12, 1)
+                e["rate_unit"] = "TFLOP/s"
+            kern[cls] = e
+        out[f"k{k}"] = {"tok_s": round(B * T * steps / dt, 1), "ms_per_step": round(dt / steps * 1e3, 3),
+                        "kernels": kern}
+        del kv
+    del gp, ws
+    torch.cuda.empty_cache()
+    out["config"] = "recurrent pair [SWA, MLP, full, MLP] at d=2304, B=1 x T=4096, last_loop, k=1..4"
+    return out
+
+
 def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -451,6 +500,24 @@ def cpu_baseline(k, n_tokens=512, slices=True):
         return out
     sl = {}
     progress(f"oracle prefill sample: {n_tokens / dt:.2f} tokens/s")
+    # the recurrent pair (C2 shape) over its first 512 tokens
+    kp = ref.layer_kinds(synth.PAIR)
+    Wp = synth.Weights(synth.PAIR, kp, 5)
+    wcache = {"embed": _RowGather(Wp.raw("embed"))}
+
+    def wpair(name):
+        if name not in wcache:
+            wcache[name] = Wp.f64(name)
+        return wcache[name]
+    op = ref.OracleModel(synth.PAIR, wpair)
+    tp = synth.tokens(5, 1, 512, synth.PAIR.vocab)
+    for kk in (1, 4):
+        t0 = time.perf_counter()
+        op.step(ref.Cache(synth.PAIR, ref.MODE_LAST, 1), tp, kk, logits=None)
+        d = time.perf_counter() - t0
+        sl[f"pair_t512_k{kk}"] = {"tokens_s": round(512 / d, 2), "s": round(d, 2),
+                                  "sample": "recurrent pair at d=2304, B=1, tokens 0..511 (of 4096), one prefill step"}
+    del op, Wp, wcache
     ctx = 32768
     cache = _oracle_context(ctx, ctx + 1, seed=11)
     tok = synth.tokens(1, 1, 1, sh.vocab)
@@ -600,6 +667,8 @@ def main():
         result["selfspec_b8_ctx4096"] = decode_selfspec(gm, shape, B=8, ctx=4096)
         progress("self-speculative rounds done")
         result["prefix_copy"] = prefix_copy(gm, shape)
+        result["pair_c2"] = pair_kernels(M)
+        progress("recurrent pair done")
         result["long_context"] = long_context(gm, shape)
         progress("long context done")
         result["decode_config"] = ("B=64, 32768 cached tokens (K/V synthesized), then 256 greedy "
