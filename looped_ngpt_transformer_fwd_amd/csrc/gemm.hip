@@ -22,7 +22,9 @@ namespace {
 constexpr int BK = 64;
 
 // ---------------------------------------------------------------------------
-// Large-M kernel: 256 x 256 output tiles, 8 waves (4 x 2, each 64 x 128), K
+// Large-M kernel: 256 x 256 output tiles (256 x 288 for bf16 outputs 2,304
+// wide: 8 column tiles fill whole rounds of 256 CUs where 9 leave the last
+// round half empty), 8 waves (4 x 2, each 64 x 128 or 64 x 144), K
 // in steps of 32 through four LDS stages filled by direct global->LDS DMA
 // (buffer_load ... lds, 16 bytes per lane), so no VGPRs stage the operands
 // and the loads of step k+3 are in flight while step k computes: a distance
@@ -120,28 +122,34 @@ __device__ __forceinline__ void wait_vm8() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int EPI, int WAVES_M, int WAVES_N>
+template <int EPI, int WAVES_M, int WAVES_N, int BN = BIG_BN>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
 gemm_big_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int BIG_WM = BIG_BM / WAVES_M, BIG_WN = BIG_BN / WAVES_N;
+  constexpr int BIG_WM = BIG_BM / WAVES_M, BIG_WN = BN / WAVES_N;
   constexpr int FM = BIG_WM / 16, FN = BIG_WN / 16;
-  constexpr int BPW = 16 / NW;               // DMA blocks per wave per operand
-  constexpr int DMA_PER_STEP = 2 * BPW;      // DMA instructions per wave per step
-  static_assert(BIG_WN == 128, "epilogues assume 128 columns per wave");
-  static_assert(DMA_PER_STEP == 4 || DMA_PER_STEP == 8, "wait counts below");
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BIG_OP_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BIG_OP_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * BIG_OP_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[2 * BIG_OP_BYTES];
+  constexpr int BPW = 16 / NW;               // A DMA blocks per wave (B: BN / 16 blocks in all)
+  constexpr int NBB = BN / 16;               // B DMA blocks of a stage
+  constexpr int BPWB = (NBB + NW - 1) / NW;  // B DMA blocks per wave, at most
+  static_assert(BIG_WN == 128 || (BN == 288 && EPI == EPI_BF16 && NW == 8),
+                "epilogues assume 128 columns per wave; 288-column tiles have the bf16 one only");
+  static_assert(NW == 8 || BN == BIG_BN, "one wave per SIMD: 256 columns");
+  // A stage holds the A tile (16 KiB) and the B tile (BN x 64 B); a 288-wide
+  // stage is padded so that the four hold the bf16 epilogue's staging
+  // (8 waves x 64 rows x 304 B)
+  constexpr int STAGE = BN == BIG_BN ? 2 * BIG_OP_BYTES : 38912;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int ntm = (g.M + BIG_BM - 1) / BIG_BM, ntn = (g.N + BIG_BN - 1) / BIG_BN;
+  const int ntm = (g.M + BIG_BM - 1) / BIG_BM, ntn = (g.N + BN - 1) / BN;
   int tm, tn;
   big_tile_coords(blockIdx.x, ntm, ntn, g.order & 0xFF, (g.order >> 8) & 1, &tm, &tn);
-  const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
+  const int m0 = tm * BIG_BM, n0 = tn * BN;
   const int ksteps = g.K / BIG_BK;           // even: K is a multiple of 64
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)(g.M - 1) * g.lda * 2 + g.K * 2));
@@ -151,11 +159,15 @@ gemm_big_kernel(GemmArgs g) {
   // DMA sources: wave w fills blocks w, w + NW of each operand tile
   const int lr = lane >> 2;                  // row within the block
   const int lc = (lane & 3) ^ ((lr >> 1) & 3);  // logical chunk (block rows are 16-aligned)
-  uint32_t aoff[BPW], boff[BPW];
+  uint32_t aoff[BPW], boff[BPWB];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int r = (wave + NW * i) * 16 + lr;
     aoff[i] = (uint32_t)((int64_t)min(m0 + r, g.M - 1) * g.lda * 2 + lc * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BPWB; ++i) {
+    const int r = (wave + NW * i) * 16 + lr;  // (rows past the tile: never loaded)
     int v = min(n0 + r, g.N - 1);
     int row = v;
     if (EPI == EPI_SWIGLU) {
@@ -178,6 +190,9 @@ gemm_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
+  // the B blocks of a 288-wide tile do not divide by the waves: waves
+  // 0 .. NBB % NW - 1 load one more, and wait for two more per step
+  const bool extra_b = NBB % NW != 0 && wave < NBB % NW;
   auto issue = [&](int ks, uint8_t* stg) {
     const uint32_t ko = (uint32_t)ks * (BIG_BK * 2);
 #pragma unroll
@@ -185,6 +200,14 @@ gemm_big_kernel(GemmArgs g) {
       dma16(ra, aoff[i], ko, stg + (wave + NW * i) * 1024);
       dma16(rb, boff[i], ko, stg + BIG_OP_BYTES + (wave + NW * i) * 1024);
     }
+    if (BPWB > BPW && extra_b) dma16(rb, boff[BPWB - 1], ko, stg + BIG_OP_BYTES + (wave + NW * BPW) * 1024);
+  };
+  // two younger steps stay in flight
+  auto wait_two = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    if (BPWB > BPW && extra_b) __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+    else __builtin_amdgcn_s_waitcnt(0x0F78);                        // vmcnt(8)
+    __builtin_amdgcn_sched_barrier(0);
   };
   bf16x8 af[FM], bfr[FN];
   if constexpr (NW == 8) {
@@ -210,12 +233,12 @@ gemm_big_kernel(GemmArgs g) {
     issue(0, st0);
     issue(1, st1);
     issue(min(2, ksteps - 1), st2);
-    wait_vm8();
+    wait_two();
     pp_barrier();
     if (wave < NW / 2) {
   #define DORY_PP_A(KS, CUR, NXT)                                             \
       mem(KS, CUR, NXT); pp_barrier();                                        \
-      big_mfma(af, bfr, acc); wait_vm8(); pp_barrier();
+      big_mfma(af, bfr, acc); wait_two(); pp_barrier();
       int ks = 0;
       for (; ks + 4 <= ksteps; ks += 4) {
         DORY_PP_A(ks, st0, st3)
@@ -231,7 +254,7 @@ gemm_big_kernel(GemmArgs g) {
       pp_barrier();
     } else {
   #define DORY_PP_B(KS, CUR, NXT)                                             \
-      mem(KS, CUR, NXT); wait_vm8(); pp_barrier();                            \
+      mem(KS, CUR, NXT); wait_two(); pp_barrier();                            \
       big_mfma(af, bfr, acc); pp_barrier();
       pp_barrier();
       int ks = 0;
@@ -386,8 +409,19 @@ gemm_big_kernel(GemmArgs g) {
     // per wave, 16-byte chunks XOR-swizzled by row) and leave as 16-byte
     // pieces of 256-byte rows.
     __syncthreads();  // every wave is done with the stages
-    uint8_t* stg = (wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3;
-    stg += (wave & 1) * 16384;
+    // staging rows: 256 B (16 chunks, XOR-swizzled) for 128 columns; 288 B
+    // plus 16 B of padding for 144 columns
+    constexpr int NCH = BIG_WN / 8;
+    constexpr int SROWB = NCH == 16 ? 256 : NCH * 16 + 16;
+    constexpr int WSTG = 64 * SROWB;
+    uint8_t* stg;
+    if constexpr (NCH == 16) {
+      stg = ((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * 16384;
+    } else {
+      // waves 0-1 in st0, 2-3 in st1, ...: 2 x 19,456 B of each 38,912 B stage
+      stg = ((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * WSTG;
+    }
+    auto soff = [&](int r, int c) { return NCH == 16 ? r * 256 + ((c ^ (r & 15)) << 4) : r * SROWB + c * 16; };
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -396,8 +430,7 @@ gemm_big_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = j * 16 + (lane & 15);
-          *reinterpret_cast<uint16_t*>(stg + r * 256 + (((col >> 3) ^ (r & 15)) << 4) + (col & 7) * 2) =
-              f2bf(acc[i][j][e]);
+          *reinterpret_cast<uint16_t*>(stg + soff(r, col >> 3) + (col & 7) * 2) = f2bf(acc[i][j][e]);
         }
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
@@ -405,10 +438,11 @@ gemm_big_kernel(GemmArgs g) {
     const int c0 = n0 + wn * BIG_WN;
     const bool vec_ok = g.ldc16 % 8 == 0 && (reinterpret_cast<uintptr_t>(g.C16) & 15) == 0;
 #pragma unroll
-    for (int pass = 0; pass < 16; ++pass) {
-      const int r = pass * 4 + (lane >> 4), c = lane & 15;
+    for (int pass = 0; pass < 64 * NCH / 64; ++pass) {
+      const int q = pass * 64 + lane;
+      const int r = NCH == 16 ? pass * 4 + (lane >> 4) : q / NCH, c = NCH == 16 ? lane & 15 : q % NCH;
       const int row = m0 + wm * BIG_WM + r;
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + soff(r, c));
       uint16_t* dst = g.C16 + (int64_t)row * g.ldc16 + c0 + c * 8;
       if (row < g.M) {
         if (vec_ok && c0 + c * 8 + 8 <= g.N) {
@@ -503,6 +537,16 @@ int big_order(int N, int K) {
 
 hipError_t launch_big(const GemmArgs& a0, int epi, hipStream_t st) {
   GemmArgs a = a0;
+  if (epi == EPI_BF16 && a.N % 288 == 0 && (a.N / 288) % 8 == 0 &&
+      !(a.N % BIG_BN == 0 && (a.N / BIG_BN) % 8 == 0)) {
+    // e.g. N = 2,304: 8 columns of 288-wide tiles fill whole rounds (256
+    // CUs) where 9 of 256 leave the last round half empty
+    a.order = big_order(a.N, a.K);
+    const int tiles = ((a.M + BIG_BM - 1) / BIG_BM) * (a.N / 288);
+    hipLaunchKernelGGL((gemm_big_kernel<EPI_BF16, BIG_WAVES_M, BIG_WAVES_N, 288>), dim3(tiles),
+                       dim3(64 * BIG_WAVES_M * BIG_WAVES_N), 0, st, a);
+    return hipGetLastError();
+  }
   a.order = big_order(a.N, a.K);
   const int tiles = ((a.M + BIG_BM - 1) / BIG_BM) * ((a.N + BIG_BN - 1) / BIG_BN);
   dim3 grid(tiles), block(64 * BIG_WAVES_M * BIG_WAVES_N);
