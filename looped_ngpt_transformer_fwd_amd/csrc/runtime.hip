@@ -1352,6 +1352,7 @@ dory_status dory_selfspec_step(dory_model* m, dory_kv* kv, const int32_t* last, 
   if (hipMemcpyAsync(drafts.data(), scratch, drafts.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipMemcpyAsync(greedy.data(), out, greedy.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
+    dory_kv_set_length(kv, L0);
     kv->invalid = true;
     return fail(DORY_ERR_HIP, "copy of the drafted and verified tokens failed");
   }
@@ -1453,12 +1454,14 @@ dory_status dory_selfspec_step_sampled(dory_model* m, dory_kv* kv, const int32_t
   int32_t* n_dev = bt;  // the verification input is consumed
   if (launch_spec_accept(logits_buf, logits_buf + (int64_t)gamma * BV, scratch + B, u + (int64_t)gamma * B,
                          B, V, gamma, temperature, n_dev, out, st) != hipSuccess) {
+    dory_kv_set_length(kv, L0);
     kv->invalid = true;
     return fail(DORY_ERR_HIP, "acceptance launch failed");
   }
   std::vector<int32_t> nb(B);
   if (hipMemcpyAsync(nb.data(), n_dev, (size_t)B * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
+    dory_kv_set_length(kv, L0);
     kv->invalid = true;
     return fail(DORY_ERR_HIP, "copy of the accepted counts failed");
   }
