@@ -124,7 +124,7 @@ attn_prefill_kernel(AttnArgs a) {
   const int tq = t0 + (lane & 31);
   const int hl = lane >> 5;
   const int64_t bg = (int64_t)b * a.n_kv + g;
-  const int64_t pq = a.p0 + tq;
+  const int pq = (int)a.p0 + tq;  // positions fit 31 bits (at most 2^24)
 
   bf16x8 qf[DH / 16];
   {
@@ -146,7 +146,6 @@ attn_prefill_kernel(AttnArgs a) {
   const int tw0 = qt * BQ;
   const int tw1 = min(C, tw0 + BQ) - 1;
   const int64_t p_lo = a.p0 + tw0, p_hi = a.p0 + tw1;
-  const int64_t k_end = a.p0 + C;
   int64_t k_lo = 0;
   if (a.window > 0) k_lo = max((int64_t)0, p_lo - a.window + 1);
   const int64_t kt_first = (k_lo / BN) * BN;
@@ -154,7 +153,7 @@ attn_prefill_kernel(AttnArgs a) {
 
   // per-wave query extent
   const bool wave_live = t0 < C;
-  const int64_t wq_lo = a.p0 + t0, wq_hi = a.p0 + min(t0 + 31, C - 1);
+  const int wq_lo = (int)a.p0 + t0, wq_hi = (int)a.p0 + min(t0 + 31, C - 1);
 
   // Fragment read offsets (lane parts). Row r of the S^T product's A operand
   // is key row perm(r) of the K tile, perm swapping bits 2 and 3 of r: in the
@@ -182,12 +181,15 @@ attn_prefill_kernel(AttnArgs a) {
 
   // Source rows are chosen with selects, not branches: a branch between the
   // DMA and the LDS reads makes the compiler drain the DMA in flight before
-  // the reads. A lane's row (K) or 8-key column group (V) within a tile is
-  // the same in every tile, so its remainder modulo the ring is taken once;
-  // per tile only the (uniform) remainder of the tile start is added, with
-  // one conditional subtraction. Positions fit 31 bits (checked on the
-  // host: at most 2^24); a layer without a ring uses a divisor above every
-  // position.
+  // the reads. Positions, rows and element offsets fit 31 bits (positions
+  // are checked on the host: at most 2^24), so the per-lane arithmetic is
+  // 32-bit: a key at offset rel + r from the fresh buffer's origin (rel the
+  // uniform tile start minus f_origin) is a cache row when that is negative,
+  // else a fresh row. A lane's row (K) or 8-key column group (V) within a
+  // tile is the same in every tile, so its remainder modulo the ring is taken
+  // once; per tile only the (uniform) remainder of the tile start is added,
+  // with one conditional subtraction. A layer without a ring uses a divisor
+  // above every position.
   const uint32_t ring_div = a.ring > 0 ? (uint32_t)a.ring : 0x7FFFFFFFu;
   // the four base pointers as uniform values (a select between two fields of
   // the argument block would become a per-lane load of the selected field)
@@ -195,6 +197,13 @@ attn_prefill_kernel(AttnArgs a) {
   const uint16_t* const kfb = uniform_ptr(a.kf + bg * a.f_rows * DH);
   const uint16_t* const vcb = uniform_ptr(a.vc + bg * DH * a.c_rows);
   const uint16_t* const vfb = uniform_ptr(a.vf + bg * DH * a.f_rows);
+  const int f_org = (int)a.f_origin;
+  const int k_last = (int)a.f_rows - 1;
+  // V^T columns from the last 8-key group holding step keys or zeros on:
+  // groups at or past the step's end read that group instead (finite values
+  // that meet probabilities of exactly 0)
+  const int v_last = (int)((a.p0 + C - a.f_origin + 7) / 8 * 8) - 8;
+  const int kt_first32 = (int)kt_first;
   constexpr int KJ = (K_BLOCKS + PF_WAVES - 1) / PF_WAVES;
   constexpr int VJ = (V_BLOCKS + PF_WAVES - 1) / PF_WAVES;
   uint32_t k_rm[KJ], v_cm[VJ];
@@ -205,8 +214,10 @@ attn_prefill_kernel(AttnArgs a) {
     const int d = (wave + j * PF_WAVES) * 8 + (lane >> 3);
     v_cm[j] = (uint32_t)(((lane & 7) ^ ((d >> 1) & 7)) * 8) % ring_div;
   }
+  const uint32_t c_rows32 = (uint32_t)a.c_rows, f_rows32 = (uint32_t)a.f_rows;
   auto issue_k = [&](int it, uint8_t* kst) __attribute__((always_inline)) {
-    const int64_t kt = kt_first + (int64_t)min(it, ntiles - 1) * BN;
+    const int kt = kt_first32 + min(it, ntiles - 1) * BN;
+    const int rel = kt - f_org;
     const uint32_t km = (uint32_t)kt % ring_div;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
@@ -214,18 +225,17 @@ attn_prefill_kernel(AttnArgs a) {
       if (K_BLOCKS % PF_WAVES != 0 && blk >= K_BLOCKS) break;
       const int r = blk * KRPB + lane / KCH;
       const int c = (lane % KCH) ^ kswz<DH>(r);
-      const int64_t u = kt + r;
+      const int ur = rel + r;
       uint32_t ci = km + k_rm[j];
-      ci = ci >= ring_div ? ci - ring_div : ci;
-      const bool in_cache = u < a.f_origin;
-      // per-lane parts in 32 bits (rows * DH stay below 2^31)
-      const uint32_t fr = (uint32_t)min(u - a.f_origin, a.f_rows - 1);
-      const uint32_t off = (in_cache ? ci : fr) * DH + c * 8;
-      dma16_flat((in_cache ? kcb : kfb) + off, kst + blk * 1024);
+      ci = min(ci, ci - ring_div);
+      const bool in_cache = ur < 0;
+      const uint32_t row = in_cache ? ci : (uint32_t)min(ur, k_last);
+      dma16_flat((in_cache ? kcb : kfb) + (row * DH + c * 8), kst + blk * 1024);
     }
   };
   auto issue_v = [&](int it, uint8_t* vst) __attribute__((always_inline)) {
-    const int64_t kt = kt_first + (int64_t)min(it, ntiles - 1) * BN;
+    const int kt = kt_first32 + min(it, ntiles - 1) * BN;
+    const int rel = kt - f_org;
     const uint32_t km = (uint32_t)kt % ring_div;
 #pragma unroll
     for (int j = 0; j < VJ; ++j) {
@@ -233,19 +243,16 @@ attn_prefill_kernel(AttnArgs a) {
       if (V_BLOCKS % PF_WAVES != 0 && blk >= V_BLOCKS) break;
       const int d = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((d >> 1) & 7);
-      // chunks at or past the last key load the row's first chunk instead:
-      // finite values that meet probabilities of exactly 0 (the loads stay
-      // unconditional so every wave issues a fixed number per tile)
-      const int64_t u = kt + c * 8;
+      const int ur = rel + c * 8;
       uint32_t ci = km + v_cm[j];
-      ci = ci >= ring_div ? ci - ring_div : ci;
-      // every candidate offset is computed, then selected (no branch);
-      // per-lane parts in 32 bits (DH * rows stays below 2^31)
-      const bool past = u >= k_end, in_cache = u < a.f_origin;
-      const bool use_c = past ? a.f_origin > 0 : in_cache;
-      const uint32_t col = past ? 0u : in_cache ? ci : (uint32_t)(u - a.f_origin);
-      const uint32_t off = (uint32_t)d * (use_c ? (uint32_t)a.c_rows : (uint32_t)a.f_rows) + col;
-      dma16_flat((use_c ? vcb : vfb) + off, vst + blk * 1024);
+      ci = min(ci, ci - ring_div);
+      const bool in_cache = ur < 0;
+      // both offsets, then a bitwise select (a plain select of the two sums
+      // is turned into a divergent branch)
+      const uint32_t sel = (uint32_t)(ur >> 31);
+      const uint32_t off = (((uint32_t)d * c_rows32 + ci) & sel) |
+                           (((uint32_t)d * f_rows32 + (uint32_t)min(ur, v_last)) & ~sel);
+      dma16_flat((in_cache ? vcb : vfb) + off, vst + blk * 1024);
     }
   };
   // DMA instructions this wave issues per K tile and per V tile
@@ -299,12 +306,11 @@ attn_prefill_kernel(AttnArgs a) {
   };
   // masks of an edge (or dead) tile, applied to its scores
   auto mask = [&](int it, floatx16 (&sacc)[BN / 32]) __attribute__((always_inline)) {
-    const int64_t kt = kt_first + (int64_t)it * BN;
+    const int kt = kt_first32 + it * BN;
     const bool interior = wave_live && kt + BN - 1 <= wq_lo &&
                           (a.window == 0 || wq_hi - kt < a.window);
     if (interior) return;
-    // relative positions fit 32 bits: |pq - u| < C + 64 + window
-    const int rel0 = (int)(pq - kt) - hl * 8;  // pq - (key index within tile)
+    const int rel0 = pq - kt - hl * 8;  // pq - (key index within tile)
     const bool qok = tq < C;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -366,9 +372,9 @@ attn_prefill_kernel(AttnArgs a) {
     }
   };
 
-  // the query fragments must have landed before the DMA stream starts: the
-  // vmcnt waits below count DMA only
-  wait_vm0_attn();
+  // the DMA stream starts while the query fragments are in flight: they were
+  // issued first, so every vmcnt wait below (which counts the most recent
+  // DMA) also covers them
   issue_k(0, ks0);
   issue_k(1, ks1);
   issue_v(0, vs0);
@@ -438,60 +444,65 @@ attn_prefill_kernel(AttnArgs a) {
     iter(j + 5, ks0, ks2, vs2, vs1, sn, sc);
     if (j + 6 >= ntiles) break;
   }
-  wait_vm0_attn();  // the clamped reloads have landed before the stages are reused
-
   // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]. The O^T
   // registers hold one query per lane, so the 32 x DH tile of a wave is
-  // transposed through LDS (the stage buffers, free after the loop) and
-  // written as contiguous 16-byte pieces of each query row. Waves 0-5 use
-  // one stage buffer each, then waves 6-7.
+  // transposed through LDS (the stage buffers, free after the loop; two
+  // waves per K stage and the first V stage, rows of DH * 2 bytes with the
+  // 16-byte chunk c of row q stored at c ^ (q mod chunks per row)) and
+  // written as contiguous 16-byte pieces of each query row. The gate loads
+  // are issued first, so their latency overlaps the wait for the last
+  // (clamped) K/V loads and the staging.
+  constexpr int CPR = DH / 8;            // 16-byte chunks per query row
+  constexpr int EPJ = 32 * CPR / 64;     // chunks per lane
+  static_assert(2 * 32 * DH * 2 <= KT_BYTES, "epilogue staging");
+  const int dq = a.n_q * DH;
+  // the lane index afresh (mbcnt), so that nothing derived from it has to be
+  // kept through the tile loop
+  const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  uint4 gv[EPJ];
+#pragma unroll
+  for (int j = 0; j < EPJ; ++j) {
+    const int c = ln + 64 * j;
+    // unconditional (rows past the step read its last row, unused) so that
+    // the loads stay in flight together
+    const int t = min(t0 + c / CPR, C - 1);
+    gv[j] = *reinterpret_cast<const uint4*>(a.gate + ((int64_t)b * C + t) * dq + head * DH + (c % CPR) * 8);
+  }
   l_run += __shfl_xor(l_run, 32, 64);
   const float il = l_run > 0.f ? 1.0f / l_run : 0.f;
-  constexpr int EP_ROW = DH * 2 + 16;   // padded LDS row (16-byte aligned)
-  constexpr int CPR = DH / 8;           // 16-byte chunks per query row
-  static_assert(32 * EP_ROW <= KT_BYTES && 32 * EP_ROW <= VT_BYTES, "epilogue staging");
-  const int dq = a.n_q * DH;
-  __syncthreads();
+  wait_vm0_attn();  // the clamped reloads have landed before the stages are reused
+  __syncthreads();  // and every wave has finished reading them
+  uint8_t* const buf = (wave < 2 ? ks0 : wave < 4 ? ks1 : wave < 6 ? ks2 : vs0) + (wave & 1) * (32 * DH * 2);
+  {
+    const int q = ln & 31;
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const bool active = round == 0 ? wave < 6 : wave >= 6;
-    const int slot = wave % 6;
-    uint8_t* buf = slot == 0 ? ks0 : slot == 1 ? ks1 : slot == 2 ? ks2 : slot == 3 ? vs0 : slot == 4 ? vs1 : vs2;
-    if (active) {
-      const int q = lane & 31;
+    for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
+      for (int eq = 0; eq < 4; ++eq) {
+        const int c = db * 4 + eq;  // 16-byte chunk of dims 8 c .. 8 c + 7
+        bf16x4 v4;
 #pragma unroll
-        for (int eq = 0; eq < 4; ++eq) {
-          const int d0 = db * 32 + eq * 8 + hl * 4;
-          bf16x4 v4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(o[db][eq * 4 + j] * il);
-          *reinterpret_cast<bf16x4*>(buf + q * EP_ROW + d0 * 2) = v4;
-        }
-    }
-    __syncthreads();
-    if (active) {
-#pragma unroll
-      for (int j = 0; j < 32 * CPR / 64; ++j) {
-        const int c = lane + 64 * j;
-        const int q = c / CPR, cc = c % CPR;
-        const int t = t0 + q;
-        if (t < C) {
-          const uint4 ov = *reinterpret_cast<const uint4*>(buf + q * EP_ROW + cc * 16);
-          const int64_t off = ((int64_t)b * C + t) * dq + head * DH + cc * 8;
-          const uint4 gv = *reinterpret_cast<const uint4*>(a.gate + off);
-          const uint16_t* oe = reinterpret_cast<const uint16_t*>(&ov);
-          const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
-          uint4 zv;
-          uint16_t* ze = reinterpret_cast<uint16_t*>(&zv);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) ze[k] = f2bf(bf2f(oe[k]) * bf2f(ge[k]));
-          *reinterpret_cast<uint4*>(a.z + off) = zv;
-        }
+        for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(o[db][eq * 4 + j] * il);
+        *reinterpret_cast<bf16x4*>(buf + q * (DH * 2) + ((c ^ (q % CPR)) << 4) + (ln >> 5) * 8) = v4;
       }
+  }
+  // each wave reads back only what it wrote (LDS operations of a wave are
+  // processed in order)
+#pragma unroll
+  for (int j = 0; j < EPJ; ++j) {
+    const int c = ln + 64 * j;
+    const int q = c / CPR, cc = c % CPR;
+    const int t = t0 + q;
+    if (t < C) {
+      const uint4 ov = *reinterpret_cast<const uint4*>(buf + q * (DH * 2) + ((cc ^ (q % CPR)) << 4));
+      const uint16_t* oe = reinterpret_cast<const uint16_t*>(&ov);
+      const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv[j]);
+      uint4 zv;
+      uint16_t* ze = reinterpret_cast<uint16_t*>(&zv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ze[k] = f2bf(bf2f(oe[k]) * bf2f(ge[k]));
+      *reinterpret_cast<uint4*>(a.z + ((int64_t)b * C + t) * dq + head * DH + cc * 8) = zv;
     }
-    __syncthreads();
   }
 }
 
