@@ -304,8 +304,19 @@ attn_prefill_kernel(AttnArgs a) {
         }
     }
   };
-  // masks of an edge (or dead) tile, applied to its scores
-  auto mask = [&](int it, floatx16 (&sacc)[BN / 32]) __attribute__((always_inline)) {
+  // the maximum score of each query over a tile (the two lanes holding a
+  // query's keys exchange theirs)
+  auto tile_max = [&](const floatx16 (&sacc)[BN / 32]) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  };
+  // masks of an edge (or dead) tile, applied to its scores; the tile's
+  // maximum (taken before masking) is then taken again
+  auto mask = [&](int it, floatx16 (&sacc)[BN / 32], float& mx) __attribute__((always_inline)) {
     const int kt = kt_first32 + it * BN;
     const bool interior = wave_live && kt + BN - 1 <= wq_lo &&
                           (a.window == 0 || wq_hi - kt < a.window);
@@ -320,48 +331,54 @@ attn_prefill_kernel(AttnArgs a) {
         const bool vis = qok && dist >= 0 && (a.window == 0 || dist < a.window);
         if (!vis) sacc[kb][e] = -INFINITY;
       }
+    mx = tile_max(sacc);
   };
-  // Online softmax of one tile's scores into bf16 probabilities. Lazy
-  // rescaling: the reference maximum m_run moves only when a score exceeds
-  // it by more than 8 in base-2 units, so probabilities stay below 2^8 and o
-  // and l are rescaled rarely; the final o / l is the same softmax either
-  // way. Returns the factor by which o must be rescaled (1 if the reference
-  // did not move; from m_run = -inf the first visible score always moves it,
-  // and all-masked queries keep -inf and get probabilities of 0). l sums the
-  // same bf16-rounded probabilities that enter the P V product.
+  // Online softmax in base 2 with lazy rescaling: the reference maximum
+  // m_run moves only when a tile's maximum exceeds it by more than 8 in
+  // base-2 units, so probabilities stay below 2^8 and o and l are rescaled
+  // rarely; the final o / l is the same softmax either way. From m_run =
+  // -inf the first visible score always moves it (exp2(-inf) = 0 rescales
+  // the empty o and l), and all-masked queries keep -inf and get
+  // probabilities of 0. reference() returns the factor by which o and l
+  // must be rescaled (1 if the reference did not move).
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto softmax = [&](const floatx16 (&sacc)[BN / 32], bf16x8 (&pf)[BN / 32][2]) __attribute__((always_inline)) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float nm = 0.f;  // -m_run in base-2 units (0 while m_run = -inf)
+  auto reference = [&](float mx) __attribute__((always_inline)) {
     const bool grow = (mx - m_run) * sl2 > 8.f;
     const float m_new = grow ? mx : m_run;
     // branch-free: exp2(0) = 1 when the reference stays, exp2(-inf) = 0 when
     // it leaves -inf
     const float corr = __builtin_amdgcn_exp2f(grow ? (m_run - m_new) * sl2 : 0.f);
     m_run = m_new;
-    const float nm = -(m_run == -INFINITY ? 0.f : m_run) * sl2;
+    nm = -(m_run == -INFINITY ? 0.f : m_run) * sl2;
+    return corr;
+  };
+  // bf16 probabilities of one tile under the current reference
+  auto probs = [&](const floatx16 (&sacc)[BN / 32], bf16x8 (&pf)[BN / 32][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[kb][h][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * h + e], sl2, nm)));
+  };
+  // l sums the same bf16 probabilities that enter the P V product
+  auto prob_sum = [&](const bf16x8 (&pf)[BN / 32][2]) __attribute__((always_inline)) {
     float la = 0.f, lb = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           bf16x2 pp;
-          pp[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * h + e], sl2, nm)));
-          pp[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * h + e + 1], sl2, nm)));
-          pf[kb][h][e] = pp[0];
-          pf[kb][h][e + 1] = pp[1];
+          pp[0] = pf[kb][h][e];
+          pp[1] = pf[kb][h][e + 1];
           if (e & 2) lb = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lb, false);
           else la = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, la, false);
         }
-      }
-    l_run = l_run * corr + (la + lb);
-    return corr;
+    return la + lb;
   };
   auto rescale = [&](float corr) __attribute__((always_inline)) {
     if (__ballot(corr != 1.f)) {
@@ -390,13 +407,19 @@ attn_prefill_kernel(AttnArgs a) {
   floatx16 sc[BN / 32], sn[BN / 32];
   bf16x8 pf[BN / 32][2];
   scores(ks0, sc);
+  float mx = tile_max(sc);
 
   // Iteration j: K read from stage (j + 1) % 3 and K of tile j + 3 loaded
   // into stage j % 3; V read from stage j % 3 and V of tile j + 2 loaded
   // into stage (j + 2) % 3. Loads past the last tile reload it (uniform
   // counts, no branch around the DMA); the scores computed from such a
   // reload after the last tile are discarded. s_cur holds the scores of tile
-  // j on entry, s_next receives those of tile j + 1.
+  // j on entry and mx their maximum (as computed before masking); s_next
+  // receives the scores of tile j + 1 and mx their maximum. After the
+  // reference update (and the rare rescale) one block runs the scores of
+  // tile j + 1 and the P V product of tile j on the matrix pipe, with the
+  // probabilities of tile j, their sum and the maximum of tile j + 1 on the
+  // VALU in between.
   auto iter = [&](int j, const uint8_t* kr, uint8_t* kw, const uint8_t* vr, uint8_t* vw,
                   floatx16 (&s_cur)[BN / 32], floatx16 (&s_next)[BN / 32])
       __attribute__((always_inline)) {
@@ -406,29 +429,26 @@ attn_prefill_kernel(AttnArgs a) {
     barrier_lds();
     issue_k(j + 3, kw);
     issue_v(j + 2, vw);
-    mask(j, s_cur);
+    mask(j, s_cur, mx);
+    const float corr = reference(mx);
+    l_run *= corr;
+    rescale(corr);
     scores(kr, s_next);
-    const float corr = softmax(s_cur, pf);
-    // interleave: per score MFMA of the next tile, one LDS fragment read and
-    // a share of the current tile's softmax
-    constexpr int NMF = (BN / 32) * (DH / 16);
+    probs(s_cur, pf);
+    pv(vr, pf);
+    l_run += prob_sum(pf);
+    mx = tile_max(s_next);
+    // interleave: per MFMA (the next tile's scores, then this tile's
+    // product) one LDS fragment read and a share of the VALU work
+    constexpr int NMF = 2 * (BN / 32) * (DH / 16);
     constexpr int AHEAD = 4;  // fragment reads in flight ahead of their MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i + AHEAD < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
     }
-    // the probabilities are complete here: without this the compiler sinks
-    // their computation below the (rarely taken) rescale branch, out of
-    // reach of the score MFMAs it is meant to overlap
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pf[kb][h]));
-    rescale(corr);
-    pv(vr, pf);
   };
   for (int j = 0;; j += 6) {
     iter(j, ks1, ks0, vs0, vs2, sc, sn);
