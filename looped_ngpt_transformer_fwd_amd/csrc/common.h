@@ -26,6 +26,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// The same rounding by the hardware conversion (v_cvt_pk_bf16_f32: one
+// instruction where f2bf takes three). Equal to f2bf for every normal
+// input; kept to epilogues whose outputs never meet fp32 denormals.
+__device__ __forceinline__ uint16_t f2bf_hw(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

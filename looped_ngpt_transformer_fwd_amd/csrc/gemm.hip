@@ -98,14 +98,17 @@ __device__ __forceinline__ void big_read(const uint8_t* sa, const uint8_t* sb, i
 
 // v_mfma_f32_16x16x32_bf16: on random bf16 data it sustains about 14% more
 // throughput on this part than the 32x32x16 form (measured, register-only).
-template <int FM, int FN>
+// TR: the operands swapped, so that block (i, j) holds the transpose (lane
+// holds row (lane % 16) and columns 4 (lane / 16) + e).
+template <bool TR, int FM, int FN>
 __device__ __forceinline__ void big_mfma(const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN],
                                          floatx4 (&acc)[FM][FN]) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
 }
 
 // Phase boundary of the ping-pong schedule: an LDS-only barrier that the
@@ -238,7 +241,7 @@ gemm_big_kernel(GemmArgs g) {
     if (wave < NW / 2) {
   #define DORY_PP_A(KS, CUR, NXT)                                             \
       mem(KS, CUR, NXT); pp_barrier();                                        \
-      big_mfma(af, bfr, acc); wait_two(); pp_barrier();
+      big_mfma<EPI == EPI_QKV>(af, bfr, acc); wait_two(); pp_barrier();
       int ks = 0;
       for (; ks + 4 <= ksteps; ks += 4) {
         DORY_PP_A(ks, st0, st3)
@@ -255,7 +258,7 @@ gemm_big_kernel(GemmArgs g) {
     } else {
   #define DORY_PP_B(KS, CUR, NXT)                                             \
       mem(KS, CUR, NXT); wait_two(); pp_barrier();                            \
-      big_mfma(af, bfr, acc); pp_barrier();
+      big_mfma<EPI == EPI_QKV>(af, bfr, acc); pp_barrier();
       pp_barrier();
       int ks = 0;
       for (; ks + 4 <= ksteps; ks += 4) {
@@ -281,7 +284,7 @@ gemm_big_kernel(GemmArgs g) {
       barrier_lds();
       issue(min(ks + 3, ksteps - 1), nxt);
       big_read(cur + a_wave, cur + b_wave, loff, af, bfr);
-      big_mfma(af, bfr, acc);
+      big_mfma<EPI == EPI_QKV>(af, bfr, acc);
     };
     issue(0, st0);
     issue(1, st1);
@@ -305,90 +308,117 @@ gemm_big_kernel(GemmArgs g) {
   const int rbase = m0 + wm * BIG_WM + (lane >> 4) * 4;
   const int cbase = n0 + wn * BIG_WN + (lane & 15);
   if (EPI == EPI_QKV) {
-    // Each wave's 128 columns are one head of q, k, v or the gate. Lane holds
-    // head dims d = 16 j + (lane % 16), j = 0..7, for 16 rows; RoPE pairs
-    // (d, d + 64) are (j, j + 4) of the same lane; the per-head norm sums the
-    // lane's 8 values and reduces over the 16 lanes that share its rows.
+    // Each wave's 128 columns are one head of q, k, v or the gate. The
+    // accumulators are transposed (the MFMA operands are swapped for this
+    // epilogue): lane l holds token row wm * 64 + 16 i + (l % 16) of the tile
+    // and head dims d = 16 j + 4 (l / 16) + e, e = 0..3, so q, k and gate
+    // rows leave as 8-byte pieces (4 consecutive dims) and V^T columns as
+    // runs of 16 consecutive tokens. RoPE pairs (d, d + 64) are blocks (j,
+    // j + 4) of the same lane; the per-head norm sums the lane's 32 values
+    // and reduces over the 4 lanes that hold the same token.
     const QkvEpi& q = g.qkv;
     const int dq = q.nq * 128, dkv = q.nkv * 128;
     const int c0 = n0 + wn * BIG_WN;
-    const int dl = lane & 15;
+    const int tl = lane & 15, dg = (lane >> 4) * 4;
     int kind, hh;
     if (c0 < dq) { kind = 0; hh = c0 >> 7; }
     else if (c0 < dq + dkv) { kind = 1; hh = (c0 - dq) >> 7; }
     else if (c0 < dq + 2 * dkv) { kind = 2; hh = (c0 - dq - dkv) >> 7; }
     else { kind = 3; hh = (c0 - dq - 2 * dkv) >> 7; }
     if (c0 >= g.N) kind = 4;
-    float sq[8];
+    float4 sq[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sq[j] = kind <= 1 ? q.s_qk[16 * j + dl] : 0.f;
-    // The RoPE table rows of the tile's 256 token rows (cos in st0/st1, sin
-    // in st2/st3: 256 B per row) go to LDS before any store, and s_qk
-    // becomes plain register values: a global load consumed between the
-    // stores would make each wait for all earlier stores (one counter).
+    for (int j = 0; j < 8; ++j)
+      sq[j] = kind <= 1 ? make_float4(q.s_qk[16 * j + dg], q.s_qk[16 * j + dg + 1], q.s_qk[16 * j + dg + 2],
+                                      q.s_qk[16 * j + dg + 3])
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    // s_qk becomes plain register values before any store: a global load
+    // consumed between the stores would make each wait for all earlier
+    // stores (one counter). The RoPE table rows of a 16-row block (the
+    // lane's 16 cos and 16 sin values) are loaded one block ahead, before
+    // the current block's stores, for the same reason.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(sq[j]));
-    __syncthreads();  // every wave is done with the stages
-    if (n0 < dq + dkv) {
-      for (int idx = tid; idx < 256 * 16; idx += 64 * NW) {
-        const int r = idx >> 4, c = idx & 15;
-        const int row = m0 + r;
-        const int t = row < g.M ? row % q.T : 0;
-        const float4 vc = reinterpret_cast<const float4*>(q.cs + (int64_t)t * 64)[c];
-        const float4 vs = reinterpret_cast<const float4*>(q.sn + (int64_t)t * 64)[c];
-        *reinterpret_cast<float4*>((r < 128 ? st0 : st1) + (r & 127) * 256 + c * 16) = vc;
-        *reinterpret_cast<float4*>((r < 128 ? st2 : st3) + (r & 127) * 256 + c * 16) = vs;
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(sq[j].x), "+v"(sq[j].y), "+v"(sq[j].z), "+v"(sq[j].w));
+    const bool rope = kind <= 1;
+    auto load_tab = [&](int i, float4 (&c4)[4], float4 (&s4)[4]) __attribute__((always_inline)) {
+      const int row = m0 + wm * BIG_WM + 16 * i + tl;
+      const int t = row < g.M ? row % q.T : 0;
+      const float4* cp = reinterpret_cast<const float4*>(q.cs + (int64_t)t * 64);
+      const float4* sp = reinterpret_cast<const float4*>(q.sn + (int64_t)t * 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c4[j] = cp[4 * j + (lane >> 4)];  // dims 16 j + dg .. + 3
+        s4[j] = sp[4 * j + (lane >> 4)];
       }
-      __syncthreads();
-    }
+    };
+    float4 tc[4], ts[4];
+    if (rope) load_tab(0, tc, ts);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int rl = wm * BIG_WM + 16 * i + tl;  // token row within the tile
+      const int row = m0 + rl;
+      const bool ok = row < g.M;
+      const int b = row / q.T, t = row - b * q.T;
+      if (kind <= 1) {
+        float4 c4[4], s4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = rbase + i * 16 + e;
-        const bool ok = row < g.M;
-        const int b = row / q.T, t = row - b * q.T;
-        const int rl = row - m0;  // row within the tile
-        float x[8];
+        for (int j = 0; j < 4; ++j) { c4[j] = tc[j]; s4[j] = ts[j]; }
+        if (i + 1 < FM) load_tab(i + 1, tc, ts);
+        float r[8][4];
+        float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = acc[i][j][e];
-        if (kind <= 1) {
-          const float* lcs = reinterpret_cast<const float*>((rl < 128 ? st0 : st1) + (rl & 127) * 256);
-          const float* lsn = reinterpret_cast<const float*>((rl < 128 ? st2 : st3) + (rl & 127) * 256);
-          float r[8];
-          float ss = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const float cv[4] = {c4[j].x, c4[j].y, c4[j].z, c4[j].w};
+          const float sv[4] = {s4[j].x, s4[j].y, s4[j].z, s4[j].w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float c = lcs[16 * j + dl], sn = lsn[16 * j + dl];
-            r[j] = x[j] * c - x[j + 4] * sn;
-            r[j + 4] = x[j + 4] * c + x[j] * sn;
-            ss += r[j] * r[j] + r[j + 4] * r[j + 4];
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = acc[i][j][e], x1 = acc[i][j + 4][e];
+            r[j][e] = x0 * cv[e] - x1 * sv[e];
+            r[j + 4][e] = x1 * cv[e] + x0 * sv[e];
+            ss += r[j][e] * r[j][e] + r[j + 4][e] * r[j + 4][e];
           }
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = __builtin_amdgcn_rsqf(ss);  // bf16 outputs: 1 ulp is ample
+        if (ok) {
+          uint16_t* dst = kind == 0
+              ? q.qh + (((int64_t)b * q.nq + hh) * q.T + t) * 128
+              : q.kf + (((int64_t)b * q.nkv + hh) * q.f_rows + t + q.row_off) * 128;
 #pragma unroll
-          for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-          const float inv = 1.0f / sqrtf(ss);
-          if (ok) {
-            uint16_t* dst = kind == 0
-                ? q.qh + (((int64_t)b * q.nq + hh) * q.T + t) * 128
-                : q.kf + (((int64_t)b * q.nkv + hh) * q.f_rows + t + q.row_off) * 128;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dst[16 * j + dl] = f2bf(r[j] * inv * sq[j]);
+          for (int j = 0; j < 8; ++j) {
+            const float sj[4] = {sq[j].x, sq[j].y, sq[j].z, sq[j].w};
+            ushort4 o;
+            o.x = f2bf_hw(r[j][0] * inv * sj[0]);
+            o.y = f2bf_hw(r[j][1] * inv * sj[1]);
+            o.z = f2bf_hw(r[j][2] * inv * sj[2]);
+            o.w = f2bf_hw(r[j][3] * inv * sj[3]);
+            *reinterpret_cast<ushort4*>(dst + 16 * j + dg) = o;
           }
-        } else if (kind == 2) {
-          if (ok) {
-            uint16_t* dst = q.vf + (((int64_t)b * q.nkv + hh) * 128 + dl) * q.f_rows + t + q.row_off;
-            const int64_t cstep = 16 * q.f_rows;
+        }
+      } else if (kind == 2) {
+        if (ok) {
+          uint16_t* dst = q.vf + ((int64_t)b * q.nkv + hh) * 128 * q.f_rows + t + q.row_off;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dst[j * cstep] = f2bf(x[j]);
-          }
-        } else if (kind == 3) {
-          if (ok) {
-            uint16_t* dst = q.gate + (int64_t)row * dq + hh * 128 + dl;
+          for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dst[16 * j] = f2bf(1.f / (1.f + __expf(-x[j])));
+            for (int e = 0; e < 4; ++e) dst[(int64_t)(16 * j + dg + e) * q.f_rows] = f2bf_hw(acc[i][j][e]);
+        }
+      } else if (kind == 3) {
+        if (ok) {
+          uint16_t* dst = q.gate + (int64_t)row * dq + hh * 128;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            ushort4 o;
+            o.x = f2bf_hw(__builtin_amdgcn_rcpf(1.f + __expf(-acc[i][j][0])));
+            o.y = f2bf_hw(__builtin_amdgcn_rcpf(1.f + __expf(-acc[i][j][1])));
+            o.z = f2bf_hw(__builtin_amdgcn_rcpf(1.f + __expf(-acc[i][j][2])));
+            o.w = f2bf_hw(__builtin_amdgcn_rcpf(1.f + __expf(-acc[i][j][3])));
+            *reinterpret_cast<ushort4*>(dst + 16 * j + dg) = o;
           }
         }
       }
+    }
   } else if (EPI == EPI_F32 || EPI == EPI_LOGITS) {
     float* C = g.C;
 #pragma unroll
