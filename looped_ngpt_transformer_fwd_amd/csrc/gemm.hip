@@ -334,25 +334,35 @@ gemm_big_kernel(GemmArgs g) {
                         : make_float4(0.f, 0.f, 0.f, 0.f);
     // s_qk becomes plain register values before any store: a global load
     // consumed between the stores would make each wait for all earlier
-    // stores (one counter). The RoPE table rows of a 16-row block (the
-    // lane's 16 cos and 16 sin values) are loaded one block ahead, before
-    // the current block's stores, for the same reason.
+    // stores (one counter).
 #pragma unroll
     for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(sq[j].x), "+v"(sq[j].y), "+v"(sq[j].z), "+v"(sq[j].w));
-    const bool rope = kind <= 1;
-    auto load_tab = [&](int i, float4 (&c4)[4], float4 (&s4)[4]) __attribute__((always_inline)) {
-      const int row = m0 + wm * BIG_WM + 16 * i + tl;
-      const int t = row < g.M ? row % q.T : 0;
-      const float4* cp = reinterpret_cast<const float4*>(q.cs + (int64_t)t * 64);
-      const float4* sp = reinterpret_cast<const float4*>(q.sn + (int64_t)t * 64);
+    // The RoPE table rows of the tile's 256 token rows go to the (now free)
+    // stages by direct global->LDS DMA, all 128 KiB in flight at once (the
+    // table is evicted from L2 by the operand stream, so a load costs a
+    // memory round trip): cos in st0/st1, sin in st2/st3, 256 B per row,
+    // 16-byte chunk c of row r stored at c ^ (r % 16) so that the 16 rows
+    // one fragment read covers fall in distinct bank groups. 1 KiB block
+    // k holds rows 4 k' .. 4 k' + 3 of its table (k' = k % 64), lane l
+    // chunk l % 16 of row 4 k' + l / 16.
+    if (n0 < dq + dkv) {
+      __syncthreads();  // every wave is done with the stages
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c4[j] = cp[4 * j + (lane >> 4)];  // dims 16 j + dg .. + 3
-        s4[j] = sp[4 * j + (lane >> 4)];
+      for (int kb = 0; kb < 128 / NW; ++kb) {
+        const int blk = wave * (128 / NW) + kb;  // 0-63 cos, 64-127 sin
+        const int r0 = (blk & 63) * 4;
+        const int rr = r0 + (lane >> 4);
+        const int row = m0 + rr;
+        const int t = row < g.M ? row % q.T : 0;
+        const int c = (lane & 15) ^ (rr & 15);
+        const float* src = (blk < 64 ? q.cs : q.sn) + (int64_t)t * 64 + c * 4;
+        uint8_t* dst = (blk < 64 ? (r0 < 128 ? st0 : st1) : (r0 < 128 ? st2 : st3)) + (r0 & 127) * 256;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       }
-    };
-    float4 tc[4], ts[4];
-    if (rope) load_tab(0, tc, ts);
+      wait_vm0();
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rl = wm * BIG_WM + 16 * i + tl;  // token row within the tile
@@ -360,10 +370,15 @@ gemm_big_kernel(GemmArgs g) {
       const bool ok = row < g.M;
       const int b = row / q.T, t = row - b * q.T;
       if (kind <= 1) {
+        const uint8_t* lcs = (rl < 128 ? st0 : st1) + (rl & 127) * 256;
+        const uint8_t* lsn = (rl < 128 ? st2 : st3) + (rl & 127) * 256;
         float4 c4[4], s4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { c4[j] = tc[j]; s4[j] = ts[j]; }
-        if (i + 1 < FM) load_tab(i + 1, tc, ts);
+        for (int j = 0; j < 4; ++j) {
+          const int po = ((4 * j + (lane >> 4)) ^ tl) << 4;  // chunk of dims 16 j + dg .. + 3
+          c4[j] = *reinterpret_cast<const float4*>(lcs + po);
+          s4[j] = *reinterpret_cast<const float4*>(lsn + po);
+        }
         float r[8][4];
         float ss = 0.f;
 #pragma unroll
