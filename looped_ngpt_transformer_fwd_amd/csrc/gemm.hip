@@ -137,10 +137,8 @@ gemm_big_kernel(GemmArgs g) {
   static_assert(BIG_WN == 128 || (BN == 288 && EPI == EPI_BF16 && NW == 8),
                 "epilogues assume 128 columns per wave; 288-column tiles have the bf16 one only");
   static_assert(NW == 8 || BN == BIG_BN, "one wave per SIMD: 256 columns");
-  // A stage holds the A tile (16 KiB) and the B tile (BN x 64 B); a 288-wide
-  // stage is padded so that the four hold the bf16 epilogue's staging
-  // (8 waves x 64 rows x 304 B)
-  constexpr int STAGE = BN == BIG_BN ? 2 * BIG_OP_BYTES : 38912;
+  // A stage holds the A tile (16 KiB) and the B tile (BN x 64 B)
+  constexpr int STAGE = BIG_OP_BYTES + BN * BIG_BK * 2;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
@@ -241,7 +239,7 @@ gemm_big_kernel(GemmArgs g) {
     if (wave < NW / 2) {
   #define DORY_PP_A(KS, CUR, NXT)                                             \
       mem(KS, CUR, NXT); pp_barrier();                                        \
-      big_mfma<EPI == EPI_QKV>(af, bfr, acc); wait_two(); pp_barrier();
+      big_mfma<EPI == EPI_QKV || EPI == EPI_BF16>(af, bfr, acc); wait_two(); pp_barrier();
       int ks = 0;
       for (; ks + 4 <= ksteps; ks += 4) {
         DORY_PP_A(ks, st0, st3)
@@ -258,7 +256,7 @@ gemm_big_kernel(GemmArgs g) {
     } else {
   #define DORY_PP_B(KS, CUR, NXT)                                             \
       mem(KS, CUR, NXT); wait_two(); pp_barrier();                            \
-      big_mfma<EPI == EPI_QKV>(af, bfr, acc); pp_barrier();
+      big_mfma<EPI == EPI_QKV || EPI == EPI_BF16>(af, bfr, acc); pp_barrier();
       pp_barrier();
       int ks = 0;
       for (; ks + 4 <= ksteps; ks += 4) {
@@ -284,7 +282,7 @@ gemm_big_kernel(GemmArgs g) {
       barrier_lds();
       issue(min(ks + 3, ksteps - 1), nxt);
       big_read(cur + a_wave, cur + b_wave, loff, af, bfr);
-      big_mfma<EPI == EPI_QKV>(af, bfr, acc);
+      big_mfma<EPI == EPI_QKV || EPI == EPI_BF16>(af, bfr, acc);
     };
     issue(0, st0);
     issue(1, st1);
@@ -450,53 +448,34 @@ gemm_big_kernel(GemmArgs g) {
         }
     }
   } else if (EPI == EPI_BF16) {
-    // The wave's 64 x 128 outputs, rounded to bf16, go through LDS (16 KB
-    // per wave, 16-byte chunks XOR-swizzled by row) and leave as 16-byte
-    // pieces of 256-byte rows.
-    __syncthreads();  // every wave is done with the stages
-    // staging rows: 256 B (16 chunks, XOR-swizzled) for 128 columns; 288 B
-    // plus 16 B of padding for 144 columns
-    constexpr int NCH = BIG_WN / 8;
-    constexpr int SROWB = NCH == 16 ? 256 : NCH * 16 + 16;
-    constexpr int WSTG = 64 * SROWB;
-    uint8_t* stg;
-    if constexpr (NCH == 16) {
-      stg = ((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * 16384;
-    } else {
-      // waves 0-1 in st0, 2-3 in st1, ...: 2 x 19,456 B of each 38,912 B stage
-      stg = ((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * WSTG;
-    }
-    auto soff = [&](int r, int c) { return NCH == 16 ? r * 256 + ((c ^ (r & 15)) << 4) : r * SROWB + c * 16; };
+    // Accumulators transposed (the MFMA operands are swapped for this
+    // epilogue): lane l holds row 16 i + (l % 16) of the wave's 64 rows and
+    // columns 16 j + 4 (l / 16) + e, e = 0..3, i.e. four consecutive
+    // outputs of one row, rounded to bf16 and stored as one 8-byte piece
+    // (no staging through LDS, no workgroup barrier).
+    const int cl = n0 + wn * BIG_WN + 4 * (lane >> 4);
+    const bool vec_ok = g.ldc16 % 4 == 0 && (reinterpret_cast<uintptr_t>(g.C16) & 7) == 0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = (lane >> 4) * 4 + i * 16 + e;
+    for (int i = 0; i < FM; ++i) {
+      const int row = m0 + wm * BIG_WM + 16 * i + (lane & 15);
+      if (row < g.M) {
+        uint16_t* dst = g.C16 + (int64_t)row * g.ldc16;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = j * 16 + (lane & 15);
-          *reinterpret_cast<uint16_t*>(stg + soff(r, col >> 3) + (col & 7) * 2) = f2bf(acc[i][j][e]);
-        }
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    const int c0 = n0 + wn * BIG_WN;
-    const bool vec_ok = g.ldc16 % 8 == 0 && (reinterpret_cast<uintptr_t>(g.C16) & 15) == 0;
+          const int col = cl + 16 * j;
+          ushort4 o;
+          o.x = f2bf_hw(acc[i][j][0]);
+          o.y = f2bf_hw(acc[i][j][1]);
+          o.z = f2bf_hw(acc[i][j][2]);
+          o.w = f2bf_hw(acc[i][j][3]);
+          if (vec_ok && col + 4 <= g.N) {
+            *reinterpret_cast<ushort4*>(dst + col) = o;
+          } else {
+            const uint16_t oe[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int pass = 0; pass < 64 * NCH / 64; ++pass) {
-      const int q = pass * 64 + lane;
-      const int r = NCH == 16 ? pass * 4 + (lane >> 4) : q / NCH, c = NCH == 16 ? lane & 15 : q % NCH;
-      const int row = m0 + wm * BIG_WM + r;
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + soff(r, c));
-      uint16_t* dst = g.C16 + (int64_t)row * g.ldc16 + c0 + c * 8;
-      if (row < g.M) {
-        if (vec_ok && c0 + c * 8 + 8 <= g.N) {
-          *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-          const uint16_t* ve = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (c0 + c * 8 + k < g.N) dst[k] = ve[k];
+            for (int k = 0; k < 4; ++k)
+              if (col + k < g.N) dst[col + k] = oe[k];
+          }
         }
       }
     }
