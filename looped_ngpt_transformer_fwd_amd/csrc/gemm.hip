@@ -150,6 +150,15 @@ gemm_big_kernel(GemmArgs g) {
   const int ntm = (g.M + BIG_BM - 1) / BIG_BM, ntn = (g.N + BN - 1) / BN;
   int tm, tn;
   big_tile_coords(blockIdx.x, ntm, ntn, g.order & 0xFF, (g.order >> 8) & 1, &tm, &tn);
+  if (EPI == EPI_QKV) {
+    // column tiles in the order s * tn mod ntn (s coprime to ntn): the tiles
+    // that run at once on an XCD (neighbouring columns) mix q, k, v and gate
+    // heads instead of all fetching RoPE rows and normalizing at the same
+    // moment (B panels of neighbouring columns share nothing, so L2 reuse
+    // is unchanged)
+    const int sp = ntn % 3 != 0 ? 3 : ntn % 7 != 0 ? 7 : 1;
+    tn = (tn * sp) % ntn;
+  }
   const int m0 = tm * BIG_BM, n0 = tn * BN;
   const int ksteps = g.K / BIG_BK;           // even: K is a multiple of 64
 
