@@ -199,6 +199,11 @@ dory_status dory_kv_slot(const dory_kv* kv, int32_t sublayer, int32_t loop, dory
  *   hidden: device fp32 [B, T, d], output of the last sublayer, or NULL.
  *   states: device fp32 [k, B, T, d], recurrent state after each loop
  *     (s_1 .. s_k), or NULL.
+ * Cached keys must have been made with the layers' current s_qk (by this
+ * model, or copied from a cache of it): the prefill attention bounds every
+ * score by max |s_qk|^2 (section Architecture: q and k heads are s_qk times
+ * unit vectors) and, when 2 max|s_qk|^2 scale log2(e) <= 120, uses that
+ * bound as a fixed softmax reference instead of a running maximum.
  * On success the cache length grows by T. */
 dory_status dory_prefill(dory_model* m, dory_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
                          int32_t k, dory_cache_mode mode, void* ws, size_t ws_bytes,

@@ -19,6 +19,8 @@
 // Decode: one query per sequence; split over keys, VALU dot products with
 // 16 lanes per 256-byte key row, partial (max, sum, o) per split, and a
 // combine kernel that merges the splits and applies the gate.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -63,7 +65,7 @@ __device__ __forceinline__ int kswz(int r) {
   return (r / RP) & (KCH - 1);
 }
 
-template <int DH, int GRP>
+template <int DH, int GRP, bool FRESH>
 __global__ void __launch_bounds__(PF_WAVES * 64)
 attn_prefill_kernel(AttnArgs a) {
   constexpr int QB = PF_WAVES / GRP;   // 32-query blocks per workgroup
@@ -125,6 +127,14 @@ attn_prefill_kernel(AttnArgs a) {
   const int hl = lane >> 5;
   const int64_t bg = (int64_t)b * a.n_kv + g;
   const int pq = (int)a.p0 + tq;  // positions fit 31 bits (at most 2^24)
+
+  // |s_qk| for the fixed softmax reference (loaded first: the waits for the
+  // DMA below count only younger loads)
+  float sqk_m = 0.f;
+  if (a.ref_s_qk) {
+#pragma unroll
+    for (int d = lane; d < DH; d += 64) sqk_m = fmaxf(sqk_m, fabsf(a.ref_s_qk[d]));
+  }
 
   bf16x8 qf[DH / 16];
   {
@@ -228,9 +238,14 @@ attn_prefill_kernel(AttnArgs a) {
       const int ur = rel + r;
       uint32_t ci = km + k_rm[j];
       ci = min(ci, ci - ring_div);
-      const bool in_cache = ur < 0;
-      const uint32_t row = in_cache ? ci : (uint32_t)min(ur, k_last);
-      dma16_flat((in_cache ? kcb : kfb) + (row * DH + c * 8), kst + blk * 1024);
+      if constexpr (FRESH) {
+        // every key of the launch is a step key (no cache rows below it)
+        dma16_flat(kfb + ((uint32_t)min(ur, k_last) * DH + c * 8), kst + blk * 1024);
+      } else {
+        const bool in_cache = ur < 0;
+        const uint32_t row = in_cache ? ci : (uint32_t)min(ur, k_last);
+        dma16_flat((in_cache ? kcb : kfb) + (row * DH + c * 8), kst + blk * 1024);
+      }
     }
   };
   auto issue_v = [&](int it, uint8_t* vst) __attribute__((always_inline)) {
@@ -246,13 +261,17 @@ attn_prefill_kernel(AttnArgs a) {
       const int ur = rel + c * 8;
       uint32_t ci = km + v_cm[j];
       ci = min(ci, ci - ring_div);
-      const bool in_cache = ur < 0;
-      // both offsets, then a bitwise select (a plain select of the two sums
-      // is turned into a divergent branch)
-      const uint32_t sel = (uint32_t)(ur >> 31);
-      const uint32_t off = (((uint32_t)d * c_rows32 + ci) & sel) |
-                           (((uint32_t)d * f_rows32 + (uint32_t)min(ur, v_last)) & ~sel);
-      dma16_flat((in_cache ? vcb : vfb) + off, vst + blk * 1024);
+      if constexpr (FRESH) {
+        dma16_flat(vfb + ((uint32_t)d * f_rows32 + (uint32_t)min(ur, v_last)), vst + blk * 1024);
+      } else {
+        const bool in_cache = ur < 0;
+        // both offsets, then a bitwise select (a plain select of the two sums
+        // is turned into a divergent branch)
+        const uint32_t sel = (uint32_t)(ur >> 31);
+        const uint32_t off = (((uint32_t)d * c_rows32 + ci) & sel) |
+                             (((uint32_t)d * f_rows32 + (uint32_t)min(ur, v_last)) & ~sel);
+        dma16_flat((in_cache ? vcb : vfb) + off, vst + blk * 1024);
+      }
     }
   };
   // DMA instructions this wave issues per K tile and per V tile
@@ -316,7 +335,7 @@ attn_prefill_kernel(AttnArgs a) {
   };
   // masks of an edge (or dead) tile, applied to its scores; the tile's
   // maximum (taken before masking) is then taken again
-  auto mask = [&](int it, floatx16 (&sacc)[BN / 32], float& mx) __attribute__((always_inline)) {
+  auto mask = [&](auto fixed, int it, floatx16 (&sacc)[BN / 32], float& mx) __attribute__((always_inline)) {
     const int kt = kt_first32 + it * BN;
     const bool interior = wave_live && kt + BN - 1 <= wq_lo &&
                           (a.window == 0 || wq_hi - kt < a.window);
@@ -331,7 +350,7 @@ attn_prefill_kernel(AttnArgs a) {
         const bool vis = qok && dist >= 0 && (a.window == 0 || dist < a.window);
         if (!vis) sacc[kb][e] = -INFINITY;
       }
-    mx = tile_max(sacc);
+    if constexpr (!decltype(fixed)::value) mx = tile_max(sacc);
   };
   // Online softmax in base 2 with lazy rescaling: the reference maximum
   // m_run moves only when a tile's maximum exceeds it by more than 8 in
@@ -407,7 +426,20 @@ attn_prefill_kernel(AttnArgs a) {
   floatx16 sc[BN / 32], sn[BN / 32];
   bf16x8 pf[BN / 32][2];
   scores(ks0, sc);
-  float mx = tile_max(sc);
+
+  // Fixed softmax reference. q and k heads are s_qk times unit vectors, so
+  // every raw score lies in [-B, B] with B = max |s_qk|^2 (times 1 + 2^-6
+  // for the bf16 rounding of q and k). When 2 B scale log2(e) <= 120 the
+  // probabilities exp2((s - B) scale log2(e)) are normal fp32 and bf16
+  // numbers in (2^-120, 1] for every possible score, so B serves as the
+  // reference itself: no running maximum, no rescaling, no per-tile lane
+  // exchange. Otherwise (or without s_qk) the running maximum below. The
+  // normalized result o / l is the same softmax either way.
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sqk_m = fmaxf(sqk_m, __shfl_xor(sqk_m, o, 64));
+  const float ref_b = sqk_m * sqk_m * (1.f + 1.f / 64.f);
+  const bool fixed_ref =
+      __builtin_amdgcn_readfirstlane((int)(a.ref_s_qk != nullptr && ref_b * sl2 <= 60.f)) != 0;
 
   // Iteration j: K read from stage (j + 1) % 3 and K of tile j + 3 loaded
   // into stage j % 3; V read from stage j % 3 and V of tile j + 2 loaded
@@ -419,51 +451,62 @@ attn_prefill_kernel(AttnArgs a) {
   // reference update (and the rare rescale) one block runs the scores of
   // tile j + 1 and the P V product of tile j on the matrix pipe, with the
   // probabilities of tile j, their sum and the maximum of tile j + 1 on the
-  // VALU in between.
-  auto iter = [&](int j, const uint8_t* kr, uint8_t* kw, const uint8_t* vr, uint8_t* vw,
-                  floatx16 (&s_cur)[BN / 32], floatx16 (&s_next)[BN / 32])
-      __attribute__((always_inline)) {
-    // the loads of iteration j - 2 (K of j + 1, V of j) have landed
-    if constexpr (kEven) __builtin_amdgcn_s_waitcnt(0x0F70 | (kPW + vPW));
-    else wait_vm(kpw + vpw);
-    barrier_lds();
-    issue_k(j + 3, kw);
-    issue_v(j + 2, vw);
-    mask(j, s_cur, mx);
-    const float corr = reference(mx);
-    l_run *= corr;
-    rescale(corr);
-    scores(kr, s_next);
-    probs(s_cur, pf);
-    pv(vr, pf);
-    l_run += prob_sum(pf);
-    mx = tile_max(s_next);
-    // interleave: per MFMA (the next tile's scores, then this tile's
-    // product) one LDS fragment read and a share of the VALU work
-    constexpr int NMF = 2 * (BN / 32) * (DH / 16);
-    constexpr int AHEAD = 4;  // fragment reads in flight ahead of their MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
+  // VALU in between. With the fixed reference the maxima and the reference
+  // update are left out.
+  auto run = [&](auto fixed) __attribute__((always_inline)) {
+    constexpr bool FIX = decltype(fixed)::value;
+    float mx = 0.f;
+    if constexpr (FIX) nm = -ref_b * sl2;
+    else mx = tile_max(sc);
+    auto iter = [&](int j, const uint8_t* kr, uint8_t* kw, const uint8_t* vr, uint8_t* vw,
+                    floatx16 (&s_cur)[BN / 32], floatx16 (&s_next)[BN / 32])
+        __attribute__((always_inline)) {
+      // the loads of iteration j - 2 (K of j + 1, V of j) have landed
+      if constexpr (kEven) __builtin_amdgcn_s_waitcnt(0x0F70 | (kPW + vPW));
+      else wait_vm(kpw + vpw);
+      barrier_lds();
+      issue_k(j + 3, kw);
+      issue_v(j + 2, vw);
+      mask(fixed, j, s_cur, mx);
+      if constexpr (!FIX) {
+        const float corr = reference(mx);
+        l_run *= corr;
+        rescale(corr);
+      }
+      scores(kr, s_next);
+      probs(s_cur, pf);
+      pv(vr, pf);
+      l_run += prob_sum(pf);
+      if constexpr (!FIX) mx = tile_max(s_next);
+      // interleave: per MFMA (the next tile's scores, then this tile's
+      // product) one LDS fragment read and a share of the VALU work
+      constexpr int NMF = 2 * (BN / 32) * (DH / 16);
+      constexpr int AHEAD = 4;  // fragment reads in flight ahead of their MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
 #pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (i + AHEAD < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i + AHEAD < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+    };
+    for (int j = 0;; j += 6) {
+      iter(j, ks1, ks0, vs0, vs2, sc, sn);
+      if (j + 1 >= ntiles) break;
+      iter(j + 1, ks2, ks1, vs1, vs0, sn, sc);
+      if (j + 2 >= ntiles) break;
+      iter(j + 2, ks0, ks2, vs2, vs1, sc, sn);
+      if (j + 3 >= ntiles) break;
+      iter(j + 3, ks1, ks0, vs0, vs2, sn, sc);
+      if (j + 4 >= ntiles) break;
+      iter(j + 4, ks2, ks1, vs1, vs0, sc, sn);
+      if (j + 5 >= ntiles) break;
+      iter(j + 5, ks0, ks2, vs2, vs1, sn, sc);
+      if (j + 6 >= ntiles) break;
     }
   };
-  for (int j = 0;; j += 6) {
-    iter(j, ks1, ks0, vs0, vs2, sc, sn);
-    if (j + 1 >= ntiles) break;
-    iter(j + 1, ks2, ks1, vs1, vs0, sn, sc);
-    if (j + 2 >= ntiles) break;
-    iter(j + 2, ks0, ks2, vs2, vs1, sc, sn);
-    if (j + 3 >= ntiles) break;
-    iter(j + 3, ks1, ks0, vs0, vs2, sn, sc);
-    if (j + 4 >= ntiles) break;
-    iter(j + 4, ks2, ks1, vs1, vs0, sc, sn);
-    if (j + 5 >= ntiles) break;
-    iter(j + 5, ks0, ks2, vs2, vs1, sn, sc);
-    if (j + 6 >= ntiles) break;
-  }
+  if (fixed_ref) run(std::true_type{});
+  else run(std::false_type{});
   // ---- epilogue: normalize, gate, store z[b*C + t][head*DH + d]. The O^T
   // registers hold one query per lane, so the 32 x DH tile of a wave is
   // transposed through LDS (the stage buffers, free after the loop; two
@@ -945,7 +988,12 @@ template <int DH, int GRP>
 hipError_t prefill_cfg(const AttnArgs& a, hipStream_t st) {
   constexpr int BQ = (PF_WAVES / GRP) * 32;
   dim3 grid((a.C + BQ - 1) / BQ, a.n_kv, a.B);
-  hipLaunchKernelGGL((attn_prefill_kernel<DH, GRP>), grid, dim3(PF_WAVES * 64), 0, st, a);
+  // a step from position 0 (no positions below the fresh buffer's origin)
+  // reads step keys only: the DMA addressing without the cache rows
+  if (DH == 128 && a.f_origin == 0)
+    hipLaunchKernelGGL((attn_prefill_kernel<DH, GRP, DH == 128>), grid, dim3(PF_WAVES * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<DH, GRP, false>), grid, dim3(PF_WAVES * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -233,6 +233,10 @@ struct AttnArgs {
   const float* cs = nullptr;
   const float* sn = nullptr;
   const float* s_qk = nullptr;
+  // prefill: the layer's s_qk ([dh]), from which the kernel bounds every
+  // score and, when the bound allows, uses it as a fixed softmax reference;
+  // null: running maximum (inputs not made by the layer, e.g. probes)
+  const float* ref_s_qk = nullptr;
 };
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 

@@ -439,8 +439,10 @@ struct FusedQk {
   const float *cs = nullptr, *sn = nullptr, *s_qk = nullptr;
 };
 
+// ref_s_qk: the layer's s_qk when q and the keys were made by the layer (the
+// prefill kernel bounds the scores with it); null for caller-made inputs.
 dory_status attend(Ctx& c, const SlotPtr& sp, bool full, const uint16_t* q, const uint16_t* gate,
-                   uint16_t* z, const FusedQk* fq = nullptr) {
+                   uint16_t* z, const FusedQk* fq = nullptr, const float* ref_s_qk = nullptr) {
   const Shape& s = c.s;
   AttnArgs aa{};
   if (fq) {
@@ -480,6 +482,7 @@ dory_status attend(Ctx& c, const SlotPtr& sp, bool full, const uint16_t* q, cons
                               c.kf(), c.vf(), c.L.f_rows, c.st));
   }
   aa.kf = c.kf(); aa.vf = c.vf(); aa.f_rows = c.L.f_rows; aa.f_origin = f_origin;
+  aa.ref_s_qk = ref_s_qk;
   PROF(c, DORY_K_ATTN);
   HIPCHK(launch_attn_prefill(aa, c.st));
   return DORY_OK;
@@ -529,7 +532,7 @@ dory_status attention_sublayer(Ctx& c, int i, int slot, bool write, const Update
                             c.gate(), c.st, RowLoops(), c.p0_dev));
     }
   }
-  st = attend(c, sp, full, c.qh(), c.gate(), c.z(), fq.part ? &fq : nullptr);
+  st = attend(c, sp, full, c.qh(), c.gate(), c.z(), fq.part ? &fq : nullptr, w.s_qk);
   if (st != DORY_OK) return st;
   if (c.T > 1 && write) {
     PROF(c, DORY_K_KV_WRITE);
