@@ -554,6 +554,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode table (B=64, 32768 cached tokens), for profiling")
+    ap.add_argument("--decode-b1", action="store_true",
+                    help="only one-sequence decode (2048 cached tokens, k = 1 and 4, 64 "
+                         "steps each), for profiling the launch-bound case")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 4 GiB device-to-device copy first (reference for "
                          "hardware byte counters)")
@@ -580,6 +583,12 @@ def main():
     kinds = M.schedule(shape)
     weights = gpu_weights(shape, kinds)
     gm = M.Model(shape, weights)
+    if args.decode_b1:
+        # one sequence: the step is bound by its chain of launches and the
+        # weight stream
+        d = decode_table(gm, shape, (1, 4), ("last_loop",), B=1, ctx=2048, steps=64, mixed=False)
+        print(json.dumps({"decode_b1_ctx2048_tok_s": d}), flush=True)
+        return
     if args.decode_only:
         d = decode_table(gm, shape, (1, 2, 4), ("last_loop", "per_loop"))
         d.update(decode_mxfp8(gm, shape))
