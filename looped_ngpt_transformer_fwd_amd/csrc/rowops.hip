@@ -259,6 +259,47 @@ __global__ void kv_write_kernel(const uint16_t* kf, const uint16_t* vf, int64_t 
   vc[(bg * dh + d) * c_rows + crow] = vf[(bg * dh + d) * f_rows + frow];
 }
 
+// The same copy in 64-position tiles (blockIdx.x counted from pos_a rounded
+// down to a multiple of 8; blockIdx.y = group, blockIdx.z = sequence): K rows
+// move as 16-byte pieces, V^T columns as 16-byte groups of 8 aligned
+// positions, which occupy 8 consecutive columns on both sides (f_origin,
+// f_rows, c_rows and the ring are multiples of 8). The one-position form
+// above writes a V^T element per thread into a different row each, i.e. 2
+// bytes per cache line per store.
+__global__ void kv_write_tiled_kernel(const uint16_t* kf, const uint16_t* vf, int64_t f_rows,
+                                      int64_t f_origin, int nkv, int dh, int64_t pos_a,
+                                      int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
+                                      int64_t ring, RowLoops rl) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (rl.k_rows && rl.k_rows[b] != rl.loop + 1) return;  // not this sequence's last loop
+  const int64_t bg = (int64_t)b * nkv + g;
+  const int64_t base = (pos_a & ~(int64_t)7) + (int64_t)blockIdx.x * 64;
+  const int cpr = dh / 8;  // 16-byte pieces per K row
+  for (int i = threadIdx.x; i < 64 * cpr; i += blockDim.x) {
+    const int64_t pos = base + i / cpr;
+    if (pos < pos_a || pos >= pos_b) continue;
+    const int c = i % cpr;
+    *reinterpret_cast<uint4*>(kc + (bg * c_rows + cache_row(pos, ring)) * dh + c * 8) =
+        *reinterpret_cast<const uint4*>(kf + (bg * f_rows + pos - f_origin) * dh + c * 8);
+  }
+  for (int i = threadIdx.x; i < 8 * dh; i += blockDim.x) {
+    const int d = i >> 3;
+    const int64_t p0 = base + (i & 7) * 8;
+    const uint16_t* srow = vf + (bg * dh + d) * f_rows;  // column pos - f_origin (pos >= f_origin)
+    uint16_t* drow = vc + (bg * dh + d) * c_rows;
+    if (p0 >= pos_a && p0 + 8 <= pos_b) {
+      *reinterpret_cast<uint4*>(drow + cache_row(p0, ring)) =
+          *reinterpret_cast<const uint4*>(srow + (p0 - f_origin));
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        const int64_t pos = p0 + e;
+        if (pos < pos_a || pos >= pos_b) continue;
+        drow[cache_row(pos, ring)] = srow[pos - f_origin];
+      }
+    }
+  }
+}
+
 // Cache-to-cache copy of positions [pos_a, pos_b) of one sequence's K rows
 // and V^T columns. blockIdx.x = 64-position tile counted from pos_a rounded
 // down to a multiple of 8, blockIdx.y = group. Rows and rings are multiples
@@ -499,8 +540,19 @@ hipError_t launch_kv_write(const uint16_t* kf, const uint16_t* vf, int64_t f_row
                            int64_t pos_b, uint16_t* kc, uint16_t* vc, int64_t c_rows,
                            int64_t ring, hipStream_t st, RowLoops rl) {
   if (pos_b <= pos_a) return hipSuccess;
-  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
-                     kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring, rl);
+  const bool aligned = dh % 8 == 0 && f_rows % 8 == 0 && f_origin % 8 == 0 && c_rows % 8 == 0 &&
+                       ring % 8 == 0 && (reinterpret_cast<uintptr_t>(kf) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(vf) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(kc) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(vc) & 15) == 0;
+  if (aligned) {
+    const int64_t span = pos_b - (pos_a & ~(int64_t)7);
+    hipLaunchKernelGGL(kv_write_tiled_kernel, dim3((unsigned)((span + 63) / 64), n_kv, B), dim3(256), 0,
+                       st, kf, vf, f_rows, f_origin, n_kv, dh, pos_a, pos_b, kc, vc, c_rows, ring, rl);
+  } else {
+    hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)(pos_b - pos_a), n_kv, B), dim3(dh), 0, st,
+                       kf, vf, f_rows, f_origin, n_kv, dh, pos_a, kc, vc, c_rows, ring, rl);
+  }
   return hipGetLastError();
 }
 
