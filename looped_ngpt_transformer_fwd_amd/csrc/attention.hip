@@ -5,8 +5,10 @@
 // times 32-query blocks, so every K/V tile staged in LDS is reused by all
 // query heads of the group. Scores are computed transposed,
 // S^T = K Q^T (v_mfma_f32_32x32x16_bf16 with K as the A operand), so that in
-// the accumulator layout each lane owns one query column: the running max and
-// sum of the online softmax need a single lane-pair exchange per tile. The
+// the accumulator layout each lane owns one query column: the softmax state
+// needs a single lane-pair exchange per tile (none with the fixed reference:
+// when the layer's s_qk bounds every score tightly enough, the bound is the
+// softmax reference and no running maximum is kept). The
 // output is likewise accumulated transposed, O^T += V^T P^T, with P^T taken
 // straight from the score registers (converted to bf16) and V^T read from an
 // LDS tile stored [head_dim][keys]. Keys come from two sources: the cache
@@ -16,9 +18,12 @@
 // epilogue; the concatenation norm is left to the output projection's
 // consumer (it cancels under N(y)).
 //
-// Decode: one query per sequence; split over keys, VALU dot products with
-// 16 lanes per 256-byte key row, partial (max, sum, o) per split, and a
-// combine kernel that merges the splits and applies the gate.
+// Decode: one query per sequence, the query/key transform of the token
+// fused in; both contractions on MFMA with the KV group's query heads as the
+// padded 16-wide side. Small batches split the keys (partial (max, sum, o)
+// per split and a combine kernel that merges them and applies the gate);
+// large batches take one workgroup per (sequence, KV head) that writes the
+// gated output itself.
 #include <type_traits>
 
 #include "common.h"

@@ -28,7 +28,9 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 
 // The same rounding by the hardware conversion (v_cvt_pk_bf16_f32: one
 // instruction where f2bf takes three). Equal to f2bf for every normal
-// input; kept to epilogues whose outputs never meet fp32 denormals.
+// input; should the hardware flush fp32 denormals, results differ by less
+// than 2^-126. Used in the large-M GEMM epilogues; the row kernels keep
+// f2bf.
 __device__ __forceinline__ uint16_t f2bf_hw(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
